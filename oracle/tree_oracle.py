@@ -1,0 +1,203 @@
+"""CPU oracle for tree attention and greedy token-tree verification.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the package's smoke check and the
+benchmark's CPU-baseline leg may import this module; the library never does.
+
+It is the plain definition of what the hot path computes, in float64 NumPy,
+from the stored input values (bf16 -> float64 and fp32 -> float64 are exact):
+
+* tree_build: S_u, the set of tokens on the path from the root to node u
+  (both ends included), found by walking u's parent chain, written as a
+  per-node ancestor bitmask; position id = prefix length + depth.
+  (SpecInfer explainer, section on the token-tree structure, where S_u is
+  defined; section on kernel fusion, item on the precomputed topology mask.)
+* tree_attention: for each node u and query head h,
+  softmax(Q_u K^T / sqrt(d_k)) V over the keys of the shared prefix plus
+  exactly the nodes of S_u, as ONE softmax over that union.
+  (Same explainer, the attention equation of the token-tree section; the
+  contributions list says the mask is consistent with KV-cache reuse, so the
+  cached prefix is attended too.)
+* verify_greedy: per-node argmax of the logits (lowest index on ties), then
+  the walk from the root that accepts a child whose draft token equals the
+  argmax at its parent (lowest node index among equal draft tokens), stopping
+  at the first node with no such child; the argmax there is the bonus token.
+  (Explainer: greedy verification is named in the tree-verification section;
+  the accept-up-to-first-mismatch-plus-one-target-token rule is the sequence
+  case on the speculative-decoding explainer, technical mechanism section, and
+  on the speculative-decoding operations guide's diagram, applied per branch.)
+
+Layouts are those of include/tree_verify.h.  No blocking, fusion or reordering
+is done beyond vectorising the prefix scores of all rows of a KV head, which
+every node attends identically.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+TV_OK = 0
+TV_ETOPOLOGY = 2
+PAGE = 16
+
+
+# ----------------------------------------------------------------------------- values
+def to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
+    """Stored values -> float64.  bf16 arrays are raw uint16 bit patterns."""
+    if dtype == "bf16":
+        return (np.asarray(a).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return np.asarray(a, dtype=np.float32).astype(np.float64)
+
+
+# ----------------------------------------------------------------------------- topology
+def validate_tree(parent: np.ndarray, depth: np.ndarray) -> bool:
+    """Single root at node 0, every other node's parent precedes it, depths agree."""
+    n = len(parent)
+    if n < 1 or parent[0] != -1 or depth[0] != 0:
+        return False
+    for u in range(1, n):
+        p = int(parent[u])
+        if not (0 <= p < u):
+            return False
+        if depth[u] != depth[p] + 1:
+            return False
+    return True
+
+
+def ancestors(parent: np.ndarray, u: int) -> list[int]:
+    """S_u: node u and every node on its parent chain up to the root."""
+    out = []
+    v = u
+    while v != -1:
+        out.append(v)
+        v = int(parent[v])
+    return out
+
+
+def tree_build(parent: np.ndarray, depth: np.ndarray, prefix_len: np.ndarray):
+    """(mask [B][n][W] uint64, pos [B][n] int32, status [B] int32).
+
+    Bit v of word v>>6 (least significant bit first) of mask[b][u] is set iff
+    v is in S_u.  Rows of a sequence whose topology is invalid are left zero and
+    its status is TV_ETOPOLOGY.
+    """
+    parent = np.asarray(parent)
+    B, n = parent.shape
+    W = (n + 63) // 64
+    mask = np.zeros((B, n, W), np.uint64)
+    pos = np.zeros((B, n), np.int32)
+    status = np.zeros(B, np.int32)
+    for b in range(B):
+        if not validate_tree(parent[b], depth[b]):
+            status[b] = TV_ETOPOLOGY
+            continue
+        for u in range(n):
+            for v in ancestors(parent[b], u):
+                mask[b, u, v >> 6] |= np.uint64(1) << np.uint64(v & 63)
+            pos[b, u] = int(prefix_len[b]) + int(depth[b, u])
+    return mask, pos, status
+
+
+# ----------------------------------------------------------------------------- prefix gather
+def gather_prefix(k_cache, v_cache, b: int, g: int, L: int, *, paged: bool, block_table=None):
+    """Keys and values of prefix tokens 0..L-1 of sequence b, KV head g, as [L][D] arrays.
+
+    contiguous: K [B][Hkv][Lmax][D], V [B][Hkv][D][Lmax]
+    paged:      token j lives in block block_table[b][j // 16], slot j % 16;
+                K [blocks][Hkv][16][D], V [blocks][Hkv][D][16]
+    """
+    if not paged:
+        return k_cache[b, g, :L, :], v_cache[b, g, :, :L].T
+    j = np.arange(L)
+    blk = np.asarray(block_table)[b, j // PAGE]
+    slot = j % PAGE
+    return k_cache[blk, g, slot, :], v_cache[blk, g, :, slot]
+
+
+# ----------------------------------------------------------------------------- attention
+def tree_attention(w: dict, seqs=None, kv_heads=None, scale: float | None = None):
+    """Tree attention of workload dict ``w`` (see workloads.make) in float64.
+
+    Returns (O [B][n][Hq][D], lse [B][n][Hq]) as float64; entries of sequences or
+    KV heads not selected are NaN.
+    """
+    cfg = w["cfg"]
+    dt = cfg.dtype
+    B, n, Hq, Hkv, D = cfg.B, cfg.n, cfg.Hq, cfg.Hkv, cfg.D
+    G = Hq // Hkv
+    scale = 1.0 / np.sqrt(D) if scale is None else scale
+    seqs = range(B) if seqs is None else seqs
+    kv_heads = range(Hkv) if kv_heads is None else kv_heads
+    O = np.full((B, n, Hq, D), np.nan)
+    LSE = np.full((B, n, Hq), np.nan)
+    parent = w["parent"]
+    for b in seqs:
+        L = int(w["prefix_len"][b])
+        # A[u][v] = 1 iff tree node v is in S_u (parent-chain walk)
+        A = np.zeros((n, n), bool)
+        for u in range(n):
+            A[u, ancestors(parent[b], u)] = True
+        for g in kv_heads:
+            Kp, Vp = gather_prefix(w["k_cache"], w["v_cache"], b, g, L, paged=cfg.paged,
+                                   block_table=w.get("block_table"))
+            Kp, Vp = to_f64(Kp, dt), to_f64(Vp, dt)
+            Kt = to_f64(w["k_tree"][b, :, g, :], dt)            # [n][D]
+            Vt = to_f64(w["v_tree"][b, :, g, :], dt)
+            heads = range(g * G, (g + 1) * G)
+            Q = to_f64(w["q"][b][:, heads, :], dt)              # [n][G][D]
+            Qr = Q.reshape(n * G, D)
+            s_pre = (Qr @ Kp.T) * scale                         # every node sees the whole prefix
+            s_tree = (Qr @ Kt.T) * scale
+            s_tree = np.where(np.repeat(A, G, axis=0), s_tree, -np.inf)
+            s = np.concatenate([s_pre, s_tree], axis=1)         # one softmax over prefix U S_u
+            m = s.max(axis=1, keepdims=True)
+            p = np.exp(s - m)
+            l = p.sum(axis=1, keepdims=True)
+            o = (p @ np.concatenate([Vp, Vt], axis=0)) / l
+            O[b][:, heads, :] = o.reshape(n, G, D)
+            LSE[b][:, heads] = (m + np.log(l)).reshape(n, G)
+    return O, LSE
+
+
+# ----------------------------------------------------------------------------- verification
+def argmax_lowest(logits: np.ndarray, dtype: str) -> np.ndarray:
+    """Index of the largest value of each row; ties go to the lowest index.
+
+    Values are compared as numbers (-0 equals +0).  NaN inputs are out of contract.
+    """
+    shp = logits.shape
+    rows = logits.reshape(-1, shp[-1])
+    out = np.empty(rows.shape[0], np.int64)
+    for r0 in range(0, rows.shape[0], 64):
+        x = to_f64(rows[r0:r0 + 64], dtype)
+        m = x.max(axis=1, keepdims=True)
+        hit = x == m
+        out[r0:r0 + 64] = hit.argmax(axis=1)   # first True = lowest index
+    return out.reshape(shp[:-1]).astype(np.int32)
+
+
+def accept_walk(am: np.ndarray, tokens: np.ndarray, parent: np.ndarray):
+    """Greedy walk of one sequence: (path list of node ids, root first; bonus token)."""
+    n = len(parent)
+    path = [0]
+    cur = 0
+    while True:
+        hits = [v for v in range(n) if parent[v] == cur and tokens[v] == am[cur]]
+        if not hits:
+            break
+        cur = min(hits)
+        path.append(cur)
+    return path, int(am[cur])
+
+
+def verify_greedy(logits: np.ndarray, tokens: np.ndarray, parent: np.ndarray, dtype: str):
+    """(argmax [B][n], path [B][n] -1 padded, path_len [B], bonus [B]) as int32."""
+    B, n = tokens.shape
+    am = argmax_lowest(logits, dtype)
+    path = np.full((B, n), -1, np.int32)
+    plen = np.zeros(B, np.int32)
+    bonus = np.zeros(B, np.int32)
+    for b in range(B):
+        p, bo = accept_walk(am[b], tokens[b], parent[b])
+        path[b, :len(p)] = p
+        plen[b] = len(p)
+        bonus[b] = bo
+    return am, path, plen, bonus
