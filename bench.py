@@ -1,0 +1,187 @@
+"""Benchmark: verified tree tokens/s of one speculative-decoding verification step.
+
+A step is the whole hot path over one batch: tree_build -> tree_attention ->
+tree_verify_greedy, on one GPU, inputs resident in HBM.  Default workload: the
+Llama-7B-shaped layer (batch 8, 32 MHA heads, head dim 128, bf16, 1024-token
+prefix, expansion tree <1,1,3,1,1,1,1,1> = 21 nodes, vocab 32000).
+
+Each timed step uses the next of R input copies (R chosen so the copies exceed
+twice the 256 MB last-level cache), the way consecutive layers each bring their
+own KV cache: a step never finds its inputs already cached.
+
+Prints ONE JSON line.  `value` = B*n / (wall time per step).  `roofline` covers
+the dominant kernel (tree_attention) measured with HIP events on the launch
+stream; `traffic` is read from the committed rocprofv3 counter summary when it
+was taken on the current kernel source, else null.  `cpu_baseline` times the
+CPU oracle on the same workload.
+
+    python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--config 2]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "tree-attn HBM GB/s & MFMA util (% peak); verified tree tokens/sec at 1 GPU"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+FP32_PEAK_TFLOPS = 157.3
+MALL_BYTES = 256 << 20
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("attn_bf16.hip", "attn_f32.hip", "tv_internal.h"):
+        with open(os.path.join(ROOT, "token_tree_verification_02_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str):
+    path = os.path.join(ROOT, "profiles", f"tree_attention_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        t = json.load(fh)
+    if t.get("source_hash") != kernel_source_hash():
+        return None
+    return t
+
+
+def cpu_baseline(w, budget_s: float):
+    """The oracle (as it stands) on the whole batch, repeated until the budget is used."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    cfg = w["cfg"]
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.tree_build(w["parent"], w["depth"], w["prefix_len"])
+        oracle.tree_attention(w)
+        if cfg.vocab:
+            oracle.verify_greedy(w["logits"], w["tokens"], w["parent"], cfg.dtype)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return {"value": reps * cfg.B * cfg.n / el, "unit": "verified tree tokens/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"{reps} full pass(es) of the {cfg.name} batch (B={cfg.B}, n={cfg.n}), float64 NumPy, "
+                      f"{el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--copies", type=int, default=0, help="input copies to rotate (0 = auto)")
+    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of this many MiB (counter calibration) and exit")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this path has no multi-GPU form (each sequence and each KV head "
+              "is independent; see the sharding notes in the design document)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "launches": 5}))
+        return
+
+    from token_tree_verification_02_amd import runner
+    from token_tree_verification_02_amd import workloads as W
+
+    cfg = W.config(args.config)
+    t_gen = time.perf_counter()
+    w = W.make(cfg)
+    t_gen = time.perf_counter() - t_gen
+    refb = W.reference_bytes(w)
+    per_copy = refb["attn_bytes"] + refb["verify_bytes"]
+    R = args.copies or max(1, math.ceil(2 * MALL_BYTES / per_copy))
+    copies = [runner.upload(w) for _ in range(R)]
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    for i in range(args.warmup):
+        runner.step(copies[i % R])
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(K):
+        d = copies[k % R]
+        e = ev[k]
+        e[0].record(stream)
+        runner.build(d)
+        e[1].record(stream)
+        runner.attention(d)
+        e[2].record(stream)
+        if "argmax" in d:
+            runner.verify(d)
+        e[3].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_build = np.mean([e[0].elapsed_time(e[1]) for e in ev]) * 1e-3
+    t_attn = np.mean([e[1].elapsed_time(e[2]) for e in ev]) * 1e-3
+    t_ver = np.mean([e[2].elapsed_time(e[3]) for e in ev]) * 1e-3
+    ms_step = wall / K * 1e3
+    tokens = cfg.B * cfg.n
+    value = tokens / (wall / K)
+
+    attn_gbs = refb["attn_bytes"] / t_attn / 1e9
+    peak_tf = BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else FP32_PEAK_TFLOPS
+    mfma_pct = refb["attn_flops"] / t_attn / 1e12 / peak_tf * 100
+    traffic = load_traffic(cfg.name)
+    roofline = {"bound": "hbm", "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
+                "traffic": None if traffic is None else traffic["bytes_per_launch"],
+                "kernel": "tree_attention", "avg_launch_us": round(t_attn * 1e6, 2),
+                "algorithmic_bytes": refb["attn_bytes"]}
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "verified tree tokens/s", "n_gpus": 1,
+        "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic (seeded, N(0,1) Q/K/V)",
+        "config": {"workload": cfg.name, "B": cfg.B, "n": cfg.n, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "D": cfg.D,
+                   "prefix_len": [cfg.L_lo, cfg.L_hi], "paged": cfg.paged, "vocab": cfg.vocab,
+                   "input_copies": R},
+        "roofline": roofline,
+        "attn_hbm_gbs": round(attn_gbs, 1), "mfma_util_pct": round(mfma_pct, 2),
+        "kernel_us": {"tree_build": round(t_build * 1e6, 2), "tree_attention": round(t_attn * 1e6, 2),
+                      "tree_verify_greedy": round(t_ver * 1e6, 2)},
+        "verify_hbm_gbs": round(refb["verify_bytes"] / t_ver / 1e9, 1) if cfg.vocab else None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,178 @@
+/*
+ * tree_verify.h -- C ABI of the MI355X (gfx950) token-tree verification library.
+ *
+ * One speculative decoding step of SpecInfer verifies a whole token tree in a
+ * single forward pass: every tree node u attends to the shared prefix KV cache
+ * plus exactly the nodes on its own root-to-u path S_u, and greedy
+ * verification then walks the tree from the root.  This library is that hot
+ * path: three calls, all asynchronous on a caller-provided HIP stream.
+ *
+ * Sources (the SpecInfer explainer at 0h-n0.github.io, "paper-2305-09781"):
+ *   - token-tree structure section: a node per token, S_u = tokens on the path
+ *     from the root to u, and the attention equation softmax(Q_u K_{S_u}^T /
+ *     sqrt(d_k)) V_{S_u};
+ *   - same section and the contributions list: a topology-aware causal mask
+ *     lets each node attend only to its ancestors, consistently with ordinary
+ *     KV-cache reuse;
+ *   - kernel-fusion section: the mask is precomputed from ancestor relations;
+ *   - tree-verification section: greedy verification; the accept rule of the
+ *     sequence case (accept up to the first mismatch, then the target model
+ *     supplies one token) is on the speculative-decoding explainer
+ *     (lab.arcteris.jp), technical-mechanism section, and in the diagram of the
+ *     speculative-decoding operations guide (flatkey.ai);
+ *   - "practical applications" section: integration with PagedAttention's
+ *     block-wise KV memory (the paged cache layout below).
+ *
+ * Conventions for every call
+ *   - Pointers named in a [..] shape are DEVICE pointers owned by the caller;
+ *     the library never frees or keeps them.  Base addresses must be 16-byte
+ *     aligned.  The last dimension of every array is contiguous.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Calls return after
+ *     host-side validation and kernel enqueue; results are ready when the
+ *     stream reaches them.
+ *   - Return value: TV_OK, or a tv_status code for an error found on the host
+ *     (nothing is enqueued then).  tv_last_error() gives a thread-local
+ *     message for the last failing call.
+ *   - Tree nodes are in a topological order: node 0 is the single root,
+ *     parent[u] < u for u >= 1 (BFS and DFS orders both qualify).
+ *   - Ancestor masks: W = ceil(n/64) uint64 words per node; bit (v & 63) of
+ *     word (v >> 6) is set iff node v is on the path root..u (u included).
+ *   - The library allocates no device memory.  tree_attention takes a caller
+ *     workspace whose size tree_attention_workspace_size() reports.
+ */
+#ifndef TREE_VERIFY_H
+#define TREE_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TV_NMAX 256     /* max tree nodes per sequence, root included          */
+#define TV_WMAX 4       /* max mask words per node = TV_NMAX / 64               */
+#define TV_PAGE 16      /* tokens per paged KV block                            */
+#define TV_VERSION 1
+
+typedef enum {
+  TV_OK = 0,
+  TV_EINVAL = 1,        /* bad argument: null pointer, size out of range         */
+  TV_ETOPOLOGY = 2,     /* tree is not a rooted, topologically ordered tree      */
+  TV_EUNSUPPORTED = 3,  /* valid but not supported (head dim, dtype, GQA ratio)  */
+  TV_EWORKSPACE = 4,    /* workspace missing or smaller than required            */
+  TV_EHIP = 5           /* a HIP runtime call failed; see tv_last_error()        */
+} tv_status;
+
+typedef enum { TV_F32 = 0, TV_BF16 = 1 } tv_dtype;
+
+/* Static text for a status code; never NULL. */
+const char* tv_status_string(int status);
+/* Thread-local message of the last failing call on this thread ("" if none). */
+const char* tv_last_error(void);
+/* TV_VERSION of the built library. */
+int tv_version(void);
+
+/* ---------------------------------------------------------------------------
+ * tree_build: topology encoder (the precomputed topology-aware mask).
+ *
+ *   parent     [B][n] int32   parent[b][0] == -1, 0 <= parent[b][u] < u
+ *   depth      [B][n] int32   depth[b][0] == 0, depth[u] == depth[parent[u]] + 1
+ *   prefix_len [B]    int32   cached prefix length L_b of each sequence
+ *   anc_mask   [B][n][W] uint64  out: ancestor bitmask of each node (u included)
+ *   pos_ids    [B][n] int32   out: L_b + depth[b][u] (the root sits at L_b)
+ *   status     [B]    int32   out: TV_OK, or TV_ETOPOLOGY if sequence b breaks
+ *                             the rules above; its mask/pos rows are then
+ *                             unspecified (but written in bounds).
+ * 1 <= n <= TV_NMAX, B >= 0 (B == 0 enqueues nothing).  Host errors: TV_EINVAL.
+ * ------------------------------------------------------------------------- */
+int tree_build(int B, int n, const int32_t* parent, const int32_t* depth,
+               const int32_t* prefix_len, uint64_t* anc_mask, int32_t* pos_ids,
+               int32_t* status, void* stream);
+
+/* Same rules, checked synchronously on HOST arrays parent[n], depth[n].
+ * Returns TV_OK, TV_ETOPOLOGY, or TV_EINVAL (null pointer, n out of range). */
+int tree_validate_host(int n, const int32_t* parent, const int32_t* depth);
+
+/* ---------------------------------------------------------------------------
+ * tree_attention: O = tree attention of every node over prefix + S_u.
+ *
+ * For node u of sequence b and query head h (KV head g = h / (Hq/Hkv)):
+ *   O[b][u][h] = sum_j p_j V_j / sum_j p_j,  p_j = exp(s_j - max s),
+ *   s_j = scale * <Q[b][u][h], K_j>,
+ * over j in { prefix tokens 0..L_b-1 } U { tree nodes v in S_u }, as one
+ * softmax.  lse[b][u][h] = max s + ln(sum_j p_j) (natural log).
+ *
+ * Layouts (E = element type of desc->dtype, D = head dim):
+ *   q, k_tree, v_tree, out   [B][n][H][D]       (H = Hq for q/out, Hkv for k/v)
+ *   contiguous cache (paged == 0):
+ *     k_cache  [B][Hkv][Lmax][D]    token-major
+ *     v_cache  [B][Hkv][D][Lmax]    d-major: each d row holds Lmax tokens
+ *   paged cache (paged == 1, block_size == 16), prefix token j of sequence b
+ *   lives in physical block block_table[b][j / 16], slot j % 16:
+ *     k_cache  [num_blocks][Hkv][16][D]
+ *     v_cache  [num_blocks][Hkv][D][16]   (PagedAttention's value-block layout)
+ *     block_table [B][max_blocks] int32
+ *   The V cache is d-major so that the P*V contraction reads runs of tokens.
+ *   anc_mask [B][n][W] from tree_build;  lse [B][n][Hq] float (may be NULL).
+ *
+ * Supported: dtype TV_BF16 (fp32 accumulation, bf16 output) or TV_F32;
+ * D in {64, 128}; Hq % Hkv == 0; 1 <= n <= TV_NMAX; Lmax % 16 == 0.
+ * 0 <= prefix_len[b] <= capacity (Lmax, or max_blocks*16); paged block ids in
+ * [0, num_blocks).  Out-of-range device values are not trusted: a length is
+ * clamped to [0, capacity] and a bad block id's tokens are skipped, so no read
+ * leaves the buffers, and if `status` [B] (may be NULL) is given it reports
+ * TV_EINVAL for that sequence (TV_OK otherwise).
+ * Cache slots past L_b are never read (they may hold NaN).
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  int32_t B, n, Hq, Hkv, D;
+  int32_t dtype;        /* tv_dtype of q, caches, tree K/V and out           */
+  float scale;          /* softmax scale; 0 means 1/sqrt(D)                   */
+  int32_t paged;        /* 0 contiguous, 1 paged                              */
+  int32_t block_size;   /* paged: must be TV_PAGE                             */
+  int32_t Lmax;         /* contiguous: per-sequence capacity (tokens)         */
+  int32_t max_blocks;   /* paged: block_table row length                      */
+  int32_t num_blocks;   /* paged: physical blocks in the cache                */
+} tv_attn_desc;
+
+/* Workspace bytes tree_attention needs for this descriptor (0 if none); the
+ * split of long prefixes into chunks depends only on the descriptor.
+ * Returns (size_t)-1 for an invalid descriptor. */
+size_t tree_attention_workspace_size(const tv_attn_desc* desc);
+
+int tree_attention(const tv_attn_desc* desc, const void* q,
+                   const void* k_cache, const void* v_cache,
+                   const int32_t* block_table, const int32_t* prefix_len,
+                   const void* k_tree, const void* v_tree,
+                   const uint64_t* anc_mask, void* out, float* lse,
+                   int32_t* status, void* workspace, size_t workspace_bytes,
+                   void* stream);
+
+/* ---------------------------------------------------------------------------
+ * tree_verify_greedy: greedy verification of the token tree.
+ *
+ *   logits  [B][n][V]  logits_dtype (TV_BF16 or TV_F32): the target model's
+ *                      next-token logits after each node
+ *   tokens  [B][n] int32  draft token of each node (tokens[b][0] is ignored)
+ *   parent  [B][n] int32  as for tree_build (assumed valid)
+ *   argmax_out [B][n] int32  out: lowest index of the row maximum of logits
+ *   path_out   [B][n] int32  out: accepted node ids, root first, -1 padded
+ *   path_len   [B]    int32  out: accepted nodes including the root (>= 1)
+ *   bonus      [B]    int32  out: argmax at the last accepted node, i.e. the
+ *                            token the target model supplies after the path
+ * Walk: cur = root; while some child c of cur has tokens[c] == argmax[cur],
+ * move to the lowest-numbered such c.  A step emits path_len-1 draft tokens
+ * plus the bonus token.  NaN logits are out of contract.
+ * 1 <= n <= TV_NMAX, V >= 1.
+ * ------------------------------------------------------------------------- */
+int tree_verify_greedy(int B, int n, int V, int logits_dtype, const void* logits,
+                       const int32_t* tokens, const int32_t* parent,
+                       int32_t* argmax_out, int32_t* path_out, int32_t* path_len,
+                       int32_t* bonus, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TREE_VERIFY_H */

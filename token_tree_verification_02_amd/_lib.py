@@ -1,0 +1,175 @@
+"""ctypes binding of libtreeverify.so: argument marshalling only.
+
+Every step of the hot path runs in the library's HIP kernels; this module turns
+torch tensors (device memory) and torch's current stream into the C ABI's raw
+pointers and sizes, allocates outputs with torch, and raises on a non-zero
+status.  It fails loudly when the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # imported before the library so both share torch's HIP runtime
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libtreeverify.so")
+
+TV_OK, TV_EINVAL, TV_ETOPOLOGY, TV_EUNSUPPORTED, TV_EWORKSPACE, TV_EHIP = range(6)
+TV_F32, TV_BF16 = 0, 1
+TV_NMAX, TV_PAGE = 256, 16
+
+_c_int, _c_float, _vp, _size_t = ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+
+
+class AttnDesc(ctypes.Structure):
+    _fields_ = [("B", _c_int), ("n", _c_int), ("Hq", _c_int), ("Hkv", _c_int), ("D", _c_int),
+                ("dtype", _c_int), ("scale", _c_float), ("paged", _c_int), ("block_size", _c_int),
+                ("Lmax", _c_int), ("max_blocks", _c_int), ("num_blocks", _c_int)]
+
+
+class TreeVerifyError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{msg} (status {code})")
+        self.code = code
+
+
+_lib = None
+
+# exported symbol -> (restype, argtypes)
+SIGNATURES = {
+    "tv_status_string": (ctypes.c_char_p, [_c_int]),
+    "tv_last_error": (ctypes.c_char_p, []),
+    "tv_version": (_c_int, []),
+    "tree_validate_host": (_c_int, [_c_int, _vp, _vp]),
+    "tree_build": (_c_int, [_c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "tree_attention_workspace_size": (_size_t, [ctypes.POINTER(AttnDesc)]),
+    "tree_attention": (_c_int, [ctypes.POINTER(AttnDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                _vp, _vp, _size_t, _vp]),
+    "tree_verify_greedy": (_c_int, [_c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+}
+
+
+def load() -> ctypes.CDLL:
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m token_tree_verification_02_amd.build` (hipcc, gfx950)")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype, fn.argtypes = res, args
+        _lib = lib
+    return _lib
+
+
+def last_error() -> str:
+    return load().tv_last_error().decode()
+
+
+def _check(rc: int, what: str):
+    if rc != TV_OK:
+        raise TreeVerifyError(rc, f"{what}: {load().tv_status_string(rc).decode()}: {last_error()}")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    return (stream if stream is not None else torch.cuda.current_stream()).cuda_stream
+
+
+def _dtype_code(t) -> int:
+    if t.dtype == torch.bfloat16:
+        return TV_BF16
+    if t.dtype == torch.float32:
+        return TV_F32
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+# ----------------------------------------------------------------------------- host-only helpers
+def validate_host(parent, depth) -> int:
+    """Synchronous CPU check of one tree (int32 sequences); returns the status code."""
+    import numpy as np
+    p = np.ascontiguousarray(parent, dtype=np.int32)
+    d = np.ascontiguousarray(depth, dtype=np.int32)
+    return load().tree_validate_host(len(p), p.ctypes.data, d.ctypes.data)
+
+
+def attn_desc(B, n, Hq, Hkv, D, dtype, *, paged=False, Lmax=0, max_blocks=0, num_blocks=0, scale=0.0):
+    return AttnDesc(B, n, Hq, Hkv, D, dtype, float(scale), int(paged), TV_PAGE if paged else 0,
+                    Lmax, max_blocks, num_blocks)
+
+
+def workspace_size(desc: AttnDesc) -> int:
+    return int(load().tree_attention_workspace_size(ctypes.byref(desc)))
+
+
+# ----------------------------------------------------------------------------- the three calls
+def tree_build(parent, depth, prefix_len, *, mask=None, pos=None, status=None, stream=None):
+    """parent, depth [B][n] int32, prefix_len [B] int32 -> (mask [B][n][W] int64 view of
+    the uint64 words, pos [B][n] int32, status [B] int32)."""
+    B, n = parent.shape
+    W = (n + 63) // 64
+    dev = parent.device
+    mask = torch.empty((B, n, W), dtype=torch.int64, device=dev) if mask is None else mask
+    pos = torch.empty((B, n), dtype=torch.int32, device=dev) if pos is None else pos
+    status = torch.empty((B,), dtype=torch.int32, device=dev) if status is None else status
+    rc = load().tree_build(B, n, _ptr(parent), _ptr(depth), _ptr(prefix_len), _ptr(mask), _ptr(pos),
+                           _ptr(status), _stream(stream))
+    _check(rc, "tree_build")
+    return mask, pos, status
+
+
+def tree_attention(q, k_cache, v_cache, prefix_len, k_tree, v_tree, mask, *, block_table=None,
+                   num_blocks=0, scale=0.0, out=None, lse=None, status=None, workspace=None,
+                   want_lse=False, stream=None):
+    """Tree attention.  q [B][n][Hq][D]; caches contiguous (k [B][Hkv][Lmax][D],
+    v [B][Hkv][D][Lmax]) or paged when block_table is given (k [blocks][Hkv][16][D],
+    v [blocks][Hkv][D][16]); k_tree, v_tree [B][n][Hkv][D]; mask from tree_build."""
+    B, n, Hq, D = q.shape
+    Hkv = k_tree.shape[2]
+    paged = block_table is not None
+    if paged:
+        desc = attn_desc(B, n, Hq, Hkv, D, _dtype_code(q), paged=True, max_blocks=block_table.shape[1],
+                         num_blocks=num_blocks or k_cache.shape[0], scale=scale)
+    else:
+        desc = attn_desc(B, n, Hq, Hkv, D, _dtype_code(q), Lmax=k_cache.shape[2], scale=scale)
+    out = torch.empty_like(q) if out is None else out
+    if want_lse and lse is None:
+        lse = torch.empty((B, n, Hq), dtype=torch.float32, device=q.device)
+    ws = workspace_size(desc)
+    if ws == (1 << 64) - 1:
+        _check(load().tree_attention(ctypes.byref(desc), *([None] * 12), 0, None), "tree_attention")
+    if workspace is None and ws > 0:
+        workspace = torch.empty(ws, dtype=torch.uint8, device=q.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = load().tree_attention(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                               _ptr(prefix_len), _ptr(k_tree), _ptr(v_tree), _ptr(mask), _ptr(out), _ptr(lse),
+                               _ptr(status), _ptr(workspace), wbytes, _stream(stream))
+    _check(rc, "tree_attention")
+    return (out, lse) if want_lse else out
+
+
+def tree_verify_greedy(logits, tokens, parent, *, argmax=None, path=None, path_len=None, bonus=None,
+                       stream=None):
+    """logits [B][n][V] -> (argmax [B][n], path [B][n], path_len [B], bonus [B]) int32."""
+    B, n, V = logits.shape
+    dev = logits.device
+    argmax = torch.empty((B, n), dtype=torch.int32, device=dev) if argmax is None else argmax
+    path = torch.empty((B, n), dtype=torch.int32, device=dev) if path is None else path
+    path_len = torch.empty((B,), dtype=torch.int32, device=dev) if path_len is None else path_len
+    bonus = torch.empty((B,), dtype=torch.int32, device=dev) if bonus is None else bonus
+    rc = load().tree_verify_greedy(B, n, V, _dtype_code(logits), _ptr(logits), _ptr(tokens), _ptr(parent),
+                                   _ptr(argmax), _ptr(path), _ptr(path_len), _ptr(bonus), _stream(stream))
+    _check(rc, "tree_verify_greedy")
+    return argmax, path, path_len, bonus

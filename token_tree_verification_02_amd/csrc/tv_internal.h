@@ -1,0 +1,68 @@
+// Internal declarations shared by the library's HIP translation units.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tree_verify.h"
+
+namespace tv {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// bf16 bit pattern -> float (exact)
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// float -> bf16 bits, round to nearest even (finite inputs; NaN stays NaN)
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  __bf16 h = (__bf16)f;
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+// ------------------------------------------------------------------ launch plans
+struct AttnPlan {
+  int rows;        // n * (Hq/Hkv): query rows per (sequence, KV head)
+  int rb;          // 32-row query blocks per workgroup (waves along rows)
+  int ks;          // key-split waves per query block
+  int tk;          // keys per wave per tile
+  int rsplit;      // workgroups along rows
+  int nchunks;     // prefix chunks (split-K) per (sequence, KV head)
+  int chunk_len;   // prefix tokens per chunk (multiple of the tile)
+  int cap;         // cache capacity per sequence in tokens
+  size_t ws_bytes; // workspace bytes
+};
+
+int plan_attention(const tv_attn_desc* d, AttnPlan* p, int num_cus);
+
+struct AttnArgs {
+  const void* q;
+  const void* kc;
+  const void* vc;
+  const int32_t* bt;
+  const int32_t* plen;
+  const void* kt;
+  const void* vt;
+  const uint64_t* mask;
+  void* out;
+  float* lse;
+  int32_t* status;
+  float* ws_o;     // [B][Hkv][nchunks][rows][D] fp32 partial outputs (unnormalised)
+  float* ws_ml;    // [B][Hkv][nchunks][rows][2] running max (log2 domain), sum
+  int B, n, Hq, Hkv, G, D, W;
+  int paged, Lmax, max_blocks, num_blocks;
+  float scale_log2;  // softmax scale * log2(e)
+};
+
+hipError_t launch_attn_bf16(const AttnArgs& a, const AttnPlan& p, hipStream_t s);
+hipError_t launch_attn_f32(const AttnArgs& a, const AttnPlan& p, hipStream_t s);
+hipError_t launch_merge(const AttnArgs& a, const AttnPlan& p, bool bf16_out, hipStream_t s);
+hipError_t launch_tree_build(int B, int n, const int32_t* parent, const int32_t* depth,
+                             const int32_t* plen, uint64_t* mask, int32_t* pos, int32_t* status,
+                             hipStream_t s);
+hipError_t launch_verify(int B, int n, int V, int bf16, const void* logits, const int32_t* tokens,
+                         const int32_t* parent, int32_t* am, int32_t* path, int32_t* plen,
+                         int32_t* bonus, hipStream_t s);
+
+}  // namespace tv

@@ -1,0 +1,85 @@
+"""Upload a workload (see workloads.make) to the GPU and run one verification step.
+
+One step = tree_build -> tree_attention -> tree_verify_greedy, the whole hot path
+of one speculative decoding step for one attention layer, all on one stream.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import _lib
+
+
+def _t(a, device, bf16=False):
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a)
+    if bf16:
+        return torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(a).to(device)
+
+
+def upload(w: dict, device="cuda") -> dict:
+    cfg = w["cfg"]
+    bf = cfg.dtype == "bf16"
+    d = dict(cfg=cfg, paged=cfg.paged, num_blocks=int(w.get("num_blocks", 0)))
+    for k in ("parent", "depth", "prefix_len", "block_table", "tokens"):
+        d[k] = _t(w.get(k), device)
+    for k in ("q", "k_cache", "v_cache", "k_tree", "v_tree", "logits"):
+        d[k] = _t(w.get(k), device, bf16=bf)
+    B, n = cfg.B, cfg.n
+    d["mask"] = torch.empty((B, n, (n + 63) // 64), dtype=torch.int64, device=device)
+    d["pos"] = torch.empty((B, n), dtype=torch.int32, device=device)
+    d["status"] = torch.empty((B,), dtype=torch.int32, device=device)
+    d["out"] = torch.empty_like(d["q"])
+    d["lse"] = torch.empty((B, n, cfg.Hq), dtype=torch.float32, device=device)
+    d["attn_status"] = torch.empty((B,), dtype=torch.int32, device=device)
+    desc = attn_desc_of(d)
+    ws = _lib.workspace_size(desc)
+    d["workspace"] = torch.empty(max(ws, 1), dtype=torch.uint8, device=device) if ws else None
+    if cfg.vocab and d.get("logits") is not None:
+        d["argmax"] = torch.empty((B, n), dtype=torch.int32, device=device)
+        d["path"] = torch.empty((B, n), dtype=torch.int32, device=device)
+        d["path_len"] = torch.empty((B,), dtype=torch.int32, device=device)
+        d["bonus"] = torch.empty((B,), dtype=torch.int32, device=device)
+    return d
+
+
+def attn_desc_of(d):
+    cfg = d["cfg"]
+    code = _lib.TV_BF16 if cfg.dtype == "bf16" else _lib.TV_F32
+    if d["paged"]:
+        return _lib.attn_desc(cfg.B, cfg.n, cfg.Hq, cfg.Hkv, cfg.D, code, paged=True,
+                              max_blocks=d["block_table"].shape[1], num_blocks=d["num_blocks"])
+    return _lib.attn_desc(cfg.B, cfg.n, cfg.Hq, cfg.Hkv, cfg.D, code, Lmax=d["k_cache"].shape[2])
+
+
+def build(d, stream=None):
+    return _lib.tree_build(d["parent"], d["depth"], d["prefix_len"], mask=d["mask"], pos=d["pos"],
+                           status=d["status"], stream=stream)
+
+
+def attention(d, stream=None):
+    return _lib.tree_attention(d["q"], d["k_cache"], d["v_cache"], d["prefix_len"], d["k_tree"], d["v_tree"],
+                               d["mask"], block_table=d["block_table"], num_blocks=d["num_blocks"],
+                               out=d["out"], lse=d["lse"], want_lse=True, status=d["attn_status"],
+                               workspace=d["workspace"], stream=stream)
+
+
+def verify(d, stream=None):
+    return _lib.tree_verify_greedy(d["logits"], d["tokens"], d["parent"], argmax=d["argmax"], path=d["path"],
+                                   path_len=d["path_len"], bonus=d["bonus"], stream=stream)
+
+
+def step(d, stream=None):
+    """One pass of the hot path over the uploaded batch."""
+    build(d, stream)
+    attention(d, stream)
+    if "argmax" in d:
+        verify(d, stream)
+
+
+def out_f64(d) -> np.ndarray:
+    o = d["out"]
+    return o.float().double().cpu().numpy() if o.dtype == torch.bfloat16 else o.double().cpu().numpy()

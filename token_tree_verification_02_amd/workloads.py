@@ -67,7 +67,9 @@ class Config:
 
     @property
     def capacity(self) -> int:
-        return self.Lmax or self.L_hi
+        """Contiguous cache capacity in tokens (a multiple of 16)."""
+        c = self.Lmax or self.L_hi
+        return (c + PAGE - 1) // PAGE * PAGE
 
 
 CONFIGS = {
