@@ -106,23 +106,21 @@ int tree_validate_host(int n, const int32_t* parent, const int32_t* depth);
  * Layouts (E = element type of desc->dtype, D = head dim):
  *   q, k_tree, v_tree, out   [B][n][H][D]       (H = Hq for q/out, Hkv for k/v)
  *   contiguous cache (paged == 0):
- *     k_cache  [B][Hkv][Lmax][D]    token-major
- *     v_cache  [B][Hkv][D][Lmax]    d-major: each d row holds Lmax tokens
+ *     k_cache, v_cache  [B][Hkv][Lmax][D]
  *   paged cache (paged == 1, block_size == 16), prefix token j of sequence b
  *   lives in physical block block_table[b][j / 16], slot j % 16:
- *     k_cache  [num_blocks][Hkv][16][D]
- *     v_cache  [num_blocks][Hkv][D][16]   (PagedAttention's value-block layout)
+ *     k_cache, v_cache  [num_blocks][Hkv][16][D]
  *     block_table [B][max_blocks] int32
- *   The V cache is d-major so that the P*V contraction reads runs of tokens.
  *   anc_mask [B][n][W] from tree_build;  lse [B][n][Hq] float (may be NULL).
  *
  * Supported: dtype TV_BF16 (fp32 accumulation, bf16 output) or TV_F32;
  * D in {64, 128}; Hq % Hkv == 0; 1 <= n <= TV_NMAX; Lmax % 16 == 0.
  * 0 <= prefix_len[b] <= capacity (Lmax, or max_blocks*16); paged block ids in
  * [0, num_blocks).  Out-of-range device values are not trusted: a length is
- * clamped to [0, capacity] and a bad block id's tokens are skipped, so no read
- * leaves the buffers, and if `status` [B] (may be NULL) is given it reports
- * TV_EINVAL for that sequence (TV_OK otherwise).
+ * clamped to [0, capacity] and a bad block id's tokens read as zeros, so no
+ * read leaves the buffers (O of that sequence is then unspecified), and if
+ * `status` [B] (may be NULL) is given it reports TV_EINVAL for that sequence
+ * (TV_OK otherwise).
  * Cache slots past L_b are never read (they may hold NaN).
  * ------------------------------------------------------------------------- */
 typedef struct {

@@ -100,16 +100,16 @@ def tree_build(parent: np.ndarray, depth: np.ndarray, prefix_len: np.ndarray):
 def gather_prefix(k_cache, v_cache, b: int, g: int, L: int, *, paged: bool, block_table=None):
     """Keys and values of prefix tokens 0..L-1 of sequence b, KV head g, as [L][D] arrays.
 
-    contiguous: K [B][Hkv][Lmax][D], V [B][Hkv][D][Lmax]
+    contiguous: K, V [B][Hkv][Lmax][D]
     paged:      token j lives in block block_table[b][j // 16], slot j % 16;
-                K [blocks][Hkv][16][D], V [blocks][Hkv][D][16]
+                K, V [blocks][Hkv][16][D]
     """
     if not paged:
-        return k_cache[b, g, :L, :], v_cache[b, g, :, :L].T
+        return k_cache[b, g, :L, :], v_cache[b, g, :L, :]
     j = np.arange(L)
     blk = np.asarray(block_table)[b, j // PAGE]
     slot = j % PAGE
-    return k_cache[blk, g, slot, :], v_cache[blk, g, :, slot]
+    return k_cache[blk, g, slot, :], v_cache[blk, g, slot, :]
 
 
 # ----------------------------------------------------------------------------- attention

@@ -44,10 +44,10 @@ def prefix_f64(w, b, g):
         if cfg.paged:
             blk = w["block_table"][b][j // 16]
             K[j] = oracle.to_f64(w["k_cache"][blk, g, j % 16, :], cfg.dtype)
-            V[j] = oracle.to_f64(w["v_cache"][blk, g, :, j % 16], cfg.dtype)
+            V[j] = oracle.to_f64(w["v_cache"][blk, g, j % 16, :], cfg.dtype)
         else:
             K[j] = oracle.to_f64(w["k_cache"][b, g, j, :], cfg.dtype)
-            V[j] = oracle.to_f64(w["v_cache"][b, g, :, j], cfg.dtype)
+            V[j] = oracle.to_f64(w["v_cache"][b, g, j, :], cfg.dtype)
     return K, V
 
 
@@ -142,7 +142,7 @@ def test_attention_equals_dense_closure_attention_all_trees_n5():
                  k_tree=rng.standard_normal((1, n, 2, D)).astype(np.float32),
                  v_tree=rng.standard_normal((1, n, 2, D)).astype(np.float32),
                  k_cache=rng.standard_normal((1, 2, L, D)).astype(np.float32),
-                 v_cache=rng.standard_normal((1, 2, D, L)).astype(np.float32))
+                 v_cache=rng.standard_normal((1, 2, L, D)).astype(np.float32))
         O, _ = oracle.tree_attention(w)
         R = closure(parent)
         for g in range(2):
@@ -220,7 +220,7 @@ def onehot_workload(parent, L, D=16):
                 k_tree=rng.standard_normal((1, n, 2, D)).astype(np.float32),
                 v_tree=vt,
                 k_cache=rng.standard_normal((1, 2, L, D)).astype(np.float32),
-                v_cache=np.zeros((1, 2, D, L), np.float32))
+                v_cache=np.zeros((1, 2, L, D), np.float32))
 
 
 @pytest.mark.parametrize("L", [0, 1, 13])
@@ -243,7 +243,7 @@ def test_constant_values_give_constant_output():
     for b in range(w["cfg"].B):
         ids = w["block_table"][b][: (Lb[b] + 15) // 16]
         for j in range(Lb[b]):
-            w["v_cache"][ids[j // 16], :, :, j % 16] = cv
+            w["v_cache"][ids[j // 16], :, j % 16, :] = cv
     O, _ = oracle.tree_attention(w)
     np.testing.assert_allclose(O, 0.375, rtol=0, atol=1e-14)
 
@@ -478,7 +478,7 @@ def test_pins_catch_planted_oracle_mistakes(monkeypatch):
         test_each_node_is_single_sequence_attention(3, dict(n=12))
     monkeypatch.setattr(T, "gather_prefix", real_gather)
 
-    def swapped_vt(k_cache, v_cache, b, g, L, *, paged, block_table=None):   # V read token-major
+    def swapped_vt(k_cache, v_cache, b, g, L, *, paged, block_table=None):   # V tokens in reverse order
         K, V = real_gather(k_cache, v_cache, b, g, L, paged=paged, block_table=block_table)
         return K, V[::-1]
 

@@ -133,9 +133,9 @@ def tree_build(parent, depth, prefix_len, *, mask=None, pos=None, status=None, s
 def tree_attention(q, k_cache, v_cache, prefix_len, k_tree, v_tree, mask, *, block_table=None,
                    num_blocks=0, scale=0.0, out=None, lse=None, status=None, workspace=None,
                    want_lse=False, stream=None):
-    """Tree attention.  q [B][n][Hq][D]; caches contiguous (k [B][Hkv][Lmax][D],
-    v [B][Hkv][D][Lmax]) or paged when block_table is given (k [blocks][Hkv][16][D],
-    v [blocks][Hkv][D][16]); k_tree, v_tree [B][n][Hkv][D]; mask from tree_build."""
+    """Tree attention.  q [B][n][Hq][D]; caches contiguous (k, v [B][Hkv][Lmax][D]) or
+    paged when block_table is given (k, v [blocks][Hkv][16][D]); k_tree, v_tree
+    [B][n][Hkv][D]; mask from tree_build."""
     B, n, Hq, D = q.shape
     Hkv = k_tree.shape[2]
     paged = block_table is not None

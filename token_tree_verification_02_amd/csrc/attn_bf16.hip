@@ -6,22 +6,27 @@
 // its sequence and to exactly the tree nodes of S_u (the precomputed ancestor
 // bitmask of the kernel-fusion section).  The prefix is attended by all nodes
 // alike, so one workgroup owns a (sequence, KV head, prefix chunk) and streams that
-// KV slice from HBM exactly once for all n*G query rows of the GQA group; the
-// tree keys follow in the same loop with the mask applied, so no separate
-// tree-phase pass or extra partial is needed.
+// KV slice from HBM once for all n*G query rows of the GQA group; the tree keys
+// follow in the same tile stream with the mask applied.
 //
-// Mapping onto the matrix cores (v_mfma_f32_32x32x16_bf16, 64-wide waves):
-//   S^T = K * Q^T : A = 32 keys x 16 d (from LDS), B = Q^T (registers, 32 queries),
-//                   so each lane holds the scores of ONE query column for 16 keys
-//                   and the softmax max/sum is lane-local plus one lane^32 swap.
-//   O^T = V^T * P^T : A = V^T (d x keys, from the d-major V tile in LDS),
-//                   B = P^T straight from the score registers after bf16 rounding.
-//   K rows are stored in LDS with bits 2 and 3 of the row index swapped, which
-//   makes the 8 score registers a lane hands to the PV product cover 8
-//   consecutive keys, so the matching V operand is one 16-byte LDS read.
-// Both tiles use 16-byte-granule XOR swizzles so the MFMA operand reads and the
-// tile writes are bank-conflict free.  Global loads are register-staged into a
-// double-buffered LDS ring (one barrier per tile).  The running max is only moved
+// Data movement: tiles of K and V (token-major, TK keys x D) go HBM -> LDS with
+// global_load_lds_dwordx4 into an S-stage ring, S-1 tiles ahead of the compute,
+// with the vmcnt waits placed by hand (one barrier per tile, no staging
+// registers).  Lanes whose key lies past the prefix (or whose block id is bad)
+// fetch a zero page instead, so NaN-filled unused cache slots are never read.
+//
+// Matrix cores (v_mfma_f32_32x32x16_bf16, 64-wide waves), one 32-query block per
+// wave:
+//   S^T = K * Q^T : A = 32 keys x 16 d (ds_read_b128 from the K tile), B = Q^T in
+//                   registers; a lane holds the scores of ONE query for 16 keys,
+//                   so the softmax max/sum is lane-local plus one lane^32 swap.
+//   O^T = V^T * P^T : A = V^T read with ds_read_b64_tr_b16 (the transposing LDS
+//                   read of gfx950) straight from the token-major V tile, B = P^T
+//                   from the score registers after bf16 rounding.
+//   K rows sit in LDS with bits 2 and 3 of the row index swapped, which makes the
+//   8 score registers a lane hands to the PV product 8 consecutive keys.
+// Both tiles use 16-byte-granule XOR swizzles (different ones for the two read
+// patterns) so operand reads are bank-conflict free.  The running max only moves
 // when a tile raises it by more than 2^8 (exact: the final normalisation uses the
 // same reference), which removes almost all accumulator rescales.
 #include <float.h>
@@ -29,45 +34,82 @@
 #include "tv_internal.h"
 
 namespace tv {
+
+// 1 KB of zeros: the source of every lane whose key is not to be read.
+__device__ __attribute__((aligned(1024))) uint4 tv_zero_page[64];
+
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+#define AS3 __attribute__((address_space(3)))
+#define AS4 __attribute__((address_space(4)))
 
 constexpr float kTau = 8.0f;  // lazy-rescale threshold in the log2 domain
 
 __device__ __forceinline__ int perm_row(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
 
-template <int D, int RB, int KS, int TK>
-struct Cfg {
-  static constexpr int NT = 64 * RB * KS;         // threads per workgroup
-  static constexpr int TKT = TK * KS;             // keys per tile
-  static constexpr int KSLAB = TK * D * 2;        // bytes of one wave's K slab  [TK][D]
-  static constexpr int VSLAB = D * TK * 2;        // bytes of one wave's V slab  [D][TK]
-  static constexpr int STAGE = KS * (KSLAB + VSLAB);
-  static constexpr int CH = TKT * D / 8;          // 16-byte chunks in a K (or V) tile
-  static constexpr int PER = (CH + NT - 1) / NT;  // chunks per thread
-  static constexpr int KB = TK / 32;              // 32-key MFMA blocks per wave tile
-  static constexpr int DB = D / 32;               // 32-row d blocks of O^T
-  static constexpr int SD = D / 16;               // k-steps of the QK^T product
-  static constexpr int VG = TK / 8;               // 16-byte granules per V slab row
-  static constexpr int MERGE = (KS > 1) ? (KS - 1) * RB * 64 * 66 * 4 : 0;
-  static constexpr int LDS = (2 * STAGE > MERGE) ? 2 * STAGE : MERGE;
-  static_assert(TK % 32 == 0 && VG >= 4, "tile");
-};
-
-__device__ __forceinline__ uint64_t pick(uint64_t a0, uint64_t a1, uint64_t a2, uint64_t a3, int w) {
-  return w == 0 ? a0 : (w == 1 ? a1 : (w == 2 ? a2 : a3));
+// HBM -> LDS copy of 16 bytes per lane; lane l lands at lds_line + 16*l.  Issued
+// through asm so the compiler does not add its own (full) waits around it; the
+// kernel waits with explicit vmcnt counts instead.
+__device__ __forceinline__ void dma16(const void* gaddr, uint32_t lds_line) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gaddr),
+               "s"(__builtin_amdgcn_readfirstlane(lds_line))
+               : "m0");
 }
 
-template <int D, int RB, int KS, int TK>
+// Workgroup barrier that orders LDS accesses only (a full fence would also wait
+// for every outstanding HBM load and empty the pipeline).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+template <int D, int RB, int KS, int TK, int S>
+struct Cfg {
+  static constexpr int NT = 64 * RB * KS;      // threads per workgroup
+  static constexpr int ROWB = 2 * D;           // bytes per token row in LDS
+  static constexpr int REG = TK * ROWB;        // bytes of a K (or V) tile region
+  static constexpr int GSTAGE = 2 * REG;       // one group's stage: K region, then V region
+  static constexpr int STAGE = KS * GSTAGE;
+  static constexpr int RING = S * STAGE;
+  static constexpr int LINES = GSTAGE / 1024;  // 1 KB DMA lines per group tile
+  static constexpr int LPW = LINES / RB;       // DMA instructions per wave per tile
+  static constexpr int RPL = 1024 / ROWB;      // token rows per line
+  static constexpr int GPR = D / 8;            // 16-byte granules per row
+  static constexpr int KB = TK / 32;           // 32-key MFMA blocks per tile
+  static constexpr int DB = D / 32;            // 32-row d blocks of O^T
+  static constexpr int SD = D / 16;            // k-steps of the QK^T product
+  static constexpr int MERGE = (KS > 1) ? (KS - 1) * RB * 64 * 66 * 4 : 0;
+  static constexpr int LDS = RING > MERGE ? RING : MERGE;
+  static_assert((LINES / 2) % RB == 0 && LPW * (S - 2) < 64, "pipeline shape");
+  static_assert(TK % 32 == 0 && TK <= 64, "tile");
+};
+
+__device__ __forceinline__ uint32_t pick32(uint64_t w0, uint64_t w1, uint64_t w2, uint64_t w3, int half) {
+  const int w = half >> 1;
+  const uint64_t x = w == 0 ? w0 : (w == 1 ? w1 : (w == 2 ? w2 : w3));
+  return (half & 1) ? (uint32_t)(x >> 32) : (uint32_t)x;
+}
+
+template <int D, int RB, int KS, int TK, int S>
 __global__ __launch_bounds__(64 * RB * KS) void attn_bf16_kernel(AttnArgs a, int rsplit, int nchunks,
                                                                  int chunk_len, int cap) {
-  using C = Cfg<D, RB, KS, TK>;
-  __shared__ __attribute__((aligned(16))) char smem[C::LDS];
+  using C = Cfg<D, RB, KS, TK, S>;
+  __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int rb = wave % RB, ks = wave / RB;
   const int col = lane & 31, hh = lane >> 5;
   const int n = a.n, G = a.G, Hkv = a.Hkv, rows = n * G;
@@ -85,6 +127,7 @@ __global__ __launch_bounds__(64 * RB * KS) void attn_bf16_kernel(AttnArgs a, int
 
   const int Lraw = a.plen[b];
   const int L = Lraw < 0 ? 0 : (Lraw > cap ? cap : Lraw);
+  const AS4 int32_t* btc = (const AS4 int32_t*)a.bt;
 
   if (a.status != nullptr && c == 0 && rs == 0 && g == 0) {
     int bad = (Lraw < 0 || Lraw > cap);
@@ -107,14 +150,88 @@ __global__ __launch_bounds__(64 * RB * KS) void attn_bf16_kernel(AttnArgs a, int
   const int nc_b = L > 0 ? (L + chunk_len - 1) / chunk_len : 1;
   const bool direct = (nc_b == 1);
 
-  const int T_pre = (npre + C::TKT - 1) / C::TKT;
-  const int T_tree = has_tree ? (n + C::TKT - 1) / C::TKT : 0;
-  const int T = T_pre + T_tree;
+  const int T_pre = (npre + TK - 1) / TK;
+  const int T = T_pre + (has_tree ? (n + TK - 1) / TK : 0);
+  const int iters = (T + KS - 1) / KS;
 
-  const uint16_t* __restrict__ kc = (const uint16_t*)a.kc;
-  const uint16_t* __restrict__ vc = (const uint16_t*)a.vc;
-  const uint16_t* __restrict__ ktr = (const uint16_t*)a.kt;
-  const uint16_t* __restrict__ vtr = (const uint16_t*)a.vt;
+  const char* kc = (const char*)a.kc;
+  const char* vc = (const char*)a.vc;
+  const char* ktr = (const char*)a.kt;
+  const char* vtr = (const char*)a.vt;
+  const char* zero = (const char*)tv_zero_page;
+  const uint32_t ring = (uint32_t)(uintptr_t)(AS3 void*)smem;
+
+  // ---- issue the DMA lines this wave owns for tile tt of its group into stage st.
+  // Line q*RB + rb of the group tile belongs to this wave; the first LINES/2 lines
+  // are the K region, so whether an unrolled slot q loads K or V is known at compile
+  // time.  Each lane's source is chosen without branches; keys that must not be
+  // read take the zero page.
+  auto issue = [=](int tt, int st) {
+    const uint32_t gbase = ring + st * C::STAGE + ks * C::GSTAGE;
+    const char* zsrc = zero + lane * 16;
+    if (tt >= T) {  // past the end: keep the vmcnt bookkeeping uniform with zero-page loads
+#pragma unroll
+      for (int q = 0; q < C::LPW; ++q) dma16(zsrc, gbase + (q * RB + rb) * 1024);
+      return;
+    }
+    const int pg = lane % C::GPR;
+    if (tt >= T_pre) {  // tree tile: token-major K_tree / V_tree rows
+      const int tstart = (tt - T_pre) * TK;
+#pragma unroll
+      for (int q = 0; q < C::LPW; ++q) {
+        constexpr int half_lines = C::LINES / 2;
+        const bool isv = q * RB >= half_lines;
+        const int line = q * RB + rb;
+        const int lrow = (isv ? line - half_lines : line) * C::RPL + lane / C::GPR;
+        const int gran = isv ? (pg ^ (2 * (lrow & 3))) : (pg ^ (lrow & 7));
+        const int v = tstart + (isv ? lrow : perm_row(lrow));
+        const char* base = isv ? vtr : ktr;
+        const char* src = base + ((((size_t)b * n + v) * Hkv + g) * D + gran * 8) * 2;
+        dma16(v < n ? src : zsrc, gbase + line * 1024);
+      }
+      return;
+    }
+    const int tstart = k0 + tt * TK;
+    if (a.paged) {
+      // block ids of the tile's 16-token blocks (uniform: scalar loads)
+      const int b0 = tstart >> 4;
+      const AS4 int32_t* row = btc + (size_t)b * a.max_blocks;
+      const int id0 = b0 < a.max_blocks ? row[b0] : -1;
+      const int id1 = b0 + 1 < a.max_blocks ? row[b0 + 1] : -1;
+      const int id2 = (TK > 32 && b0 + 2 < a.max_blocks) ? row[b0 + 2] : -1;
+      const int id3 = (TK > 32 && b0 + 3 < a.max_blocks) ? row[b0 + 3] : -1;
+#pragma unroll
+      for (int q = 0; q < C::LPW; ++q) {
+        constexpr int half_lines = C::LINES / 2;
+        const bool isv = q * RB >= half_lines;
+        const int line = q * RB + rb;
+        const int lrow = (isv ? line - half_lines : line) * C::RPL + lane / C::GPR;
+        const int gran = isv ? (pg ^ (2 * (lrow & 3))) : (pg ^ (lrow & 7));
+        const int key = isv ? lrow : perm_row(lrow);
+        const int j = tstart + key;
+        const int kq = key >> 4;
+        const int blk = kq == 0 ? id0 : (kq == 1 ? id1 : (kq == 2 ? id2 : id3));
+        const bool ok = j < k1 && blk >= 0 && blk < a.num_blocks;
+        const char* base = isv ? vc : kc;
+        const char* src = base + ((((size_t)blk * Hkv + g) * TV_PAGE + (j & 15)) * D + gran * 8) * 2;
+        dma16(ok ? src : zsrc, gbase + line * 1024);
+      }
+    } else {
+      const size_t rowbase = ((size_t)b * Hkv + g) * a.Lmax;
+#pragma unroll
+      for (int q = 0; q < C::LPW; ++q) {
+        constexpr int half_lines = C::LINES / 2;
+        const bool isv = q * RB >= half_lines;
+        const int line = q * RB + rb;
+        const int lrow = (isv ? line - half_lines : line) * C::RPL + lane / C::GPR;
+        const int gran = isv ? (pg ^ (2 * (lrow & 3))) : (pg ^ (lrow & 7));
+        const int j = tstart + (isv ? lrow : perm_row(lrow));
+        const char* base = isv ? vc : kc;
+        const char* src = base + ((rowbase + j) * D + gran * 8) * 2;
+        dma16(j < k1 ? src : zsrc, gbase + line * 1024);
+      }
+    }
+  };
 
   // ---- this lane's query column: operand registers and ancestor mask
   const int qrow = rs * 32 * RB + 32 * rb + col;
@@ -139,108 +256,7 @@ __global__ __launch_bounds__(64 * RB * KS) void attn_bf16_kernel(AttnArgs a, int
     }
   }
 
-  u32x4 kreg[C::PER], vreg[C::PER];
-
-  auto kv_base_contig = [&](void) { return (size_t)(b * Hkv + g); };
-
-  auto load_tile = [&](int tt) {
-    if (tt < T_pre) {
-      const int kt0 = k0 + tt * C::TKT;
-#pragma unroll
-      for (int i = 0; i < C::PER; ++i) {
-        const int ch = tid + i * C::NT;
-        u32x4 kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
-        if (ch < C::CH) {
-          {  // K: chunk -> (key, 8-wide d granule), 16 consecutive lanes read one 256-byte row
-            const int key = ch / (D / 8), dg = ch % (D / 8);
-            const int j = kt0 + key;
-            if (j < k1) {
-              const uint16_t* p = nullptr;
-              if (a.paged) {
-                const int blk = a.bt[(size_t)b * a.max_blocks + (j >> 4)];
-                if (blk >= 0 && blk < a.num_blocks)
-                  p = kc + (((size_t)blk * Hkv + g) * TV_PAGE + (j & 15)) * D + dg * 8;
-              } else {
-                p = kc + (kv_base_contig() * a.Lmax + j) * D + dg * 8;
-              }
-              if (p) kv = *(const u32x4*)p;
-            }
-          }
-          {  // V (d-major cache): chunk -> (d row, 8-token granule)
-            const int d = ch / (C::TKT / 8), kg = ch % (C::TKT / 8);
-            const int j0 = kt0 + kg * 8;
-            if (j0 < k1) {
-              const uint16_t* p = nullptr;
-              if (a.paged) {
-                const int blk = a.bt[(size_t)b * a.max_blocks + (j0 >> 4)];
-                if (blk >= 0 && blk < a.num_blocks)
-                  p = vc + (((size_t)blk * Hkv + g) * D + d) * TV_PAGE + (j0 & 15);
-              } else {
-                p = vc + (kv_base_contig() * D + d) * a.Lmax + j0;
-              }
-              if (p) {
-                vv = *(const u32x4*)p;
-                const int valid = k1 - j0;  // tokens past the prefix may hold NaN: select zero
-                if (valid < 8) {
-#pragma unroll
-                  for (int e = 0; e < 8; ++e)
-                    if (e >= valid) vv[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
-                }
-              }
-            }
-          }
-        }
-        kreg[i] = kv;
-        vreg[i] = vv;
-      }
-    } else {
-      const int v0 = (tt - T_pre) * C::TKT;
-#pragma unroll
-      for (int i = 0; i < C::PER; ++i) {
-        const int ch = tid + i * C::NT;
-        u32x4 kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
-        if (ch < C::CH) {
-          const int key = ch / (D / 8), dg = ch % (D / 8);
-          const int v = v0 + key;
-          if (v < n) {
-            const size_t off = (((size_t)b * n + v) * Hkv + g) * D + dg * 8;
-            kv = *(const u32x4*)(ktr + off);
-            vv = *(const u32x4*)(vtr + off);
-          }
-        }
-        kreg[i] = kv;
-        vreg[i] = vv;
-      }
-    }
-  };
-
-  auto store_tile = [&](int stage, int tt) {
-    char* base = smem + stage * C::STAGE;
-    char* vbase = base + KS * C::KSLAB;
-#pragma unroll
-    for (int i = 0; i < C::PER; ++i) {
-      const int ch = tid + i * C::NT;
-      if (ch < C::CH) {
-        const int key = ch / (D / 8), dg = ch % (D / 8);
-        const int slab = key / TK, row = perm_row(key % TK);
-        *(u32x4*)(base + slab * C::KSLAB + row * (2 * D) + ((dg ^ (row & 7)) << 4)) = kreg[i];
-        if (tt < T_pre) {
-          const int d = ch / (C::TKT / 8), kg = ch % (C::TKT / 8);
-          const int vs = (kg * 8) / TK, gi = kg % C::VG;
-          *(u32x4*)(vbase + vs * C::VSLAB + d * (2 * TK) + ((gi ^ (d & (C::VG - 1))) << 4)) = vreg[i];
-        } else {  // tree V arrives token-major: transpose while writing
-          const int ik = key % TK;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int d = dg * 8 + e;
-            const uint16_t val = (uint16_t)(vreg[i][e >> 1] >> ((e & 1) * 16));
-            *(uint16_t*)(vbase + slab * C::VSLAB + d * (2 * TK) + ((((ik >> 3) ^ (d & (C::VG - 1)))) << 4) +
-                         (ik & 7) * 2) = val;
-          }
-        }
-      }
-    }
-  };
+  wait_vmcnt<0>();  // operands are in registers before the pipeline starts
 
   f32x16 O[C::DB];
 #pragma unroll
@@ -250,45 +266,67 @@ __global__ __launch_bounds__(64 * RB * KS) void attn_bf16_kernel(AttnArgs a, int
   float m_run = -INFINITY, lsum = 0.f;
   const float sl2 = a.scale_log2;
 
-  load_tile(0);
-  store_tile(0, 0);
-  __syncthreads();
+  // prologue: S-1 tiles in flight
+#pragma unroll
+  for (int i = 0; i < S - 1; ++i) issue(i * KS + ks, i);
 
-  for (int tt = 0; tt < T; ++tt) {
-    if (tt + 1 < T) load_tile(tt + 1);
-    {
-      const int stage = tt & 1;
-      const char* Ks = smem + stage * C::STAGE + ks * C::KSLAB;
-      const char* Vs = smem + stage * C::STAGE + KS * C::KSLAB + ks * C::VSLAB;
-      f32x16 S[C::KB];
+  for (int it = 0; it < iters; ++it) {
+    wait_vmcnt<(S - 2) * C::LPW>();  // this wave's lines of iteration `it` have landed
+    lds_barrier();                    // ... everyone's, and everyone left iteration it-1
+    issue((it + S - 1) * KS + ks, (it + S - 1) % S);
+
+    const int tt = it * KS + ks;
+    if (tt < T) {
+      const int st = it % S;
+      const char AS3* Kr = (const char AS3*)(smem) + st * C::STAGE + ks * C::GSTAGE;
+      const char AS3* Vr = Kr + C::REG;
+      f32x16 Sc[C::KB];
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) S[kb][r] = 0.f;
+        for (int r = 0; r < 16; ++r) Sc[kb][r] = 0.f;
         const int row = kb * 32 + col;
 #pragma unroll
         for (int sd = 0; sd < C::SD; ++sd) {
-          const bf16x8 kop = *(const bf16x8*)(Ks + row * (2 * D) + (((2 * sd + hh) ^ (row & 7)) << 4));
-          S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[sd], S[kb], 0, 0, 0);
+          const bf16x8 kop = *(const bf16x8 AS3*)(Kr + row * C::ROWB + (((2 * sd + hh) ^ (row & 7)) << 4));
+          Sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[sd], Sc[kb], 0, 0, 0);
         }
       }
-      // scale, mask, tile max
-      const bool is_tree = tt >= T_pre;
-      const int kbase = is_tree ? (tt - T_pre) * C::TKT + ks * TK : k0 + tt * C::TKT + ks * TK;
-      const int kend = is_tree ? n : k1;
+      // ---- masks (uniform choice of mode per tile), tile max
+      const bool tree = tt >= T_pre;
+      const int tstart = tree ? (tt - T_pre) * TK : k0 + tt * TK;
       float mx = -INFINITY;
+      if (!tree && tstart + TK <= k1) {  // full prefix tile: nothing to mask
 #pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb)
+        for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kbase + kb * 32 + 16 * (r >> 3) + 8 * hh + (r & 7);
-          bool ok = qvalid && key < kend;
-          if (is_tree) ok = ok && ((pick(mw0, mw1, mw2, mw3, key >> 6) >> (key & 63)) & 1);
-          const float x = ok ? S[kb][r] * sl2 : -INFINITY;
-          S[kb][r] = x;
-          mx = fmaxf(mx, x);
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, Sc[kb][r]);
+      } else if (!tree) {  // last prefix tile: keys past the prefix end
+        const int lim = k1 - tstart;
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int ko = kb * 32 + 16 * (r >> 3) + 8 * hh + (r & 7);
+            Sc[kb][r] = ko < lim ? Sc[kb][r] : -INFINITY;
+            mx = fmaxf(mx, Sc[kb][r]);
+          }
+      } else {  // tree tile: ancestor bits of this lane's node
+        const int lim = n - tstart;
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb) {
+          const uint32_t w32 = pick32(mw0, mw1, mw2, mw3, (tstart + kb * 32) >> 5);
+          const uint32_t bits = w32 >> (8 * hh);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int ko = kb * 32 + 16 * (r >> 3) + 8 * hh + (r & 7);
+            const bool ok = ko < lim && ((bits >> (16 * (r >> 3) + (r & 7))) & 1u);
+            Sc[kb][r] = ok ? Sc[kb][r] : -INFINITY;
+            mx = fmaxf(mx, Sc[kb][r]);
+          }
         }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;  // scale > 0 commutes with max
       if (__any(mx > m_run + kTau)) {
         const float m_new = fmaxf(m_run, mx);
         const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
@@ -300,12 +338,14 @@ __global__ __launch_bounds__(64 * RB * KS) void attn_bf16_kernel(AttnArgs a, int
         m_run = m_new;
       }
       const float msub = (m_run == -INFINITY) ? 0.f : m_run;
+      const int l16 = lane & 15;
+      const int mhalf = (lane >> 4) & 1;
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb) {
         bf16x8 pop[2];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(S[kb][r] - msub);
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(Sc[kb][r], sl2, -msub));
           lsum += p;
           pop[r >> 3][r & 7] = (__bf16)p;
         }
@@ -313,19 +353,26 @@ __global__ __launch_bounds__(64 * RB * KS) void attn_bf16_kernel(AttnArgs a, int
         for (int half = 0; half < 2; ++half)
 #pragma unroll
           for (int db = 0; db < C::DB; ++db) {
-            const int drow = 32 * db + col;
-            const int gran = (kb * 4 + half * 2 + hh) ^ (drow & (C::VG - 1));
-            const bf16x8 vop = *(const bf16x8*)(Vs + drow * (2 * TK) + (gran << 4));
+            s16x4 v4[2];
+#pragma unroll
+            for (int q4 = 0; q4 < 2; ++q4) {
+              const int vrow = kb * 32 + 16 * half + 8 * hh + 4 * q4 + (l16 >> 2);
+              const int gran = (4 * db + 2 * mhalf + ((lane & 3) >> 1)) ^ (2 * (vrow & 3));
+              const char AS3* p = Vr + vrow * C::ROWB + (gran << 4) + ((lane & 1) << 3);
+              v4[q4] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 AS3*)p);
+            }
+            const s16x8 v8 = __builtin_shufflevector(v4[0], v4[1], 0, 1, 2, 3, 4, 5, 6, 7);
+            const bf16x8 vop = __builtin_bit_cast(bf16x8, v8);
             O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop[half], O[db], 0, 0, 0);
           }
       }
     }
-    if (tt + 1 < T) store_tile((tt + 1) & 1, tt + 1);
-    __syncthreads();
   }
+  wait_vmcnt<0>();  // drain the trailing zero-page loads before LDS is reused or released
 
-  // ---- combine the key-split waves of each query block
+  // ---- combine the key-split groups of each query block
   if constexpr (KS > 1) {
+    lds_barrier();
     float* mb = (float*)smem;
     if (ks > 0) {
       float* dst = mb + (((ks - 1) * RB + rb) * 64 + lane) * 66;
@@ -336,7 +383,7 @@ __global__ __launch_bounds__(64 * RB * KS) void attn_bf16_kernel(AttnArgs a, int
       dst[64] = m_run;
       dst[65] = lsum;
     }
-    __syncthreads();
+    lds_barrier();
     if (ks > 0) return;
 #pragma unroll
     for (int k = 1; k < KS; ++k) {
@@ -389,21 +436,21 @@ __global__ __launch_bounds__(64 * RB * KS) void attn_bf16_kernel(AttnArgs a, int
   }
 }
 
-template <int D, int RB, int KS, int TK>
+template <int D, int RB, int KS, int TK, int S>
 hipError_t launch_cfg(const AttnArgs& a, const AttnPlan& p, hipStream_t s) {
   const int grid = a.B * a.Hkv * p.nchunks * p.rsplit;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((attn_bf16_kernel<D, RB, KS, TK>), dim3(grid), dim3(64 * RB * KS), 0, s, a, p.rsplit,
+  hipLaunchKernelGGL((attn_bf16_kernel<D, RB, KS, TK, S>), dim3(grid), dim3(64 * RB * KS), 0, s, a, p.rsplit,
                      p.nchunks, p.chunk_len, p.cap);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_d(const AttnArgs& a, const AttnPlan& p, hipStream_t s) {
-  if (p.rb == 1) return launch_cfg<D, 1, 4, 32>(a, p, s);
-  if (p.rb == 2) return launch_cfg<D, 2, 2, 32>(a, p, s);
-  if (p.rb == 4) return launch_cfg<D, 4, 1, 64>(a, p, s);
-  return launch_cfg<D, 8, 1, 64>(a, p, s);
+  if (p.rb == 1) return launch_cfg<D, 1, 2, 32, 4>(a, p, s);
+  if (p.rb == 2) return launch_cfg<D, 2, 2, 32, 4>(a, p, s);
+  if (p.rb == 4) return launch_cfg<D, 4, 1, 64, 4>(a, p, s);
+  return launch_cfg<D, 8, 1, 64, 4>(a, p, s);
 }
 
 }  // namespace

@@ -2,7 +2,8 @@
 //
 // The fp32 path serves fp32 workloads (small models, tests at full precision):
 // one wave per (sequence, node, query head).  Keys are spread over the 64 lanes
-// for the scores, values over lanes by head dimension for the weighted sum, with
+// for the scores, values over lanes by head dimension for the weighted sum (each step reads a
+// 64-token run of one head-dim column), with
 // the usual running max / running sum of an online softmax over 64-key chunks.
 // The set attended is the same as the bf16 path: every cached prefix token plus
 // the tree nodes whose bit is set in the node's ancestor mask (SpecInfer
@@ -79,9 +80,9 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a, int cap) {
     if (a.paged) {
       const int blk = a.bt[(size_t)b * a.max_blocks + (j >> 4)];
       if (blk < 0 || blk >= a.num_blocks) return 0.f;
-      return vc[(((size_t)blk * Hkv + g) * D + d) * TV_PAGE + (j & 15)];
+      return vc[(((size_t)blk * Hkv + g) * TV_PAGE + (j & 15)) * D + d];
     }
-    return vc[(((size_t)b * Hkv + g) * D + d) * a.Lmax + j];
+    return vc[(((size_t)b * Hkv + g) * a.Lmax + j) * D + d];
   };
   // fold one chunk of scores (lane = key) into the running state
   auto fold = [&](float s, bool valid, int cnt, auto&& value_of) {

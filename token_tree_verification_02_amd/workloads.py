@@ -14,10 +14,8 @@ round-to-nearest-even where the workload is bf16.
 
 Layouts (last dimension contiguous, matching ``include/tree_verify.h``):
   q, k_tree, v_tree     [B][n][H][D]
-  k_cache contiguous    [B][Hkv][Lmax][D]   token-major
-  v_cache contiguous    [B][Hkv][D][Lmax]   d-major
-  k_cache paged         [num_blocks][Hkv][16][D]
-  v_cache paged         [num_blocks][Hkv][D][16]
+  k_cache, v_cache contiguous    [B][Hkv][Lmax][D]
+  k_cache, v_cache paged         [num_blocks][Hkv][16][D]
   block_table           [B][max_blocks]  int32, -1 where unused
   logits                [B][n][V]
 Cache slots past a sequence's prefix length hold NaN, so a kernel that reads
@@ -313,7 +311,7 @@ def make(cfg: Config, seed: int | None = None, *, variant: str = "plain", plant:
         perm = _rng(seed, _S_PERM).permutation(total_blocks).astype(np.int32)
         bt = np.full((B, max_blocks), -1, np.int32)
         k_cache = np.full((total_blocks, Hkv, PAGE, D), _nan(dt), edt)
-        v_cache = np.full((total_blocks, Hkv, D, PAGE), _nan(dt), edt)
+        v_cache = np.full((total_blocks, Hkv, PAGE, D), _nan(dt), edt)
         bo = 0
         for b in range(B):
             L = int(prefix_len[b])
@@ -325,23 +323,23 @@ def make(cfg: Config, seed: int | None = None, *, variant: str = "plain", plant:
             full = L // PAGE
             if full:
                 k_cache[ids[:full]] = kv[:full * PAGE].reshape(full, PAGE, Hkv, D).transpose(0, 2, 1, 3)
-                v_cache[ids[:full]] = vv[:full * PAGE].reshape(full, PAGE, Hkv, D).transpose(0, 2, 3, 1)
+                v_cache[ids[:full]] = vv[:full * PAGE].reshape(full, PAGE, Hkv, D).transpose(0, 2, 1, 3)
             rem = L - full * PAGE
             if rem:
                 blk = ids[full]
                 k_cache[blk, :, :rem, :] = kv[full * PAGE:].transpose(1, 0, 2)
-                v_cache[blk, :, :, :rem] = vv[full * PAGE:].transpose(1, 2, 0)
+                v_cache[blk, :, :rem, :] = vv[full * PAGE:].transpose(1, 0, 2)
         out.update(block_table=bt, max_blocks=max_blocks, num_blocks=total_blocks, Lmax=0)
     else:
         Lmax = cfg.capacity
         k_cache = np.full((B, Hkv, Lmax, D), _nan(dt), edt)
-        v_cache = np.full((B, Hkv, D, Lmax), _nan(dt), edt)
+        v_cache = np.full((B, Hkv, Lmax, D), _nan(dt), edt)
         for b in range(B):
             L = int(prefix_len[b])
             kv = kvals[offs[b] * Hkv * D:offs[b + 1] * Hkv * D].reshape(L, Hkv, D)
             vv = vvals[offs[b] * Hkv * D:offs[b + 1] * Hkv * D].reshape(L, Hkv, D)
             k_cache[b, :, :L, :] = kv.transpose(1, 0, 2)
-            v_cache[b, :, :, :L] = vv.transpose(1, 2, 0)
+            v_cache[b, :, :L, :] = vv.transpose(1, 0, 2)
         out.update(block_table=None, max_blocks=0, num_blocks=0, Lmax=Lmax)
     del kvals, vvals
     if not poison:
