@@ -89,6 +89,7 @@ def main():
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--copies", type=int, default=0, help="input copies to rotate (0 = auto)")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--eager", action="store_true", help="launch each step eagerly instead of replaying a HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of this many MiB (counter calibration) and exit")
@@ -124,33 +125,53 @@ def main():
     per_copy = refb["attn_bytes"] + refb["verify_bytes"]
     R = args.copies or max(1, math.ceil(2 * MALL_BYTES / per_copy))
     copies = [runner.upload(w) for _ in range(R)]
+    steps = [runner.Step(d) for d in copies]
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
 
-    for i in range(args.warmup):
-        runner.step(copies[i % R])
-    torch.cuda.synchronize()
-
+    # per-kernel durations: HIP events on the launch stream around each C-ABI call
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    for i in range(args.warmup):
+        steps[i % R]()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
     for k in range(K):
-        d = copies[k % R]
-        e = ev[k]
+        st, e = steps[k % R], ev[k]
         e[0].record(stream)
-        runner.build(d)
+        st.build(sh)
         e[1].record(stream)
-        runner.attention(d)
+        st.attention(sh)
         e[2].record(stream)
-        if "argmax" in d:
-            runner.verify(d)
+        st.verify(sh)
         e[3].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     t_build = np.mean([e[0].elapsed_time(e[1]) for e in ev]) * 1e-3
     t_attn = np.mean([e[1].elapsed_time(e[2]) for e in ev]) * 1e-3
     t_ver = np.mean([e[2].elapsed_time(e[3]) for e in ev]) * 1e-3
+
+    # throughput: K whole steps back to back.  Default: one HIP graph holding one step
+    # per input copy (R steps), replayed K/R times; --eager launches each call.
+    if args.eager:
+        for i in range(args.warmup):
+            steps[i % R]()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(K):
+            steps[k % R]()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    else:
+        K = max(R, K // R * R)
+        graph = runner.capture_steps(steps)
+        for i in range(max(1, args.warmup // R)):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(K // R):
+            graph.replay()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
     ms_step = wall / K * 1e3
     tokens = cfg.B * cfg.n
     value = tokens / (wall / K)
@@ -171,7 +192,7 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic (seeded, N(0,1) Q/K/V)",
         "config": {"workload": cfg.name, "B": cfg.B, "n": cfg.n, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "D": cfg.D,
                    "prefix_len": [cfg.L_lo, cfg.L_hi], "paged": cfg.paged, "vocab": cfg.vocab,
-                   "input_copies": R},
+                   "input_copies": R, "launch": "eager" if args.eager else "hip_graph"},
         "roofline": roofline,
         "attn_hbm_gbs": round(attn_gbs, 1), "mfma_util_pct": round(mfma_pct, 2),
         "kernel_us": {"tree_build": round(t_build * 1e6, 2), "tree_attention": round(t_attn * 1e6, 2),

@@ -208,3 +208,38 @@ def test_full_size_sampled(index):
     if cfg.vocab:
         log("  oracle verification")
         check_verify(w, d)
+
+
+def test_graph_replay_matches_eager():
+    """A HIP-graph replay of the step gives the eager outputs, on every replay,
+    with eager work and synchronisations between replays."""
+    log("case graph replay")
+    w = W.make(W.config(4, B=3, L_lo=100, L_hi=2500, vocab=0), seed=12)
+    d = runner.upload(w)
+    st = runner.Step(d)
+    st()
+    torch.cuda.synchronize()
+    ref = d["out"].clone(), d["lse"].clone(), d["mask"].clone()
+    g = st.capture()
+    for rep in range(4):
+        d["out"].zero_()
+        d["lse"].zero_()
+        d["mask"].zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(d["out"], ref[0]) and torch.equal(d["lse"], ref[1]) and torch.equal(d["mask"], ref[2])
+    w2 = W.make(W.config(2, B=2, L_lo=300, L_hi=300), seed=3)
+    d2 = runner.upload(w2)
+    st2 = runner.Step(d2)
+    st2()
+    torch.cuda.synchronize()
+    ref2 = [d2[k].clone() for k in ("argmax", "path", "path_len", "bonus", "out")]
+    g2 = st2.capture()
+    for rep in range(3):
+        for k in ("argmax", "path", "path_len", "bonus", "out"):
+            d2[k].zero_()
+        g2.replay()
+        torch.cuda.synchronize()
+        for k, r in zip(("argmax", "path", "path_len", "bonus", "out"), ref2):
+            assert torch.equal(d2[k], r), k

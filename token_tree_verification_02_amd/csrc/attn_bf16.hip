@@ -12,8 +12,10 @@
 // Data movement: tiles of K and V (token-major, TK keys x D) go HBM -> LDS with
 // global_load_lds_dwordx4 into an S-stage ring, S-1 tiles ahead of the compute,
 // with the vmcnt waits placed by hand (one barrier per tile, no staging
-// registers).  Lanes whose key lies past the prefix (or whose block id is bad)
-// fetch a zero page instead, so NaN-filled unused cache slots are never read.
+// registers).  Full prefix tiles use the scalar-base form of the load with
+// per-lane offsets computed once; the last prefix tile and the tree tiles take
+// per-lane addresses, and lanes whose key lies past the prefix (or whose block
+// id is bad) fetch a zero page, so NaN-filled unused cache slots are never read.
 //
 // Matrix cores (v_mfma_f32_32x32x16_bf16, 64-wide waves), one 32-query block per
 // wave:
@@ -23,20 +25,26 @@
 //   O^T = V^T * P^T : A = V^T read with ds_read_b64_tr_b16 (the transposing LDS
 //                   read of gfx950) straight from the token-major V tile, B = P^T
 //                   from the score registers after bf16 rounding.
+//   The QK^T products of a tile's key blocks run as independent accumulator
+//   chains stepped together, so back-to-back MFMAs do not wait on each other;
+//   the softmax and PV product then go block by block.
 //   K rows sit in LDS with bits 2 and 3 of the row index swapped, which makes the
 //   8 score registers a lane hands to the PV product 8 consecutive keys.
-// Both tiles use 16-byte-granule XOR swizzles (different ones for the two read
-// patterns) so operand reads are bank-conflict free.  The running max only moves
-// when a tile raises it by more than 2^8 (exact: the final normalisation uses the
-// same reference), which removes almost all accumulator rescales.
+// The LDS has 64 banks of 4 bytes.  K and V tiles use 16-byte-granule XOR
+// swizzles chosen for their read patterns (16 K rows per ds_read_b128 cycle, 4 V
+// rows x 4 granules per ds_read_b64_tr_b16 cycle) so operand reads are
+// conflict free.  The running max only moves when a block raises it by more than
+// 2^8 (exact: the final normalisation uses the same reference), which removes
+// almost all accumulator rescales.
 #include <float.h>
 
 #include "tv_internal.h"
 
 namespace tv {
 
-// 1 KB of zeros: the source of every lane whose key is not to be read.
-__device__ __attribute__((aligned(1024))) uint4 tv_zero_page[64];
+// Zeros: the source of every lane (or line) whose key is not to be read.  4 KB
+// covers the per-lane offsets of one 16-token paged block line.
+__device__ __attribute__((aligned(4096))) uint4 tv_zero_page[256];
 
 namespace {
 
@@ -52,6 +60,16 @@ constexpr float kTau = 8.0f;  // lazy-rescale threshold in the log2 domain
 
 __device__ __forceinline__ int perm_row(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
 
+// Granule swizzles (16-byte granules within a token row of the tile).
+template <int D>
+__device__ __forceinline__ int kswz(int row) {  // 16 consecutive rows -> 16 distinct bank groups
+  return D == 128 ? (row & 15) : ((row >> 1) & 7);
+}
+template <int D>
+__device__ __forceinline__ int vswz(int row) {  // 4 consecutive rows x 4 granules -> distinct
+  return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
+}
+
 // HBM -> LDS copy of 16 bytes per lane; lane l lands at lds_line + 16*l.  Issued
 // through asm so the compiler does not add its own (full) waits around it; the
 // kernel waits with explicit vmcnt counts instead.
@@ -60,6 +78,21 @@ __device__ __forceinline__ void dma16(const void* gaddr, uint32_t lds_line) {
                "s"(__builtin_amdgcn_readfirstlane(lds_line))
                : "m0");
 }
+// Same with a wave-uniform 64-bit base and a per-lane 32-bit byte offset.
+__device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, uint32_t lds_line) {
+  const uint64_t b = (uint64_t)sbase;
+  const uint64_t ub = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(ub),
+               "s"(__builtin_amdgcn_readfirstlane(lds_line))
+               : "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
 
 // Workgroup barrier that orders LDS accesses only (a full fence would also wait
 // for every outstanding HBM load and empty the pipeline).
@@ -67,12 +100,6 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
 template <int D, int RB, int KS, int TK, int S>
@@ -84,6 +111,7 @@ struct Cfg {
   static constexpr int STAGE = KS * GSTAGE;
   static constexpr int RING = S * STAGE;
   static constexpr int LINES = GSTAGE / 1024;  // 1 KB DMA lines per group tile
+  static constexpr int HL = LINES / 2;         // lines of the K region
   static constexpr int LPW = LINES / RB;       // DMA instructions per wave per tile
   static constexpr int RPL = 1024 / ROWB;      // token rows per line
   static constexpr int GPR = D / 8;            // 16-byte granules per row
@@ -92,8 +120,8 @@ struct Cfg {
   static constexpr int SD = D / 16;            // k-steps of the QK^T product
   static constexpr int MERGE = (KS > 1) ? (KS - 1) * RB * 64 * 66 * 4 : 0;
   static constexpr int LDS = RING > MERGE ? RING : MERGE;
-  static_assert((LINES / 2) % RB == 0 && LPW * (S - 2) < 64, "pipeline shape");
-  static_assert(TK % 32 == 0 && TK <= 64, "tile");
+  static_assert(HL % RB == 0 && LPW * (S - 2) < 64, "pipeline shape");
+  static_assert(TK % 32 == 0 && TK <= 64 && 16 % RPL == 0, "tile");
 };
 
 __device__ __forceinline__ uint32_t pick32(uint64_t w0, uint64_t w1, uint64_t w2, uint64_t w3, int half) {
@@ -160,12 +188,27 @@ __global__ __launch_bounds__(64 * RB * KS) void attn_bf16_kernel(AttnArgs a, int
   const char* vtr = (const char*)a.vt;
   const char* zero = (const char*)tv_zero_page;
   const uint32_t ring = (uint32_t)(uintptr_t)(AS3 void*)smem;
+  const size_t rowbase = ((size_t)b * Hkv + g) * a.Lmax;  // contiguous cache row of token 0
 
-  // ---- issue the DMA lines this wave owns for tile tt of its group into stage st.
-  // Line q*RB + rb of the group tile belongs to this wave; the first LINES/2 lines
-  // are the K region, so whether an unrolled slot q loads K or V is known at compile
-  // time.  Each lane's source is chosen without branches; keys that must not be
-  // read take the zero page.
+  // ---- per-lane DMA geometry: line q*RB + rb of the group tile belongs to this
+  // wave; the first HL lines are the K region, so whether slot q loads K or V is
+  // known at compile time.
+  int lrow_[C::LPW], gran_[C::LPW];
+  uint32_t voff[C::LPW];  // byte offset of this lane's granule from the line's base (full tiles)
+#pragma unroll
+  for (int q = 0; q < C::LPW; ++q) {
+    const bool isv = q * RB >= C::HL;
+    const int line = q * RB + rb;
+    const int lrow = (isv ? line - C::HL : line) * C::RPL + lane / C::GPR;
+    const int pg = lane % C::GPR;
+    const int gran = isv ? (pg ^ vswz<D>(lrow)) : (pg ^ kswz<D>(lrow));
+    const int key = isv ? lrow : perm_row(lrow);
+    lrow_[q] = lrow;
+    gran_[q] = gran;
+    voff[q] = (uint32_t)(((a.paged ? (key & 15) : key) * D + gran * 8) * 2);
+  }
+
+  // ---- issue the DMA lines this wave owns for tile tt of its group into stage st
   auto issue = [=](int tt, int st) {
     const uint32_t gbase = ring + st * C::STAGE + ks * C::GSTAGE;
     const char* zsrc = zero + lane * 16;
@@ -174,24 +217,19 @@ __global__ __launch_bounds__(64 * RB * KS) void attn_bf16_kernel(AttnArgs a, int
       for (int q = 0; q < C::LPW; ++q) dma16(zsrc, gbase + (q * RB + rb) * 1024);
       return;
     }
-    const int pg = lane % C::GPR;
-    if (tt >= T_pre) {  // tree tile: token-major K_tree / V_tree rows
+    if (tt >= T_pre) {  // tree tile: token-major K_tree / V_tree rows, per-lane addresses
       const int tstart = (tt - T_pre) * TK;
 #pragma unroll
       for (int q = 0; q < C::LPW; ++q) {
-        constexpr int half_lines = C::LINES / 2;
-        const bool isv = q * RB >= half_lines;
-        const int line = q * RB + rb;
-        const int lrow = (isv ? line - half_lines : line) * C::RPL + lane / C::GPR;
-        const int gran = isv ? (pg ^ (2 * (lrow & 3))) : (pg ^ (lrow & 7));
-        const int v = tstart + (isv ? lrow : perm_row(lrow));
-        const char* base = isv ? vtr : ktr;
-        const char* src = base + ((((size_t)b * n + v) * Hkv + g) * D + gran * 8) * 2;
-        dma16(v < n ? src : zsrc, gbase + line * 1024);
+        const bool isv = q * RB >= C::HL;
+        const int v = tstart + (isv ? lrow_[q] : perm_row(lrow_[q]));
+        const char* src = (isv ? vtr : ktr) + ((((size_t)b * n + v) * Hkv + g) * D + gran_[q] * 8) * 2;
+        dma16(v < n ? src : zsrc, gbase + (q * RB + rb) * 1024);
       }
       return;
     }
     const int tstart = k0 + tt * TK;
+    const bool full = tstart + TK <= k1;
     if (a.paged) {
       // block ids of the tile's 16-token blocks (uniform: scalar loads)
       const int b0 = tstart >> 4;
@@ -202,33 +240,32 @@ __global__ __launch_bounds__(64 * RB * KS) void attn_bf16_kernel(AttnArgs a, int
       const int id3 = (TK > 32 && b0 + 3 < a.max_blocks) ? row[b0 + 3] : -1;
 #pragma unroll
       for (int q = 0; q < C::LPW; ++q) {
-        constexpr int half_lines = C::LINES / 2;
-        const bool isv = q * RB >= half_lines;
+        const bool isv = q * RB >= C::HL;
         const int line = q * RB + rb;
-        const int lrow = (isv ? line - half_lines : line) * C::RPL + lane / C::GPR;
-        const int gran = isv ? (pg ^ (2 * (lrow & 3))) : (pg ^ (lrow & 7));
-        const int key = isv ? lrow : perm_row(lrow);
-        const int j = tstart + key;
-        const int kq = key >> 4;
+        const int kq = ((isv ? line - C::HL : line) * C::RPL) >> 4;  // 16-token block of the whole line
         const int blk = kq == 0 ? id0 : (kq == 1 ? id1 : (kq == 2 ? id2 : id3));
-        const bool ok = j < k1 && blk >= 0 && blk < a.num_blocks;
-        const char* base = isv ? vc : kc;
-        const char* src = base + ((((size_t)blk * Hkv + g) * TV_PAGE + (j & 15)) * D + gran * 8) * 2;
-        dma16(ok ? src : zsrc, gbase + line * 1024);
+        const bool bok = blk >= 0 && blk < a.num_blocks;
+        const char* lbase = (isv ? vc : kc) + ((size_t)blk * Hkv + g) * TV_PAGE * D * 2;
+        if (full) {
+          dma16s(bok ? lbase : zero, voff[q], gbase + line * 1024);
+        } else {
+          const int j = tstart + (isv ? lrow_[q] : perm_row(lrow_[q]));
+          dma16(bok && j < k1 ? lbase + voff[q] : zsrc, gbase + line * 1024);
+        }
       }
     } else {
-      const size_t rowbase = ((size_t)b * Hkv + g) * a.Lmax;
+      const char* kb = kc + (rowbase + tstart) * D * 2;
+      const char* vb = vc + (rowbase + tstart) * D * 2;
 #pragma unroll
       for (int q = 0; q < C::LPW; ++q) {
-        constexpr int half_lines = C::LINES / 2;
-        const bool isv = q * RB >= half_lines;
+        const bool isv = q * RB >= C::HL;
         const int line = q * RB + rb;
-        const int lrow = (isv ? line - half_lines : line) * C::RPL + lane / C::GPR;
-        const int gran = isv ? (pg ^ (2 * (lrow & 3))) : (pg ^ (lrow & 7));
-        const int j = tstart + (isv ? lrow : perm_row(lrow));
-        const char* base = isv ? vc : kc;
-        const char* src = base + ((rowbase + j) * D + gran * 8) * 2;
-        dma16(j < k1 ? src : zsrc, gbase + line * 1024);
+        if (full) {
+          dma16s(isv ? vb : kb, voff[q], gbase + line * 1024);
+        } else {
+          const int j = tstart + (isv ? lrow_[q] : perm_row(lrow_[q]));
+          dma16(j < k1 ? (isv ? vb : kb) + voff[q] : zsrc, gbase + line * 1024);
+        }
       }
     }
   };
@@ -255,8 +292,21 @@ __global__ __launch_bounds__(64 * RB * KS) void attn_bf16_kernel(AttnArgs a, int
       if (a.W > 3) mw3 = mp[3];
     }
   }
-
   wait_vmcnt<0>();  // operands are in registers before the pipeline starts
+
+  // ---- per-lane LDS read offsets (the key-block and stage parts are added later)
+  uint32_t kofs[C::SD], vofs[C::DB];
+#pragma unroll
+  for (int sd = 0; sd < C::SD; ++sd) kofs[sd] = col * C::ROWB + (((2 * sd + hh) ^ kswz<D>(col)) << 4);
+  {
+    const int l16 = lane & 15, mhalf = (lane >> 4) & 1;
+    const int vr = 8 * hh + (l16 >> 2);  // row within a 16-key half block (multiples of 4 added later)
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) {
+      const int lg = 4 * db + 2 * mhalf + ((lane & 3) >> 1);
+      vofs[db] = vr * C::ROWB + ((lg ^ vswz<D>(vr)) << 4) + ((lane & 1) << 3);
+    }
+  }
 
   f32x16 O[C::DB];
 #pragma unroll
@@ -280,72 +330,79 @@ __global__ __launch_bounds__(64 * RB * KS) void attn_bf16_kernel(AttnArgs a, int
       const int st = it % S;
       const char AS3* Kr = (const char AS3*)(smem) + st * C::STAGE + ks * C::GSTAGE;
       const char AS3* Vr = Kr + C::REG;
-      f32x16 Sc[C::KB];
-#pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) Sc[kb][r] = 0.f;
-        const int row = kb * 32 + col;
-#pragma unroll
-        for (int sd = 0; sd < C::SD; ++sd) {
-          const bf16x8 kop = *(const bf16x8 AS3*)(Kr + row * C::ROWB + (((2 * sd + hh) ^ (row & 7)) << 4));
-          Sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[sd], Sc[kb], 0, 0, 0);
-        }
-      }
-      // ---- masks (uniform choice of mode per tile), tile max
       const bool tree = tt >= T_pre;
       const int tstart = tree ? (tt - T_pre) * TK : k0 + tt * TK;
-      float mx = -INFINITY;
-      if (!tree && tstart + TK <= k1) {  // full prefix tile: nothing to mask
+      const int lim = tree ? n - tstart : k1 - tstart;  // keys of this tile that exist
+      const bool full = !tree && lim >= TK;
+
+      // QK^T of the tile's key blocks as independent accumulator chains, stepped
+      // together over the head dimension, so consecutive MFMAs never wait on each
+      // other and each K operand read has a full step of lead time.  A single
+      // 32-key block uses two half-sum chains (even / odd steps) instead.
+      f32x16 Sacc[C::KB > 1 ? C::KB : 2];
 #pragma unroll
-        for (int kb = 0; kb < C::KB; ++kb)
+      for (int i = 0; i < (C::KB > 1 ? C::KB : 2); ++i)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, Sc[kb][r]);
-      } else if (!tree) {  // last prefix tile: keys past the prefix end
-        const int lim = k1 - tstart;
+        for (int r = 0; r < 16; ++r) Sacc[i][r] = 0.f;
 #pragma unroll
-        for (int kb = 0; kb < C::KB; ++kb)
+      for (int sd = 0; sd < C::SD; ++sd) {
+        if constexpr (C::KB > 1) {
+#pragma unroll
+          for (int kb = 0; kb < C::KB; ++kb) {
+            const bf16x8 kop = *(const bf16x8 AS3*)(Kr + kb * 32 * C::ROWB + kofs[sd]);
+            Sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[sd], Sacc[kb], 0, 0, 0);
+          }
+        } else {
+          const bf16x8 kop = *(const bf16x8 AS3*)(Kr + kofs[sd]);
+          Sacc[sd & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[sd], Sacc[sd & 1], 0, 0, 0);
+        }
+      }
+      if constexpr (C::KB == 1) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) Sacc[0][r] += Sacc[1][r];
+      }
+
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb) {
+        f32x16 Scur = Sacc[kb];
+        // ---- mask (uniform choice of mode per tile) and block max
+        float mx = -INFINITY;
+        if (full) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, Scur[r]);
+        } else if (!tree) {  // last prefix tile: keys past the prefix end
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int ko = kb * 32 + 16 * (r >> 3) + 8 * hh + (r & 7);
-            Sc[kb][r] = ko < lim ? Sc[kb][r] : -INFINITY;
-            mx = fmaxf(mx, Sc[kb][r]);
+            Scur[r] = ko < lim ? Scur[r] : -INFINITY;
+            mx = fmaxf(mx, Scur[r]);
           }
-      } else {  // tree tile: ancestor bits of this lane's node
-        const int lim = n - tstart;
-#pragma unroll
-        for (int kb = 0; kb < C::KB; ++kb) {
-          const uint32_t w32 = pick32(mw0, mw1, mw2, mw3, (tstart + kb * 32) >> 5);
-          const uint32_t bits = w32 >> (8 * hh);
+        } else {  // tree tile: ancestor bits of this lane's node
+          const uint32_t bits = pick32(mw0, mw1, mw2, mw3, (tstart + kb * 32) >> 5) >> (8 * hh);
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int ko = kb * 32 + 16 * (r >> 3) + 8 * hh + (r & 7);
             const bool ok = ko < lim && ((bits >> (16 * (r >> 3) + (r & 7))) & 1u);
-            Sc[kb][r] = ok ? Sc[kb][r] : -INFINITY;
-            mx = fmaxf(mx, Sc[kb][r]);
+            Scur[r] = ok ? Scur[r] : -INFINITY;
+            mx = fmaxf(mx, Scur[r]);
           }
         }
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;  // scale > 0 commutes with max
-      if (__any(mx > m_run + kTau)) {
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-        lsum *= alpha;
+        mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;  // scale > 0 commutes with max
+        if (__any(mx > m_run + kTau)) {
+          const float m_new = fmaxf(m_run, mx);
+          const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+          lsum *= alpha;
 #pragma unroll
-        for (int db = 0; db < C::DB; ++db)
+          for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) O[db][r] *= alpha;
-        m_run = m_new;
-      }
-      const float msub = (m_run == -INFINITY) ? 0.f : m_run;
-      const int l16 = lane & 15;
-      const int mhalf = (lane >> 4) & 1;
-#pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb) {
+            for (int r = 0; r < 16; ++r) O[db][r] *= alpha;
+          m_run = m_new;
+        }
+        const float msub = (m_run == -INFINITY) ? 0.f : m_run;
         bf16x8 pop[2];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(Sc[kb][r], sl2, -msub));
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(Scur[r], sl2, -msub));
           lsum += p;
           pop[r >> 3][r & 7] = (__bf16)p;
         }
@@ -353,17 +410,12 @@ __global__ __launch_bounds__(64 * RB * KS) void attn_bf16_kernel(AttnArgs a, int
         for (int half = 0; half < 2; ++half)
 #pragma unroll
           for (int db = 0; db < C::DB; ++db) {
-            s16x4 v4[2];
-#pragma unroll
-            for (int q4 = 0; q4 < 2; ++q4) {
-              const int vrow = kb * 32 + 16 * half + 8 * hh + 4 * q4 + (l16 >> 2);
-              const int gran = (4 * db + 2 * mhalf + ((lane & 3) >> 1)) ^ (2 * (vrow & 3));
-              const char AS3* p = Vr + vrow * C::ROWB + (gran << 4) + ((lane & 1) << 3);
-              v4[q4] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 AS3*)p);
-            }
-            const s16x8 v8 = __builtin_shufflevector(v4[0], v4[1], 0, 1, 2, 3, 4, 5, 6, 7);
-            const bf16x8 vop = __builtin_bit_cast(bf16x8, v8);
-            O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop[half], O[db], 0, 0, 0);
+            const char AS3* vp = Vr + (kb * 32 + 16 * half) * C::ROWB + vofs[db];
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 AS3*)vp);
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 AS3*)(vp + 4 * C::ROWB));
+            const s16x8 v8 = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v8), pop[half], O[db], 0,
+                                                            0, 0);
           }
       }
     }
@@ -447,7 +499,7 @@ hipError_t launch_cfg(const AttnArgs& a, const AttnPlan& p, hipStream_t s) {
 
 template <int D>
 hipError_t launch_d(const AttnArgs& a, const AttnPlan& p, hipStream_t s) {
-  if (p.rb == 1) return launch_cfg<D, 1, 2, 32, 4>(a, p, s);
+  if (p.rb == 1) return launch_cfg<D, 1, 3, 32, 3>(a, p, s);
   if (p.rb == 2) return launch_cfg<D, 2, 2, 32, 4>(a, p, s);
   if (p.rb == 4) return launch_cfg<D, 4, 1, 64, 4>(a, p, s);
   return launch_cfg<D, 8, 1, 64, 4>(a, p, s);

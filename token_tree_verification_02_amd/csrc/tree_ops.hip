@@ -18,25 +18,31 @@
 namespace tv {
 namespace {
 
-// One workgroup per sequence, one thread per node.
+// One workgroup per sequence, one thread per node.  parent, depth and the
+// prefix length arrive in one round of global loads; everything after that
+// (validation, the parent-chain walk) reads LDS.
 __global__ __launch_bounds__(256) void tree_build_kernel(int n, const int32_t* __restrict__ parent,
                                                          const int32_t* __restrict__ depth,
                                                          const int32_t* __restrict__ plen,
                                                          uint64_t* __restrict__ mask, int32_t* __restrict__ pos,
                                                          int32_t* __restrict__ status) {
-  __shared__ int sp[TV_NMAX];
+  __shared__ int sp[TV_NMAX], sd[TV_NMAX];
   const int b = blockIdx.x, u = threadIdx.x;
   const int W = (n + 63) >> 6;
-  if (u < n) sp[u] = parent[(size_t)b * n + u];
+  const int L = plen[b];
+  if (u < n) {
+    sp[u] = parent[(size_t)b * n + u];
+    sd[u] = depth[(size_t)b * n + u];
+  }
   __syncthreads();
   int bad = 0;
   if (u < n) {
     const int p = sp[u];
-    const int du = depth[(size_t)b * n + u];
+    const int du = sd[u];
     if (u == 0)
       bad = (p != -1) || (du != 0);
     else
-      bad = (p < 0) || (p >= u) || (du != depth[(size_t)b * n + p] + 1);
+      bad = (p < 0) || (p >= u) || (du != sd[p] + 1);
     uint64_t w0 = 0, w1 = 0, w2 = 0, w3 = 0;
     int v = u;
     // walk the parent chain; every hop must move to a smaller id, so at most u+1 steps
@@ -60,7 +66,7 @@ __global__ __launch_bounds__(256) void tree_build_kernel(int n, const int32_t* _
     if (W > 1) mr[1] = w1;
     if (W > 2) mr[2] = w2;
     if (W > 3) mr[3] = w3;
-    pos[(size_t)b * n + u] = plen[b] + du;
+    pos[(size_t)b * n + u] = L + du;
   }
   bad = __syncthreads_or(bad);
   if (u == 0) status[b] = bad ? TV_ETOPOLOGY : TV_OK;
@@ -75,72 +81,81 @@ __device__ __forceinline__ bool beats(float v2, int i2, float v1, int i1) {
   return v2 > v1 || (v2 == v1 && i2 < i1) || (i1 == INT_MAX && i2 != INT_MAX);
 }
 
-// One workgroup of 256 threads per logits row.  Each thread scans its elements
-// in increasing index order keeping the first maximum, then a wave shuffle and
-// an LDS step reduce (value, index) pairs under the same order.
+// One workgroup of 256 threads per logits row.  Each thread loads 8 16-byte
+// vectors per round before it compares anything, keeps the index of the first
+// vector whose maximum beats its running best, and at the end re-reads that one
+// vector (a cache hit) to find the lowest index of the maximum inside it; a wave
+// shuffle and an LDS step then reduce (value, index) pairs.
 template <bool BF16>
 __global__ __launch_bounds__(256) void argmax_kernel(const void* __restrict__ logits, int V,
                                                      int32_t* __restrict__ am) {
   constexpr int EPV = BF16 ? 8 : 4;  // elements per 16-byte vector
+  constexpr int R = 8;               // vectors in flight per thread
   const size_t row = blockIdx.x;
   const int tid = threadIdx.x;
-  float bv = -INFINITY;
-  int bi = INT_MAX;
-  auto take = [&](float x, int i) {
-    if (x > bv || bi == INT_MAX) {
-      bv = x;
-      bi = i;
-    }
-  };
   const size_t es = BF16 ? 2 : 4;
   const char* rp = (const char*)logits + row * (size_t)V * es;
+  float bv = -INFINITY;
+  int bi = INT_MAX;
   int done = 0;
   if ((((uintptr_t)rp) & 15) == 0) {
     const int nv = V / EPV;
     const uint4* vp = (const uint4*)rp;
-    int i = tid;
-    for (; i + 3 * 256 < nv; i += 4 * 256) {
-      uint4 w[4];
+    float vbest = -INFINITY;
+    int vidx = -1;
+    for (int base = 0; base < nv; base += R * 256) {
+      uint4 w[R];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) w[k] = vp[i + k * 256];
+      for (int k = 0; k < R; ++k)  // unconditional loads (clamped index): all R stay in flight
+        w[k] = vp[min(base + k * 256 + tid, nv - 1)];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint32_t ws[4] = {w[k].x, w[k].y, w[k].z, w[k].w};
-        const int e0 = (i + k * 256) * EPV;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (BF16) {
-            take(bf16lo(ws[e]), e0 + 2 * e);
-            take(bf16hi(ws[e]), e0 + 2 * e + 1);
-          } else {
-            take(__uint_as_float(ws[e]), e0 + e);
-          }
+      for (int k = 0; k < R; ++k) {
+        const int i = base + k * 256 + tid;
+        float m;
+        if (BF16) {
+          m = fmaxf(fmaxf(fmaxf(bf16lo(w[k].x), bf16hi(w[k].x)), fmaxf(bf16lo(w[k].y), bf16hi(w[k].y))),
+                    fmaxf(fmaxf(bf16lo(w[k].z), bf16hi(w[k].z)), fmaxf(bf16lo(w[k].w), bf16hi(w[k].w))));
+        } else {
+          m = fmaxf(fmaxf(__uint_as_float(w[k].x), __uint_as_float(w[k].y)),
+                    fmaxf(__uint_as_float(w[k].z), __uint_as_float(w[k].w)));
         }
+        // vectors are visited in increasing index order: strict > keeps the first
+        const bool take = i < nv && (m > vbest || vidx < 0);
+        vbest = take ? m : vbest;
+        vidx = take ? i : vidx;
       }
     }
-    // the 4-way batches above all precede this thread's remaining vectors, and
-    // each thread's indices still increase monotonically
-    for (; i < nv; i += 256) {
-      const uint4 w = vp[i];
-      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-      const int e0 = i * EPV;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if (BF16) {
-          take(bf16lo(ws[e]), e0 + 2 * e);
-          take(bf16hi(ws[e]), e0 + 2 * e + 1);
-        } else {
-          take(__uint_as_float(ws[e]), e0 + e);
-        }
+    if (vidx >= 0) {  // lowest index of the maximum inside the winning vector (re-read: cached)
+      const uint4 v = vp[vidx];
+      const uint32_t w0 = v.x, w1 = v.y, w2 = v.z, w3 = v.w;
+      int e = EPV;
+      if (BF16) {
+        e = bf16hi(w3) == vbest ? 7 : e;
+        e = bf16lo(w3) == vbest ? 6 : e;
+        e = bf16hi(w2) == vbest ? 5 : e;
+        e = bf16lo(w2) == vbest ? 4 : e;
+        e = bf16hi(w1) == vbest ? 3 : e;
+        e = bf16lo(w1) == vbest ? 2 : e;
+        e = bf16hi(w0) == vbest ? 1 : e;
+        e = bf16lo(w0) == vbest ? 0 : e;
+      } else {
+        e = __uint_as_float(w3) == vbest ? 3 : e;
+        e = __uint_as_float(w2) == vbest ? 2 : e;
+        e = __uint_as_float(w1) == vbest ? 1 : e;
+        e = __uint_as_float(w0) == vbest ? 0 : e;
       }
+      bi = vidx * EPV + e;
+      bv = vbest;
     }
     done = nv * EPV;
   }
-  for (int i = done + tid; i < V; i += 256) {
+  for (int i = done + tid; i < V; i += 256) {  // unaligned rows and the tail
     const float x = BF16 ? bf16_to_f32(((const uint16_t*)rp)[i]) : ((const float*)rp)[i];
-    take(x, i);
+    if (x > bv || bi == INT_MAX) {
+      bv = x;
+      bi = i;
+    }
   }
-  // reduce
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     const float ov = __shfl_xor(bv, o);
@@ -167,40 +182,44 @@ __global__ __launch_bounds__(256) void argmax_kernel(const void* __restrict__ lo
   }
 }
 
-// One wave per sequence.  Every step moves to a child with a larger id, so the
-// walk ends within n steps whatever the input.
-__global__ __launch_bounds__(64) void walk_kernel(int n, const int32_t* __restrict__ am,
-                                                  const int32_t* __restrict__ tokens,
-                                                  const int32_t* __restrict__ parent, int32_t* __restrict__ path,
-                                                  int32_t* __restrict__ plen, int32_t* __restrict__ bonus) {
-  __shared__ int sp[TV_NMAX], st[TV_NMAX], sa[TV_NMAX];
-  const int b = blockIdx.x, lane = threadIdx.x;
-  for (int i = lane; i < n; i += 64) {
-    sp[i] = parent[(size_t)b * n + i];
-    st[i] = tokens[(size_t)b * n + i];
-    sa[i] = am[(size_t)b * n + i];
+// One workgroup per sequence, one thread per node.  Every node first decides in
+// parallel whether its draft token equals the argmax at its parent; the lowest
+// such child of each node is kept with an LDS atomic min.  The walk is then a
+// pointer chase through that table, each hop to a larger node id, so it ends
+// within n steps whatever the input.
+__global__ __launch_bounds__(256) void walk_kernel(int n, const int32_t* __restrict__ am,
+                                                   const int32_t* __restrict__ tokens,
+                                                   const int32_t* __restrict__ parent, int32_t* __restrict__ path,
+                                                   int32_t* __restrict__ plen, int32_t* __restrict__ bonus) {
+  __shared__ int sa[TV_NMAX], fc[TV_NMAX], sp[TV_NMAX];
+  __shared__ int slen;
+  const int b = blockIdx.x, v = threadIdx.x;
+  int p = -1, tok = 0;
+  if (v < n) {
+    sa[v] = am[(size_t)b * n + v];
+    p = parent[(size_t)b * n + v];
+    tok = tokens[(size_t)b * n + v];
+    fc[v] = INT_MAX;
   }
   __syncthreads();
-  int cur = 0, len = 1;
+  if (v < n && v > 0 && p >= 0 && p < v && tok == sa[p]) atomicMin(&fc[p], v);
+  __syncthreads();
   int32_t* pr = path + (size_t)b * n;
-  if (lane == 0) pr[0] = 0;
-  for (int step = 1; step < n; ++step) {
-    const int target = sa[cur];
-    int best = INT_MAX;
-    for (int v = lane; v < n; v += 64)
-      if (v > cur && sp[v] == cur && st[v] == target) best = min(best, v);
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) best = min(best, __shfl_xor(best, o));
-    if (best == INT_MAX) break;
-    cur = best;
-    if (lane == 0) pr[len] = cur;
-    ++len;
-  }
-  for (int i = len + lane; i < n; i += 64) pr[i] = -1;
-  if (lane == 0) {
+  if (v == 0) {
+    int cur = 0, len = 1;
+    sp[0] = 0;
+    while (len < n) {
+      const int c = fc[cur];
+      if (c == INT_MAX) break;
+      cur = c;
+      sp[len++] = cur;
+    }
+    slen = len;
     plen[b] = len;
     bonus[b] = sa[cur];
   }
+  __syncthreads();
+  if (v < n) pr[v] = v < slen ? sp[v] : -1;
 }
 
 }  // namespace
@@ -223,7 +242,8 @@ hipError_t launch_verify(int B, int n, int V, int bf16, const void* logits, cons
     hipLaunchKernelGGL(argmax_kernel<false>, dim3(B * n), dim3(256), 0, s, logits, V, am);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(walk_kernel, dim3(B), dim3(64), 0, s, n, am, tokens, parent, path, plen, bonus);
+  hipLaunchKernelGGL(walk_kernel, dim3(B), dim3(((n + 63) / 64) * 64), 0, s, n, am, tokens, parent, path, plen,
+                     bonus);
   return hipGetLastError();
 }
 

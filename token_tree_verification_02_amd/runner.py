@@ -80,6 +80,88 @@ def step(d, stream=None):
         verify(d, stream)
 
 
+class Step:
+    """One verification step over an uploaded batch with the C-ABI arguments built once.
+
+    Calling it enqueues tree_build, tree_attention and tree_verify_greedy on the
+    given (or current) stream with no per-call Python marshalling beyond the
+    stream handle; capture() records the same three calls into a HIP graph.
+    """
+
+    def __init__(self, d):
+        import ctypes
+        lib = _lib.load()
+        self.d = d
+        self.lib = lib
+        cfg = d["cfg"]
+        P = _lib._ptr
+        self.desc = attn_desc_of(d)
+        self._desc_ref = ctypes.byref(self.desc)
+        ws = d["workspace"]
+        wbytes = 0 if ws is None else ws.numel()
+        self.build_args = (cfg.B, cfg.n, P(d["parent"]), P(d["depth"]), P(d["prefix_len"]), P(d["mask"]),
+                           P(d["pos"]), P(d["status"]))
+        self.attn_args = (self._desc_ref, P(d["q"]), P(d["k_cache"]), P(d["v_cache"]), P(d["block_table"]),
+                          P(d["prefix_len"]), P(d["k_tree"]), P(d["v_tree"]), P(d["mask"]), P(d["out"]),
+                          P(d["lse"]), P(d["attn_status"]), P(ws), wbytes)
+        self.verify_args = None
+        if "argmax" in d:
+            code = _lib.TV_BF16 if cfg.dtype == "bf16" else _lib.TV_F32
+            self.verify_args = (cfg.B, cfg.n, cfg.vocab, code, P(d["logits"]), P(d["tokens"]), P(d["parent"]),
+                                P(d["argmax"]), P(d["path"]), P(d["path_len"]), P(d["bonus"]))
+
+    def build(self, sh):
+        rc = self.lib.tree_build(*self.build_args, sh)
+        if rc:
+            _lib._check(rc, "tree_build")
+
+    def attention(self, sh):
+        rc = self.lib.tree_attention(*self.attn_args, sh)
+        if rc:
+            _lib._check(rc, "tree_attention")
+
+    def verify(self, sh):
+        if self.verify_args is not None:
+            rc = self.lib.tree_verify_greedy(*self.verify_args, sh)
+            if rc:
+                _lib._check(rc, "tree_verify_greedy")
+
+    def __call__(self, stream=None):
+        sh = (stream or torch.cuda.current_stream()).cuda_stream
+        self.build(sh)
+        self.attention(sh)
+        self.verify(sh)
+
+    def capture(self):
+        """A torch.cuda.CUDAGraph holding one step (replay() re-runs it)."""
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            self()  # warm the launch path outside capture
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            self()
+        return g
+
+
+def capture_steps(steps) -> "torch.cuda.CUDAGraph":
+    """One graph that runs the given steps back to back (replay() runs them all)."""
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for st in steps:
+            st()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for st in steps:
+            st()
+    return g
+
+
 def out_f64(d) -> np.ndarray:
     o = d["out"]
     return o.float().double().cpu().numpy() if o.dtype == torch.bfloat16 else o.double().cpu().numpy()
