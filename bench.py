@@ -130,25 +130,26 @@ def main():
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
 
-    # per-kernel durations: HIP events on the launch stream around each C-ABI call
+    # per-kernel durations: HIP events on the launch stream around K back-to-back
+    # launches of one call (rotating over the input copies), so the figure is the
+    # kernel's own average duration, not the dispatch latency around one call
     K = args.steps
-    for i in range(args.warmup):
+    for i in range(max(args.warmup, R)):
         steps[i % R]()
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
-    for k in range(K):
-        st, e = steps[k % R], ev[k]
-        e[0].record(stream)
-        st.build(sh)
-        e[1].record(stream)
-        st.attention(sh)
-        e[2].record(stream)
-        st.verify(sh)
-        e[3].record(stream)
-    torch.cuda.synchronize()
-    t_build = np.mean([e[0].elapsed_time(e[1]) for e in ev]) * 1e-3
-    t_attn = np.mean([e[1].elapsed_time(e[2]) for e in ev]) * 1e-3
-    t_ver = np.mean([e[2].elapsed_time(e[3]) for e in ev]) * 1e-3
+
+    def timed(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for k in range(K):
+            fn(steps[k % R])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / K
+
+    t_build = timed(lambda st: st.build(sh))
+    t_attn = timed(lambda st: st.attention(sh))
+    t_ver = timed(lambda st: st.verify(sh))
 
     # throughput: K whole steps back to back.  Default: one HIP graph holding one step
     # per input copy (R steps), replayed K/R times; --eager launches each call.
