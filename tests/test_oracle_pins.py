@@ -485,3 +485,58 @@ def test_pins_catch_planted_oracle_mistakes(monkeypatch):
     monkeypatch.setattr(T, "gather_prefix", swapped_vt)
     with pytest.raises(AssertionError):
         test_each_node_is_single_sequence_attention(4, dict(n=10, L_lo=20, L_hi=60))
+
+
+def test_pins_catch_more_planted_oracle_mistakes(monkeypatch):
+    """Wrong scale, descendants for ancestors, highest-index argmax ties and the
+    highest matching child in the walk each make a pin fail."""
+    import oracle.tree_oracle as T
+
+    real_ta = T.tree_attention
+
+    def wrong_scale(w, *a, **k):            # 1/d instead of 1/sqrt(d)
+        k["scale"] = 1.0 / w["q"].shape[-1]
+        return real_ta(w, *a, **k)
+
+    monkeypatch.setattr(oracle, "tree_attention", wrong_scale)
+    with pytest.raises(AssertionError):
+        test_chain_tree_is_causal_attention(3)
+    monkeypatch.setattr(oracle, "tree_attention", real_ta)
+
+    real_anc = T.ancestors
+
+    def descendants(parent, u):             # the transposed relation
+        out = [u]
+        for v in range(u + 1, len(parent)):
+            if u in real_anc(parent, v):
+                out.append(v)
+        return out
+
+    monkeypatch.setattr(T, "ancestors", descendants)
+    with pytest.raises(AssertionError):
+        test_chain_tree_is_causal_attention(1)
+    monkeypatch.setattr(T, "ancestors", real_anc)
+
+    real_am = T.argmax_lowest
+
+    def highest_tie(logits, dtype):         # last occurrence of the maximum
+        x = T.to_f64(logits, dtype)
+        return (x.shape[-1] - 1 - np.argmax(x[..., ::-1], axis=-1)).astype(np.int32)
+
+    monkeypatch.setattr(oracle, "argmax_lowest", highest_tie)
+    with pytest.raises(AssertionError):
+        test_argmax_lowest_index_brute_force("bf16")
+    monkeypatch.setattr(oracle, "argmax_lowest", real_am)
+
+    def highest_child(am, tokens, parent):  # the highest-numbered matching child
+        path, cur = [0], 0
+        while True:
+            hits = [v for v in range(len(parent)) if parent[v] == cur and tokens[v] == am[cur]]
+            if not hits:
+                return path, int(am[cur])
+            cur = max(hits)
+            path.append(cur)
+
+    monkeypatch.setattr(oracle, "accept_walk", highest_child)
+    with pytest.raises(AssertionError):
+        test_duplicate_siblings_lowest_node_wins()
