@@ -39,7 +39,7 @@ MALL_BYTES = 256 << 20
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for f in ("attn_bf16.hip", "attn_f32.hip", "tv_internal.h"):
+    for f in ("attn_bf16.hip", "attn_sk.hip", "attn_bf16_common.h", "attn_f32.hip", "tv_internal.h"):
         with open(os.path.join(ROOT, "token_tree_verification_02_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

@@ -1,0 +1,63 @@
+// Device helpers shared by the bf16 tree-attention kernels (gfx950 only).
+#pragma once
+#include "tv_internal.h"
+
+namespace tv {
+namespace attn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+#define AS3 __attribute__((address_space(3)))
+#define AS4 __attribute__((address_space(4)))
+
+constexpr float kTau = 8.0f;  // lazy-rescale threshold in the log2 domain
+
+__device__ __forceinline__ int perm_row(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
+
+// Granule swizzles (16-byte granules within a token row of the tile).
+template <int D>
+__device__ __forceinline__ int kswz(int row) {  // 16 consecutive rows -> 16 distinct bank groups
+  return D == 128 ? (row & 15) : ((row >> 1) & 7);
+}
+template <int D>
+__device__ __forceinline__ int vswz(int row) {  // 4 consecutive rows x 4 granules -> distinct
+  return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
+}
+
+// HBM -> LDS copy of 16 bytes per lane; lane l lands at lds_line + 16*l.  Issued
+// through asm so the compiler does not add its own (full) waits around it; the
+// kernel waits with explicit vmcnt counts instead.
+__device__ __forceinline__ void dma16(const void* gaddr, uint32_t lds_line) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gaddr),
+               "s"(__builtin_amdgcn_readfirstlane(lds_line))
+               : "m0");
+}
+// Same with a wave-uniform 64-bit base and a per-lane 32-bit byte offset.
+__device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, uint32_t lds_line) {
+  const uint64_t b = (uint64_t)sbase;
+  const uint64_t ub = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(ub),
+               "s"(__builtin_amdgcn_readfirstlane(lds_line))
+               : "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier that orders LDS accesses only (a full fence would also wait
+// for every outstanding HBM load and empty the pipeline).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+}  // namespace attn
+}  // namespace tv

@@ -1,0 +1,716 @@
+// Tree attention for bf16 inputs with many query rows per KV head (GQA groups
+// times tree nodes > 128): a persistent, load-balanced variant of the fused
+// prefix + tree kernel.
+//
+// What is computed is the same as in the other bf16 kernel (SpecInfer explainer,
+// token-tree structure section, attention equation; kernel-fusion section,
+// precomputed topology mask): node u attends in one softmax to every cached
+// prefix token of its sequence and to the tree nodes of S_u.
+//
+// Work decomposition.  The unit of work is a 64-key tile of one item, an item
+// being one (sequence, KV head).  An item's tiles are its prefix tiles followed
+// by its tree tiles.  All items' tiles form one list, in (sequence, KV head)
+// order, and the list is cut into NV equal ranges; each range belongs to one
+// "virtual workgroup" (rsplit real workgroups when the rows of an item need
+// more than one workgroup, each taking a 256-row slice over the same tiles).  A
+// range may start or end inside an item: such a piece writes an unnormalised
+// partial (running max, sum, O) into a slot of its workgroup, and a merge pass
+// combines the pieces of every item split that way.  Items that a range covers
+// whole are written directly.  Ragged prefix lengths therefore cost no idle
+// compute units; the plan is computed on the device from the prefix lengths by
+// a one-workgroup scheduling kernel, since the host does not know them.
+//
+// Inside a workgroup: 4 waves (one per SIMD), each owning 64 query rows as two
+// 32-row MFMA column blocks, so every K or V operand read from LDS feeds two
+// v_mfma_f32_32x32x16_bf16.  The KV tiles stream HBM -> LDS through an S-stage
+// ring with global_load_lds_dwordx4 and hand-placed vmcnt waits (one LDS-only
+// barrier per tile).  Full prefix tiles and masked tiles (the ragged last
+// prefix tile, the tree tiles) run separate code, so the common case carries no
+// per-score selects.  Per score the softmax costs one FMA, one exp2, half a
+// max3, half a bf16 pack and half a dot2: the row sums are taken from the
+// bf16-rounded probabilities that also feed the PV product.
+#include <float.h>
+
+#include "attn_bf16_common.h"
+
+namespace tv {
+
+namespace {
+
+using namespace attn;
+
+constexpr int kTK = 64;  // keys per tile
+#ifndef TV_SK_QB
+#define TV_SK_QB 1
+#endif
+constexpr int kSkQB = TV_SK_QB;  // 32-row query blocks per wave (256 rows per workgroup)
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __attribute__((aligned(4096))) uint4 sk_zero_page[256];
+
+
+// Scheduling record in the workspace (int32):
+//   [0] total tiles T, [1] tiles per virtual workgroup, [2] NV, [3] unused,
+//   [4 .. 4+B]   exclusive prefix sum of tiles over sequences (B+1 entries),
+//   [cur .. ]    start cursor of every virtual workgroup: (b, g, tile in item, 0).
+__host__ __device__ inline int sk_cursor_offset(int B) { return 4 + ((B + 1 + 3) & ~3); }
+
+__device__ __forceinline__ int clamp_len(int L, int cap) { return L < 0 ? 0 : (L > cap ? cap : L); }
+
+// One workgroup of 1024 threads.  Two passes over the prefix lengths (the
+// second knows the per-range size) so nothing written here is read back here.
+__global__ __launch_bounds__(1024) void sk_sched_kernel(const int32_t* __restrict__ plen, int B, int n, int cap,
+                                                        int Hkv, int NV, int32_t* __restrict__ sched) {
+  __shared__ int wsum[16];
+  __shared__ int carry;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int ttree = (n + kTK - 1) / kTK;
+  int32_t* cum = sched + 4;
+  int32_t* curs = sched + sk_cursor_offset(B);
+  int per = 1, T = 0;
+  for (int pass = 0; pass < 2; ++pass) {
+    if (tid == 0) carry = 0;
+    __syncthreads();
+    for (int base = 0; base < B; base += 1024) {
+      const int b = base + tid;
+      int tb = 0, L = 0;
+      if (b < B) {
+        L = clamp_len(plen[b], cap);
+        tb = (L + kTK - 1) / kTK + ttree;
+      }
+      const int t = tb * Hkv;
+      int x = t;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o);
+        if (lane >= o) x += y;
+      }
+      if (lane == 63) wsum[wv] = x;
+      __syncthreads();
+      int off = carry;
+      for (int w = 0; w < wv; ++w) off += wsum[w];
+      const int ex = off + x - t;  // tiles before sequence b
+      if (pass == 1 && b < B) {
+        cum[b] = ex;
+        // every range whose first tile lies in sequence b starts its cursor here
+        const int vf = (ex + per - 1) / per;
+        const int vl = (ex + t - 1) / per;
+        for (int v = vf; v <= vl && v < NV; ++v) {
+          const int r = (int)((long long)v * per - ex);
+          curs[4 * v] = b;
+          curs[4 * v + 1] = r / tb;
+          curs[4 * v + 2] = r % tb;
+          curs[4 * v + 3] = 0;
+        }
+      }
+      __syncthreads();
+      if (tid == 1023) carry = off + x;
+      __syncthreads();
+    }
+    T = carry;
+    per = T > 0 ? (T + NV - 1) / NV : 1;
+    __syncthreads();
+  }
+  if (tid == 0) {
+    cum[B] = T;
+    sched[0] = T;
+    sched[1] = per;
+    sched[2] = NV;
+    sched[3] = 0;
+  }
+  for (int v = tid; v < NV; v += 1024)
+    if ((long long)v * per >= T) {
+      curs[4 * v] = B;
+      curs[4 * v + 1] = 0;
+      curs[4 * v + 2] = 0;
+      curs[4 * v + 3] = 0;
+    }
+}
+
+struct SkArgs {
+  const int32_t* sched;
+  float* po;   // [2*NV][rsplit][RW][D] partial O (unnormalised)
+  float* pml;  // [2*NV][rsplit][RW][2]  (max in the log2 domain, sum)
+  int rsplit, NV, cap;
+};
+
+// Position in the tile list: item (b, g), tile `off` within the item.
+struct Cursor {
+  int b, g, off, L, tpre, titem;
+};
+
+__device__ __forceinline__ void cursor_seq(Cursor& c, const AS4 int32_t* plen, int cap, int ttree) {
+  c.L = clamp_len(plen[c.b], cap);
+  c.tpre = (c.L + kTK - 1) / kTK;
+  c.titem = c.tpre + ttree;
+}
+
+__device__ __forceinline__ void cursor_next(Cursor& c, const AS4 int32_t* plen, int B, int Hkv, int cap, int ttree) {
+  if (++c.off < c.titem) return;
+  c.off = 0;
+  if (++c.g < Hkv) return;
+  c.g = 0;
+  if (++c.b < B) cursor_seq(c, plen, cap, ttree);
+}
+
+// 64-bit word `w` (< 4) of a node's mask, from registers.
+__device__ __forceinline__ uint64_t pick_word(const uint64_t (&m)[4], int w) {
+  return w == 0 ? m[0] : (w == 1 ? m[1] : (w == 2 ? m[2] : m[3]));
+}
+
+// Scores of a 32-key block past the tile's valid keys, or (tree tiles) of keys
+// that are not ancestors of the lane's node, become -inf.  The lane holds key
+// 16*(r>>3) + 8*hh + (r&7) of the block.
+__device__ __forceinline__ void sk_mask(f32x16& s, int kb, int lim, bool tree, uint64_t bits, int hh) {
+  const uint32_t w32 = (uint32_t)(bits >> (32 * kb)) >> (8 * hh);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int ko = kb * 32 + 16 * (r >> 3) + 8 * hh + (r & 7);
+    const bool ok = ko < lim && (!tree || ((w32 >> (16 * (r >> 3) + (r & 7))) & 1u));
+    s[r] = ok ? s[r] : -INFINITY;
+  }
+}
+
+// Maximum of the lane's 16 scores and its partner's (lane ^ 32): the column max.
+__device__ __forceinline__ float sk_colmax(const f32x16& s) {
+  float mx = fmaxf(fmaxf(s[0], s[1]), s[2]);
+#pragma unroll
+  for (int r = 3; r < 15; r += 2) mx = fmaxf(fmaxf(mx, s[r]), s[r + 1]);
+  mx = fmaxf(mx, s[15]);
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+  return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+
+// Probabilities of 16 scores against the running max (log2 domain), rounded to
+// bf16 (the PV operand); their sum is added to l with a bf16 dot product.
+__device__ __forceinline__ void sk_probs(const f32x16& s, bf16x8 (&P)[2], float& l, float sl2, float msub) {
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      bf16x2 pr;
+      pr[0] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * h2 + e], sl2, -msub));
+      pr[1] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * h2 + e + 1], sl2, -msub));
+      l = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l, false);
+      P[h2][e] = pr[0];
+      P[h2][e + 1] = pr[1];
+    }
+}
+
+// Running-max update for one query block (log2 domain): the accumulators are
+// rescaled only when the block max exceeds the running max by more than kTau.
+template <int D>
+__device__ __forceinline__ void sk_rescale(f32x16 (&Oq)[D / 32], float& m_run, float& lsum, float mx) {
+  const float m_new = fmaxf(m_run, mx);
+  const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+  lsum *= alpha;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) Oq[db][r] *= alpha;
+    __builtin_amdgcn_sched_barrier(0);  // bounds the registers in flight
+  }
+  m_run = m_new;
+}
+
+// O^T += V^T P^T for one 32-key block: each V operand (two transposing LDS
+// reads) feeds all QB query blocks.
+template <int D, int QB>
+__device__ __forceinline__ void sk_pv(const char AS3* Vr, int kb, const bf16x8 (&P)[QB][2], f32x16 (&O)[QB][D / 32],
+                                      const uint32_t (&vofs)[D / 32]) {
+  constexpr int DB = D / 32, ROWB = 2 * D;
+#pragma unroll
+  for (int half = 0; half < 2; ++half)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const char AS3* vp = Vr + (kb * 32 + 16 * half) * ROWB + vofs[db];
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 AS3*)vp);
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 AS3*)(vp + 4 * ROWB));
+      const bf16x8 vop = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+        O[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, P[qb][half], O[qb][db], 0, 0, 0);
+    }
+}
+
+// S^T = K Q^T for one 32-key block and all QB query blocks (each K operand read
+// once for all of them).
+template <int D, int QB>
+__device__ __forceinline__ void sk_qk(const char AS3* Kr, int kb, const bf16x8 (&qop)[QB][D / 16],
+                                      const uint32_t (&kofs)[D / 16], f32x16 (&Sa)[QB]) {
+  constexpr int SD = D / 16, ROWB = 2 * D;
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) Sa[qb][r] = 0.f;
+#pragma unroll
+  for (int sd = 0; sd < SD; ++sd) {
+    const bf16x8 kop = *(const bf16x8 AS3*)(Kr + kb * 32 * ROWB + kofs[sd]);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+      Sa[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[qb][sd], Sa[qb], 0, 0, 0);
+  }
+}
+
+// One 64-key tile for one wave holding QB 32-row query blocks.  MASKED: key
+// validity from `lim` (keys of the tile that exist) and, for tree tiles, the
+// ancestor bits of each query's node.
+//   QB == 1 (two waves per SIMD): the two 32-key blocks in turn, QK -> max ->
+//     (rare) rescale -> softmax -> PV; the other wave on the SIMD fills the gaps.
+//   QB == 2 (one wave per SIMD): QK of both key blocks first, ONE max check per
+//     tile, then softmax and PV of both blocks as one branch-free stretch that
+//     the scheduler can overlap.
+template <int D, int QB, bool MASKED>
+__device__ __forceinline__ void sk_tile(const char AS3* Kr, const char AS3* Vr, const bf16x8 (&qop)[QB][D / 16],
+                                        f32x16 (&O)[QB][D / 32], float (&m_run)[QB], float (&lsum)[QB],
+                                        const uint32_t (&kofs)[D / 16], const uint32_t (&vofs)[D / 32], float sl2,
+                                        int lim, bool tree, const uint64_t (&bits)[QB], int hh) {
+  if constexpr (QB == 1) {
+    // Both key blocks' QK products are issued first: block 1's run in the
+    // matrix core while block 0's softmax executes on the VALU (in-flight MFMAs
+    // overlap later independent instructions, across the rescale branch too).
+    f32x16 Sa[2][1];
+    sk_qk<D, 1>(Kr, 0, qop, kofs, Sa[0]);
+    sk_qk<D, 1>(Kr, 1, qop, kofs, Sa[1]);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      if constexpr (MASKED) sk_mask(Sa[kb][0], kb, lim, tree, bits[0], hh);
+      const float mx = sk_colmax(Sa[kb][0]) * sl2;  // scale > 0 commutes with max
+      if (__builtin_expect(__any(mx > m_run[0] + kTau), 0)) sk_rescale<D>(O[0], m_run[0], lsum[0], mx);
+      bf16x8 P[1][2];
+      sk_probs(Sa[kb][0], P[0], lsum[0], sl2, (m_run[0] == -INFINITY) ? 0.f : m_run[0]);
+      sk_pv<D, 1>(Vr, kb, P, O, vofs);
+    }
+  } else {
+    f32x16 Sa[2][QB];  // [key block][query block]
+    sk_qk<D, QB>(Kr, 0, qop, kofs, Sa[0]);
+    sk_qk<D, QB>(Kr, 1, qop, kofs, Sa[1]);
+    float mx[QB];
+    bool up = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      if constexpr (MASKED) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) sk_mask(Sa[kb][qb], kb, lim, tree, bits[qb], hh);
+      }
+      mx[qb] = fmaxf(sk_colmax(Sa[0][qb]), sk_colmax(Sa[1][qb])) * sl2;
+      up = up || mx[qb] > m_run[qb] + kTau;
+    }
+    if (__builtin_expect(__any(up), 0)) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) sk_rescale<D>(O[qb], m_run[qb], lsum[qb], mx[qb]);
+    }
+    float msub[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) msub[qb] = (m_run[qb] == -INFINITY) ? 0.f : m_run[qb];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      bf16x8 P[QB][2];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) sk_probs(Sa[kb][qb], P[qb], lsum[qb], sl2, msub[qb]);
+      sk_pv<D, QB>(Vr, kb, P, O, vofs);
+    }
+  }
+}
+
+template <int D, int QB, int RB, int S>
+__global__ __launch_bounds__(64 * RB) void attn_sk_kernel(AttnArgs a, SkArgs k) {
+  constexpr int RW = 32 * QB * RB;          // query rows per workgroup
+  constexpr int ROWB = 2 * D;               // bytes per token row
+  constexpr int REG = kTK * ROWB;           // K (or V) region of a stage
+  constexpr int STAGE = 2 * REG;
+  constexpr int LINES = STAGE / 1024;       // 1 KB DMA lines per tile
+  constexpr int HL = LINES / 2;             // lines of the K region
+  constexpr int LPW = LINES / RB;           // DMA instructions per wave per tile
+  constexpr int RPL = 1024 / ROWB;          // token rows per line
+  constexpr int GPR = D / 8;                // 16-byte granules per row
+  constexpr int SD = D / 16, DB = D / 32;
+  static_assert(HL % RB == 0 && LPW * (S - 2) < 64, "pipeline shape");
+  __shared__ __attribute__((aligned(1024))) char smem[S * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int rb = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31, hh = lane >> 5;
+  const int n = a.n, G = a.G, Hkv = a.Hkv, rows = n * G, B = a.B;
+  const int ttree = (n + kTK - 1) / kTK;
+
+  // XCD-aware order: consecutive logical ids (the row slices of one range, then
+  // neighbouring ranges) land on the same XCD and share its L2.
+  const int nwg = gridDim.x, wg = blockIdx.x;
+  const int perx = nwg >> 3, rem = nwg & 7, xcd = wg & 7;
+  const int lid = xcd * perx + min(xcd, rem) + (wg >> 3);
+  const int rs = lid % k.rsplit, v = lid / k.rsplit;
+
+  const AS4 int32_t* sc = (const AS4 int32_t*)k.sched;
+  const AS4 int32_t* plen = (const AS4 int32_t*)a.plen;
+  const int T = sc[0], per = sc[1];
+  const long long r0l = (long long)v * per;
+  if (r0l >= T) return;  // uniform per workgroup
+  const int r0 = (int)r0l;
+  const int ntiles = min(T - r0, per);
+  const AS4 int32_t* cp = sc + sk_cursor_offset(B) + 4 * v;
+  Cursor ic;
+  ic.b = cp[0];
+  ic.g = cp[1];
+  ic.off = cp[2];
+  cursor_seq(ic, plen, k.cap, ttree);
+  Cursor cc = ic;
+
+  const char* kc = (const char*)a.kc;
+  const char* vc = (const char*)a.vc;
+  const char* ktr = (const char*)a.kt;
+  const char* vtr = (const char*)a.vt;
+  const char* zero = (const char*)sk_zero_page;
+  const char* zsrc = zero + lane * 16;
+  const uint32_t ring = (uint32_t)(uintptr_t)(AS3 void*)smem;
+  const AS4 int32_t* btc = (const AS4 int32_t*)a.bt;
+
+  // per-lane DMA geometry: line q*RB + rb of the tile belongs to this wave; the
+  // lane's token row within the tile and its source granule (swizzled) follow
+  // from q alone, so only the byte offsets of full tiles are kept.
+  auto lrow_of = [=](int ln, int q) {
+    const int line = q * RB + rb;
+    return (q * RB >= HL ? line - HL : line) * RPL + ln / GPR;
+  };
+  auto gran_of = [=](int ln, int q) {
+    const int lrow = lrow_of(ln, q), pg = ln % GPR;
+    return q * RB >= HL ? (pg ^ vswz<D>(lrow)) : (pg ^ kswz<D>(lrow));
+  };
+  uint32_t voff[LPW];
+#pragma unroll
+  for (int q = 0; q < LPW; ++q) {
+    const int lrow = lrow_of(lane, q);
+    const int key = q * RB >= HL ? lrow : perm_row(lrow);
+    voff[q] = (uint32_t)(((a.paged ? (key & 15) : key) * D + gran_of(lane, q) * 8) * 2);
+  }
+
+  // DMA of this wave's lines of the tile at cursor c into stage st (c == null: zeros)
+  auto issue = [=](const Cursor& c, bool live, int st) {
+    const uint32_t gbase = ring + st * STAGE;
+    // an opaque copy of the lane id keeps the compiler from hoisting the
+    // per-line geometry of the rare paths out of the loop (it would hold dozens
+    // of registers for them)
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    if (!live) {
+#pragma unroll
+      for (int q = 0; q < LPW; ++q) dma16(zsrc, gbase + (q * RB + rb) * 1024);
+      return;
+    }
+    const int b = c.b, g = c.g;
+    if (c.off >= c.tpre) {  // tree tile
+      const int tstart = (c.off - c.tpre) * kTK;
+#pragma unroll
+      for (int q = 0; q < LPW; ++q) {
+        const bool isv = q * RB >= HL;
+        const int vv = tstart + (isv ? lrow_of(ln, q) : perm_row(lrow_of(ln, q)));
+        const char* src = (isv ? vtr : ktr) + ((((size_t)b * n + vv) * Hkv + g) * D + gran_of(ln, q) * 8) * 2;
+        dma16(vv < n ? src : zsrc, gbase + (q * RB + rb) * 1024);
+      }
+      return;
+    }
+    const int tstart = c.off * kTK;
+    const bool full = tstart + kTK <= c.L;
+    if (a.paged) {
+      const int b0 = tstart >> 4;
+      const AS4 int32_t* row = btc + (size_t)b * a.max_blocks;
+      const int id0 = b0 < a.max_blocks ? row[b0] : -1;
+      const int id1 = b0 + 1 < a.max_blocks ? row[b0 + 1] : -1;
+      const int id2 = b0 + 2 < a.max_blocks ? row[b0 + 2] : -1;
+      const int id3 = b0 + 3 < a.max_blocks ? row[b0 + 3] : -1;
+#pragma unroll
+      for (int q = 0; q < LPW; ++q) {
+        const bool isv = q * RB >= HL;
+        const int line = q * RB + rb;
+        const int kq = ((isv ? line - HL : line) * RPL) >> 4;  // 16-token block of the line
+        const int blk = kq == 0 ? id0 : (kq == 1 ? id1 : (kq == 2 ? id2 : id3));
+        const bool bok = blk >= 0 && blk < a.num_blocks;
+        const char* lbase = (isv ? vc : kc) + ((size_t)blk * Hkv + g) * TV_PAGE * D * 2;
+        if (full) {
+          dma16s(bok ? lbase : zero, voff[q], gbase + line * 1024);
+        } else {
+          const int j = tstart + (isv ? lrow_of(ln, q) : perm_row(lrow_of(ln, q)));
+          dma16(bok && j < c.L ? lbase + voff[q] : zsrc, gbase + line * 1024);
+        }
+      }
+    } else {
+      const size_t rowbase = ((size_t)b * Hkv + g) * a.Lmax + tstart;
+      const char* kb = kc + rowbase * D * 2;
+      const char* vb = vc + rowbase * D * 2;
+#pragma unroll
+      for (int q = 0; q < LPW; ++q) {
+        const bool isv = q * RB >= HL;
+        const int line = q * RB + rb;
+        if (full) {
+          dma16s(isv ? vb : kb, voff[q], gbase + line * 1024);
+        } else {
+          const int j = tstart + (isv ? lrow_of(ln, q) : perm_row(lrow_of(ln, q)));
+          dma16(j < c.L ? (isv ? vb : kb) + voff[q] : zsrc, gbase + line * 1024);
+        }
+      }
+    }
+  };
+
+  // per-lane LDS read offsets
+  uint32_t kofs[SD], vofs[DB];
+#pragma unroll
+  for (int sd = 0; sd < SD; ++sd) kofs[sd] = col * ROWB + (((2 * sd + hh) ^ kswz<D>(col)) << 4);
+  {
+    const int l16 = lane & 15, mhalf = (lane >> 4) & 1;
+    const int vr = 8 * hh + (l16 >> 2);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int lg = 4 * db + 2 * mhalf + ((lane & 3) >> 1);
+      vofs[db] = vr * ROWB + ((lg ^ vswz<D>(vr)) << 4) + ((lane & 1) << 3);
+    }
+  }
+
+  const int rowbase = rs * RW + 32 * QB * rb;  // first query row of this wave within an item
+  const float sl2 = a.scale_log2;
+
+  // prologue: S-1 tiles in flight
+#pragma unroll
+  for (int i = 0; i < S - 1; ++i) {
+    const bool live = i < ntiles;
+    issue(ic, live, i);
+    if (live) cursor_next(ic, plen, B, Hkv, k.cap, ttree);
+  }
+
+  // Segments: the part of one item inside this range.  Queries, masks and
+  // accumulators are set up before a segment's tile loop and written out after
+  // it, so the loop itself touches the accumulators only through the MFMAs
+  // (and the rare rescale).
+  int it = 0;
+  for (int seg = 0; it < ntiles; ++seg) {
+    const bool seg_whole = cc.off == 0;
+    const int seg_len = min(cc.titem - cc.off, ntiles - it);
+    const bool item_end = cc.off + seg_len == cc.titem;
+    bf16x8 qop[QB][SD];
+    uint64_t mw[QB][4];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int row = rowbase + 32 * qb + col;
+      const bool ok = row < rows;
+      const int u = ok ? row / G : 0, gi = ok ? row % G : 0;
+      const uint16_t* qp = (const uint16_t*)a.q + ((size_t)(cc.b * n + u) * a.Hq + cc.g * G + gi) * D;
+#pragma unroll
+      for (int sd = 0; sd < SD; ++sd) {
+        u32x4 x = {0, 0, 0, 0};
+        if (ok) x = *(const u32x4*)(qp + 16 * sd + 8 * hh);
+        qop[qb][sd] = __builtin_bit_cast(bf16x8, x);
+      }
+      const uint64_t* mp = a.mask + ((size_t)cc.b * n + u) * a.W;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) mw[qb][w] = (ok && w < a.W) ? mp[w] : 0ull;
+    }
+    wait_vmcnt<0>();  // queries and masks are in registers (drains the ring once per segment)
+    f32x16 O[QB][DB];
+    float m_run[QB], lsum[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      m_run[qb] = -INFINITY;
+      lsum[qb] = 0.f;
+    }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) O[qb][db][r] = 0.f;
+
+    for (int j = 0; j < seg_len; ++j, ++it) {
+      wait_vmcnt<(S - 2) * LPW>();  // this wave's lines of tile `it` have landed
+      lds_barrier();                // ... everyone's, and everyone left tile it-1
+      {
+        const bool live = it + S - 1 < ntiles;
+        issue(ic, live, (it + S - 1) % S);
+        if (live) cursor_next(ic, plen, B, Hkv, k.cap, ttree);
+      }
+      const int off = cc.off + j;
+      const int st = it % S;
+      const char AS3* Kr = (const char AS3*)smem + st * STAGE;
+      const char AS3* Vr = Kr + REG;
+      if (off < cc.tpre && (off + 1) * kTK <= cc.L) {
+        const uint64_t nob[QB] = {};
+        sk_tile<D, QB, false>(Kr, Vr, qop, O, m_run, lsum, kofs, vofs, sl2, kTK, false, nob, hh);
+      } else {
+        const bool tree = off >= cc.tpre;
+        const int tstart = tree ? (off - cc.tpre) * kTK : off * kTK;
+        const int lim = tree ? n - tstart : cc.L - tstart;
+        const int wsel = tstart >> 6;
+        uint64_t bits[QB];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) bits[qb] = tree ? pick_word(mw[qb], wsel) : 0ull;
+        sk_tile<D, QB, true>(Kr, Vr, qop, O, m_run, lsum, kofs, vofs, sl2, lim, tree, bits, hh);
+      }
+    }
+
+    // write the segment out: whole items directly, pieces into this range's slots
+    const bool whole = seg_whole && item_end;
+    const int slot = 2 * v + (seg == 0 ? 0 : 1);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lsum[qb]), __float_as_uint(lsum[qb]),
+                                                       false, false);
+      const float ltot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+      const int row = rowbase + 32 * qb + col;
+      if (row >= rows) continue;
+      const int u = row / G, gi = row % G, h = cc.g * G + gi;
+      if (whole) {
+        const float inv = 1.f / ltot;
+        uint16_t* op = (uint16_t*)a.out + ((size_t)(cc.b * n + u) * a.Hq + h) * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int rq = 0; rq < 4; ++rq) {
+            const int d0 = 32 * db + 8 * rq + 4 * hh;
+            uint2 w;
+            w.x = (uint32_t)f32_to_bf16(O[qb][db][4 * rq] * inv) |
+                  ((uint32_t)f32_to_bf16(O[qb][db][4 * rq + 1] * inv) << 16);
+            w.y = (uint32_t)f32_to_bf16(O[qb][db][4 * rq + 2] * inv) |
+                  ((uint32_t)f32_to_bf16(O[qb][db][4 * rq + 3] * inv) << 16);
+            *(uint2*)(op + d0) = w;
+          }
+        if (a.lse != nullptr && hh == 0)
+          a.lse[(size_t)(cc.b * n + u) * a.Hq + h] = (m_run[qb] + __log2f(ltot)) * kLn2;
+      } else {
+        const size_t pidx = ((size_t)slot * k.rsplit + rs) * RW + (row - rs * RW);
+        float* wo = k.po + pidx * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int rq = 0; rq < 4; ++rq) {
+            const int d0 = 32 * db + 8 * rq + 4 * hh;
+            *(float4*)(wo + d0) = make_float4(O[qb][db][4 * rq], O[qb][db][4 * rq + 1], O[qb][db][4 * rq + 2],
+                                              O[qb][db][4 * rq + 3]);
+          }
+        if (hh == 0) {
+          k.pml[2 * pidx] = m_run[qb];
+          k.pml[2 * pidx + 1] = ltot;
+        }
+      }
+    }
+    // on to the next item
+    cc.off = 0;
+    if (++cc.g == Hkv) {
+      cc.g = 0;
+      if (++cc.b < B) cursor_seq(cc, plen, k.cap, ttree);
+    }
+  }
+  wait_vmcnt<0>();  // trailing zero-page loads land before the workgroup's LDS is released
+}
+
+// Combines the pieces of items that were split between ranges, and reports bad
+// prefix lengths and block ids.  One workgroup per (item, row slice, 64 rows).
+template <bool BF16OUT>
+__global__ __launch_bounds__(256) void sk_merge_kernel(AttnArgs a, SkArgs k, int RW, int chunks) {
+  const int D = a.D, rows = a.n * a.G, Hkv = a.Hkv;
+  int t = blockIdx.x;
+  const int ch = t % chunks;
+  t /= chunks;
+  const int rs = t % k.rsplit;
+  t /= k.rsplit;
+  const int g = t % Hkv, b = t / Hkv;
+  const int tid = threadIdx.x;
+
+  if (a.status != nullptr && g == 0 && rs == 0 && ch == 0) {
+    const int Lraw = a.plen[b];
+    int bad = (Lraw < 0 || Lraw > k.cap);
+    if (a.paged) {
+      const int L = clamp_len(Lraw, k.cap);
+      const int nb = (L + TV_PAGE - 1) / TV_PAGE;
+      for (int i = tid; i < nb; i += 256) {
+        const int id = a.bt[(size_t)b * a.max_blocks + i];
+        bad |= (id < 0 || id >= a.num_blocks);
+      }
+    }
+    bad = __syncthreads_or(bad);
+    if (tid == 0) a.status[b] = bad ? TV_EINVAL : TV_OK;
+  }
+
+  const int T = k.sched[0], per = k.sched[1];
+  const int cb0 = k.sched[4 + b], cb1 = k.sched[4 + b + 1];
+  const int titem = (cb1 - cb0) / Hkv;
+  const int s0 = cb0 + g * titem, e0 = s0 + titem;
+  const int ws = s0 / per, we = (e0 - 1) / per;
+  if (ws == we || T == 0) return;  // one range held the whole item and wrote it
+
+  const int tpr = D / 4;  // threads per row (4 values each)
+  const int rpp = 256 / tpr;
+  for (int rr = tid / tpr; rr < 64; rr += rpp) {
+    const int rloc = ch * 64 + rr;  // row within the slice
+    const int row = rs * RW + rloc;
+    if (rloc >= RW || row >= rows) continue;
+    const int d0 = (tid % tpr) * 4;
+    float M = -INFINITY;
+    for (int w = ws; w <= we; ++w) {
+      const int slot = (s0 <= (long long)w * per) ? 2 * w : 2 * w + 1;
+      const size_t pi = ((size_t)slot * k.rsplit + rs) * RW + rloc;
+      M = fmaxf(M, k.pml[2 * pi]);
+    }
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    float lt = 0.f;
+    for (int w = ws; w <= we; ++w) {
+      const int slot = (s0 <= (long long)w * per) ? 2 * w : 2 * w + 1;
+      const size_t pi = ((size_t)slot * k.rsplit + rs) * RW + rloc;
+      const float mc = k.pml[2 * pi], lc = k.pml[2 * pi + 1];
+      const float wgt = (mc == -INFINITY) ? 0.f : exp2f(mc - M);
+      const float4 oc = *(const float4*)(k.po + pi * D + d0);
+      acc.x += wgt * oc.x;
+      acc.y += wgt * oc.y;
+      acc.z += wgt * oc.z;
+      acc.w += wgt * oc.w;
+      lt += wgt * lc;
+    }
+    const float inv = 1.f / lt;
+    const int u = row / a.G, gi = row % a.G, h = g * a.G + gi;
+    const size_t oi = ((size_t)(b * a.n + u) * a.Hq + h) * D + d0;
+    if (BF16OUT) {
+      uint2 wv;
+      wv.x = (uint32_t)f32_to_bf16(acc.x * inv) | ((uint32_t)f32_to_bf16(acc.y * inv) << 16);
+      wv.y = (uint32_t)f32_to_bf16(acc.z * inv) | ((uint32_t)f32_to_bf16(acc.w * inv) << 16);
+      *(uint2*)((uint16_t*)a.out + oi) = wv;
+    } else {
+      *(float4*)((float*)a.out + oi) = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+    }
+    if (a.lse != nullptr && d0 == 0) a.lse[(size_t)(b * a.n + u) * a.Hq + h] = (M + log2f(lt)) * kLn2;
+  }
+}
+
+}  // namespace
+
+size_t sk_sched_bytes(int B, int NV) {
+  return (((size_t)sk_cursor_offset(B) + 4 * (size_t)NV) * sizeof(int32_t) + 255) & ~(size_t)255;
+}
+
+hipError_t launch_attn_sk(const AttnArgs& a, const AttnPlan& p, void* ws, hipStream_t s) {
+  if (a.B == 0) return hipSuccess;
+  const int NV = p.sk_nv, rsplit = p.rsplit, RW = 256;
+  SkArgs k;
+  k.sched = (const int32_t*)ws;
+  const size_t sb = sk_sched_bytes(a.B, NV);
+  const size_t slots = (size_t)2 * NV * rsplit * RW;
+  k.po = (float*)((char*)ws + sb);
+  k.pml = (float*)((char*)ws + sb + ((slots * a.D * sizeof(float) + 255) & ~(size_t)255));
+  k.rsplit = rsplit;
+  k.NV = NV;
+  k.cap = p.cap;
+  hipLaunchKernelGGL(sk_sched_kernel, dim3(1), dim3(1024), 0, s, a.plen, a.B, a.n, p.cap, a.Hkv, NV,
+                     (int32_t*)ws);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (a.D == 64)
+    hipLaunchKernelGGL((attn_sk_kernel<64, kSkQB, 8 / kSkQB, 4>), dim3(NV * rsplit), dim3(512 / kSkQB), 0, s, a, k);
+  else
+    hipLaunchKernelGGL((attn_sk_kernel<128, kSkQB, 8 / kSkQB, 4>), dim3(NV * rsplit), dim3(512 / kSkQB), 0, s, a,
+                       k);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int chunks = RW / 64;
+  hipLaunchKernelGGL(sk_merge_kernel<true>, dim3(a.B * a.Hkv * rsplit * chunks), dim3(256), 0, s, a, k, RW,
+                     chunks);
+  return hipGetLastError();
+}
+
+}  // namespace tv

@@ -64,6 +64,7 @@ int plan_attention(const tv_attn_desc* d, AttnPlan* p, int cus) {
   p->rows = d->n * G;
   p->cap = d->paged ? d->max_blocks * TV_PAGE : d->Lmax;
   p->ws_bytes = 0;
+  p->sk_nv = 0;
   p->rsplit = 1;
   p->nchunks = 1;
   p->chunk_len = p->cap > 0 ? p->cap : TV_PAGE;
@@ -80,6 +81,19 @@ int plan_attention(const tv_attn_desc* d, AttnPlan* p, int cus) {
   } else if (qb <= 4) {
     p->rb = 4, p->ks = 1, p->tk = 64;
   } else {
+    // many rows per KV head: 256-row workgroups on a balanced schedule of
+    // 64-key tiles (the tile count must fit in int32)
+    const long long rs = (p->rows + 255) / 256;
+    const long long tiles = (long long)d->B * d->Hkv * ((p->cap + 63) / 64 + (d->n + 63) / 64);
+    if (tiles < (1LL << 30)) {
+      p->rb = 4, p->ks = 1, p->tk = 64;
+      p->rsplit = (int)rs;
+      p->sk_nv = (int)(rs >= cus ? 1 : cus / rs);
+      const size_t slots = (size_t)2 * p->sk_nv * p->rsplit * 256;
+      p->ws_bytes = tv::sk_sched_bytes(d->B, p->sk_nv) + ((slots * d->D * sizeof(float) + 255) & ~(size_t)255) +
+                    ((slots * 2 * sizeof(float) + 255) & ~(size_t)255);
+      return TV_OK;
+    }
     p->rb = 8, p->ks = 1, p->tk = 64;
     p->rsplit = (qb + 7) / 8;
   }
@@ -206,16 +220,20 @@ int tree_attention(const tv_attn_desc* desc, const void* q, const void* k_cache,
   a.scale_log2 = scale * tv::kLog2e;
   a.ws_o = nullptr;
   a.ws_ml = nullptr;
-  if (p.ws_bytes > 0) {
+  if (p.ws_bytes > 0 && p.sk_nv == 0) {
     const size_t parts = (size_t)a.B * a.Hkv * p.nchunks * p.rows;
     const size_t o = (parts * a.D * sizeof(float) + 255) & ~(size_t)255;
     a.ws_o = (float*)workspace;
     a.ws_ml = (float*)((char*)workspace + o);
   }
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = desc->dtype == TV_BF16 ? tv::launch_attn_bf16(a, p, s) : tv::launch_attn_f32(a, p, s);
+  hipError_t e;
+  if (p.sk_nv > 0)
+    e = tv::launch_attn_sk(a, p, workspace, s);
+  else
+    e = desc->dtype == TV_BF16 ? tv::launch_attn_bf16(a, p, s) : tv::launch_attn_f32(a, p, s);
   if (e != hipSuccess) return hip_fail(e, "tree_attention launch");
-  if (desc->dtype == TV_BF16 && p.nchunks > 1) {
+  if (desc->dtype == TV_BF16 && p.sk_nv == 0 && p.nchunks > 1) {
     e = tv::launch_merge(a, p, true, s);
     if (e != hipSuccess) return hip_fail(e, "tree_attention merge launch");
   }

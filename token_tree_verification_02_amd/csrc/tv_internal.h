@@ -31,6 +31,7 @@ struct AttnPlan {
   int nchunks;     // prefix chunks (split-K) per (sequence, KV head)
   int chunk_len;   // prefix tokens per chunk (multiple of the tile)
   int cap;         // cache capacity per sequence in tokens
+  int sk_nv;       // > 0: balanced persistent schedule over this many tile ranges
   size_t ws_bytes; // workspace bytes
 };
 
@@ -57,6 +58,8 @@ struct AttnArgs {
 
 hipError_t launch_attn_bf16(const AttnArgs& a, const AttnPlan& p, hipStream_t s);
 hipError_t launch_attn_f32(const AttnArgs& a, const AttnPlan& p, hipStream_t s);
+size_t sk_sched_bytes(int B, int NV);
+hipError_t launch_attn_sk(const AttnArgs& a, const AttnPlan& p, void* ws, hipStream_t s);
 hipError_t launch_merge(const AttnArgs& a, const AttnPlan& p, bool bf16_out, hipStream_t s);
 hipError_t launch_tree_build(int B, int n, const int32_t* parent, const int32_t* depth,
                              const int32_t* plen, uint64_t* mask, int32_t* pos, int32_t* status,
