@@ -31,6 +31,8 @@
 // bf16-rounded probabilities that also feed the PV product.
 #include <float.h>
 
+#include <type_traits>
+
 #include "attn_bf16_common.h"
 
 namespace tv {
@@ -221,17 +223,22 @@ __device__ __forceinline__ void sk_pv(const char AS3* Vr, int kb, const bf16x8 (
                                       const uint32_t (&vofs)[D / 32]) {
   constexpr int DB = D / 32, ROWB = 2 * D;
 #pragma unroll
-  for (int half = 0; half < 2; ++half)
+  for (int half = 0; half < 2; ++half) {
+    bf16x8 vop[DB];  // the half block's operand reads first, then its products
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       const char AS3* vp = Vr + (kb * 32 + 16 * half) * ROWB + vofs[db];
       const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 AS3*)vp);
       const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 AS3*)(vp + 4 * ROWB));
-      const bf16x8 vop = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      vop[db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
-        O[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, P[qb][half], O[qb][db], 0, 0, 0);
-    }
+        O[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[db], P[qb][half], O[qb][db], 0, 0, 0);
+  }
 }
 
 // S^T = K Q^T for one 32-key block and all QB query blocks (each K operand read
@@ -244,13 +251,17 @@ __device__ __forceinline__ void sk_qk(const char AS3* Kr, int kb, const bf16x8 (
   for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) Sa[qb][r] = 0.f;
+  // all operand reads of the block first (they pipeline in the LDS), then the
+  // products: the scheduler may not pair each read with its product
+  bf16x8 kop[SD];
 #pragma unroll
-  for (int sd = 0; sd < SD; ++sd) {
-    const bf16x8 kop = *(const bf16x8 AS3*)(Kr + kb * 32 * ROWB + kofs[sd]);
+  for (int sd = 0; sd < SD; ++sd) kop[sd] = *(const bf16x8 AS3*)(Kr + kb * 32 * ROWB + kofs[sd]);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int sd = 0; sd < SD; ++sd)
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
-      Sa[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[qb][sd], Sa[qb], 0, 0, 0);
-  }
+      Sa[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[sd], qop[qb][sd], Sa[qb], 0, 0, 0);
 }
 
 // One 64-key tile for one wave holding QB 32-row query blocks.  MASKED: key
@@ -519,7 +530,12 @@ __global__ __launch_bounds__(64 * RB) void attn_sk_kernel(AttnArgs a, SkArgs k) 
 #pragma unroll
         for (int r = 0; r < 16; ++r) O[qb][db][r] = 0.f;
 
-    for (int j = 0; j < seg_len; ++j, ++it) {
+    // One tile iteration: wait for the tile, free the stage of the previous one,
+    // refill the ring, compute.  The full prefix tiles of the segment run first
+    // in a loop without any masking code, then the masked ones (the ragged last
+    // prefix tile and the tree tiles) in a second loop.
+    auto step = [&](auto masked_c, int j) {
+      constexpr bool MASKED = decltype(masked_c)::value;
       wait_vmcnt<(S - 2) * LPW>();  // this wave's lines of tile `it` have landed
       lds_barrier();                // ... everyone's, and everyone left tile it-1
       {
@@ -531,20 +547,25 @@ __global__ __launch_bounds__(64 * RB) void attn_sk_kernel(AttnArgs a, SkArgs k) 
       const int st = it % S;
       const char AS3* Kr = (const char AS3*)smem + st * STAGE;
       const char AS3* Vr = Kr + REG;
-      if (off < cc.tpre && (off + 1) * kTK <= cc.L) {
-        const uint64_t nob[QB] = {};
-        sk_tile<D, QB, false>(Kr, Vr, qop, O, m_run, lsum, kofs, vofs, sl2, kTK, false, nob, hh);
-      } else {
-        const bool tree = off >= cc.tpre;
+      uint64_t bits[QB];
+      int lim = kTK;
+      bool tree = false;
+      if constexpr (MASKED) {
+        tree = off >= cc.tpre;
         const int tstart = tree ? (off - cc.tpre) * kTK : off * kTK;
-        const int lim = tree ? n - tstart : cc.L - tstart;
-        const int wsel = tstart >> 6;
-        uint64_t bits[QB];
+        lim = tree ? n - tstart : cc.L - tstart;
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) bits[qb] = tree ? pick_word(mw[qb], wsel) : 0ull;
-        sk_tile<D, QB, true>(Kr, Vr, qop, O, m_run, lsum, kofs, vofs, sl2, lim, tree, bits, hh);
+        for (int qb = 0; qb < QB; ++qb) bits[qb] = tree ? pick_word(mw[qb], tstart >> 6) : 0ull;
+      } else {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) bits[qb] = 0ull;
       }
-    }
+      sk_tile<D, QB, MASKED>(Kr, Vr, qop, O, m_run, lsum, kofs, vofs, sl2, lim, tree, bits, hh);
+      ++it;
+    };
+    const int nfull = max(0, min(seg_len, cc.L / kTK - cc.off));  // full prefix tiles come first
+    for (int j = 0; j < nfull; ++j) step(std::integral_constant<bool, false>(), j);
+    for (int j = nfull; j < seg_len; ++j) step(std::integral_constant<bool, true>(), j);
 
     // write the segment out: whole items directly, pieces into this range's slots
     const bool whole = seg_whole && item_end;
