@@ -240,7 +240,6 @@ __global__ __launch_bounds__(64 * RB * KS) void attn_bf16_kernel(AttnArgs a, int
       if (a.W > 3) mw3 = mp[3];
     }
   }
-  wait_vmcnt<0>();  // operands are in registers before the pipeline starts
 
   // ---- per-lane LDS read offsets (the key-block and stage parts are added later)
   uint32_t kofs[C::SD], vofs[C::DB];
@@ -264,13 +263,19 @@ __global__ __launch_bounds__(64 * RB * KS) void attn_bf16_kernel(AttnArgs a, int
   float m_run = -INFINITY, lsum = 0.f;
   const float sl2 = a.scale_log2;
 
-  // prologue: S-1 tiles in flight
+  // prologue: S-1 tiles in flight, issued before the query loads have returned
+  // so the two latencies overlap; the full wait (which the compiler can see)
+  // then leaves no load of its own pending inside the loop
 #pragma unroll
   for (int i = 0; i < S - 1; ++i) issue(i * KS + ks, i);
+  wait_vmcnt<0>();
 
   for (int it = 0; it < iters; ++it) {
     wait_vmcnt<(S - 2) * C::LPW>();  // this wave's lines of iteration `it` have landed
-    lds_barrier();                    // ... everyone's, and everyone left iteration it-1
+    // With one wave per key-split group a wave only reads the ring region it
+    // filled itself (its own vmcnt wait covers it, and its reads of the stage it
+    // refills next were consumed last iteration), so it runs without barriers.
+    if constexpr (RB > 1) lds_barrier();  // ... everyone's, and everyone left iteration it-1
     issue((it + S - 1) * KS + ks, (it + S - 1) % S);
 
     const int tt = it * KS + ks;
