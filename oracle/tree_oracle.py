@@ -25,6 +25,13 @@ from the stored input values (bf16 -> float64 and fp32 -> float64 are exact):
   the accept-up-to-first-mismatch-plus-one-target-token rule is the sequence
   case on the speculative-decoding explainer, technical mechanism section, and
   on the speculative-decoding operations guide's diagram, applied per branch.)
+* commit_kv: the keys and values of the accepted root path become ordinary
+  prefix tokens: path node t goes to cache position L_b + t, so the cache
+  again holds one linear sequence and the next step attends it like any
+  prefix.  (Explainer, kernel-fusion section, item on depth-first traversal
+  keeping the tree consistent with the existing KV cache; "practical
+  applications" section on PagedAttention's block-wise KV memory, which gives
+  the paged layout.)
 
 Layouts are those of include/tree_verify.h.  No blocking, fusion or reordering
 is done beyond vectorising the prefix scores of all rows of a KV head, which
@@ -35,6 +42,7 @@ from __future__ import annotations
 import numpy as np
 
 TV_OK = 0
+TV_EINVAL = 1
 TV_ETOPOLOGY = 2
 PAGE = 16
 
@@ -201,3 +209,51 @@ def verify_greedy(logits: np.ndarray, tokens: np.ndarray, parent: np.ndarray, dt
         plen[b] = len(p)
         bonus[b] = bo
     return am, path, plen, bonus
+
+
+# ----------------------------------------------------------------------------- KV commit
+def cache_index(w: dict, b: int, j: int):
+    """Index of token j of sequence b in a cache array: selects its [Hkv][D] rows."""
+    if w["cfg"].paged:
+        return (int(w["block_table"][b][j // PAGE]), slice(None), j % PAGE)
+    return (b, slice(None), j)
+
+
+def commit_kv(w: dict, path: np.ndarray, path_len: np.ndarray):
+    """Append the accepted path's tree keys/values to each sequence's cache.
+
+    Sequence b with prefix length L and P = path_len[b] accepted nodes gets
+    k_tree[b][path[b][t]] (all KV heads) at cache position L + t for t < P;
+    its new length is L + P.  A sequence is rejected as a whole (status
+    TV_EINVAL, cache untouched, new length L) if P is outside [0, n], a path
+    entry t < P is outside [0, n), L + P exceeds the capacity, or (paged) a
+    block id covering positions L..L+P-1 is outside [0, num_blocks).
+
+    Returns (k_cache, v_cache, new_len [B], status [B]); the caches are copies.
+    """
+    cfg = w["cfg"]
+    B, n = cfg.B, cfg.n
+    kc, vc = w["k_cache"].copy(), w["v_cache"].copy()
+    plen = np.asarray(w["prefix_len"])
+    new_len = plen.astype(np.int32).copy()
+    status = np.full(B, TV_OK, np.int32)
+    if cfg.paged:
+        bt = np.asarray(w["block_table"])
+        cap = w["max_blocks"] * PAGE
+    else:
+        cap = w["Lmax"]
+    for b in range(B):
+        L, P = int(plen[b]), int(path_len[b])
+        ok = 0 <= L and 0 <= P <= n and L + P <= cap
+        ok = ok and all(0 <= int(path[b][t]) < n for t in range(P))
+        if ok and cfg.paged:
+            ok = all(0 <= int(bt[b, j // PAGE]) < w["num_blocks"] for j in range(L, L + P))
+        if not ok:
+            status[b] = TV_EINVAL
+            continue
+        for t in range(P):
+            at = cache_index(w, b, L + t)
+            kc[at] = w["k_tree"][b, int(path[b][t])]
+            vc[at] = w["v_tree"][b, int(path[b][t])]
+        new_len[b] = L + P
+    return kc, vc, new_len, status

@@ -266,7 +266,7 @@ def children_lists(parent: np.ndarray) -> list[list[int]]:
 
 # ----------------------------------------------------------------------------- workload
 def make(cfg: Config, seed: int | None = None, *, variant: str = "plain", plant: bool = True,
-         poison: bool = True, with_logits: bool = True) -> dict:
+         poison: bool = True, with_logits: bool = True, room: int = 0) -> dict:
     """Seeded inputs for one workload.
 
     variant:
@@ -277,6 +277,8 @@ def make(cfg: Config, seed: int | None = None, *, variant: str = "plain", plant:
                  tolerance.  a_b solves a^2 = sqrt(D)*(ln(L_b/|S|) + (a^2 + D/16)/(2D)).
       "needle"   one dominant prefix key at j = L_b - 1 (pins the prefix end).
     plant: planted accept paths, duplicate sibling tokens and logit ties (needs vocab).
+    room: cache capacity kept free after each prefix, in tokens (NaN-filled), for
+          committing accepted tokens; paged sequences get blocks for L_b + room tokens.
     """
     seed = cfg.index if seed is None else seed
     dt = cfg.dtype
@@ -305,9 +307,9 @@ def make(cfg: Config, seed: int | None = None, *, variant: str = "plain", plant:
     offs = np.concatenate([[0], np.cumsum(prefix_len.astype(np.int64))])
     edt = np.uint16 if dt == "bf16" else np.float32
     if cfg.paged:
-        nblk = (prefix_len + PAGE - 1) // PAGE
+        nblk = (prefix_len + room + PAGE - 1) // PAGE
         total_blocks = int(nblk.sum())
-        max_blocks = (cfg.L_hi + PAGE - 1) // PAGE
+        max_blocks = (cfg.L_hi + room + PAGE - 1) // PAGE
         perm = _rng(seed, _S_PERM).permutation(total_blocks).astype(np.int32)
         bt = np.full((B, max_blocks), -1, np.int32)
         k_cache = np.full((total_blocks, Hkv, PAGE, D), _nan(dt), edt)
@@ -331,7 +333,7 @@ def make(cfg: Config, seed: int | None = None, *, variant: str = "plain", plant:
                 v_cache[blk, :, :rem, :] = vv[full * PAGE:].transpose(1, 0, 2)
         out.update(block_table=bt, max_blocks=max_blocks, num_blocks=total_blocks, Lmax=0)
     else:
-        Lmax = cfg.capacity
+        Lmax = max(cfg.capacity, (cfg.L_hi + room + PAGE - 1) // PAGE * PAGE)
         k_cache = np.full((B, Hkv, Lmax, D), _nan(dt), edt)
         v_cache = np.full((B, Hkv, Lmax, D), _nan(dt), edt)
         for b in range(B):
