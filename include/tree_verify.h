@@ -5,7 +5,8 @@
  * single forward pass: every tree node u attends to the shared prefix KV cache
  * plus exactly the nodes on its own root-to-u path S_u, and greedy
  * verification then walks the tree from the root.  This library is that hot
- * path: three calls, all asynchronous on a caller-provided HIP stream.
+ * path: three calls, all asynchronous on a caller-provided HIP stream, and a
+ * fourth that commits the accepted path's keys and values to the cache.
  *
  * Sources (the SpecInfer explainer at 0h-n0.github.io, "paper-2305-09781"):
  *   - token-tree structure section: a node per token, S_u = tokens on the path
@@ -168,6 +169,43 @@ int tree_verify_greedy(int B, int n, int V, int logits_dtype, const void* logits
                        const int32_t* tokens, const int32_t* parent,
                        int32_t* argmax_out, int32_t* path_out, int32_t* path_len,
                        int32_t* bonus, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * tree_commit_kv: the accepted path's keys and values become prefix tokens.
+ *
+ * After verification the accepted root path is an ordinary continuation of the
+ * sequence: its KV is written into the cache right after the prefix, in path
+ * (root-first, depth-first) order, so the next step attends it as prefix (the
+ * explainer's kernel-fusion section: depth-first order keeps the tree consistent
+ * with the existing KV cache; its "practical applications" section: the
+ * block-wise memory of PagedAttention).  For sequence b with L = prefix_len[b]
+ * and P = path_len[b]:
+ *   cache position L + t  <-  k_tree[b][path[b][t]], v_tree[b][path[b][t]]
+ *                             (all Hkv heads), t = 0 .. P-1
+ *   new_prefix_len[b] = L + P
+ *
+ *   desc        as for tree_attention (Hq and scale are not used)
+ *   k_cache, v_cache   in/out, layouts of tree_attention; only positions
+ *                      L..L+P-1 of each sequence are written.  Paged: the
+ *                      caller has already put blocks for those positions in
+ *                      block_table (block allocation is the caller's).
+ *   k_tree, v_tree  [B][n][Hkv][D]    path [B][n], path_len [B] int32 (the
+ *                   outputs of tree_verify_greedy; entries t >= P not read)
+ *   new_prefix_len [B] int32 out; must not overlap prefix_len
+ *   status [B] int32 out (may be NULL): TV_OK, or TV_EINVAL for a sequence with
+ *     P outside [0, n], a path entry t < P outside [0, n), L < 0,
+ *     L + P > capacity, or (paged) a block id for positions L..L+P-1 outside
+ *     [0, num_blocks).  Such a sequence is not written at all and its
+ *     new_prefix_len is L.
+ * Blocks written for different sequences must be distinct (writes to a block
+ * shared by two sequences race).  Host errors: TV_EINVAL, TV_EUNSUPPORTED as
+ * for tree_attention.
+ * ------------------------------------------------------------------------- */
+int tree_commit_kv(const tv_attn_desc* desc, void* k_cache, void* v_cache,
+                   const int32_t* block_table, const int32_t* prefix_len,
+                   const void* k_tree, const void* v_tree, const int32_t* path,
+                   const int32_t* path_len, int32_t* new_prefix_len,
+                   int32_t* status, void* stream);
 
 #ifdef __cplusplus
 }

@@ -130,3 +130,25 @@ def test_verify_argument_errors(lib):
     assert lib.tree_verify_greedy(2, 7, 10, 9, *args, None) == tv.TV_EUNSUPPORTED
     assert lib.tree_verify_greedy(2, 7, 10, tv.TV_F32, *([None] * 8), None) == tv.TV_EINVAL
     assert lib.tree_verify_greedy(0, 7, 10, tv.TV_F32, *([None] * 8), None) == tv.TV_OK
+
+
+def call_commit(lib, d, ptrs=None, new_len=0x300000):
+    p = [0x100000, 0x100000, 0x100000, 0x200000, 0x100000, 0x100000, 0x100000, 0x100000] if ptrs is None else ptrs
+    return lib.tree_commit_kv(ctypes.byref(d), *p, new_len, None, None)
+
+
+def test_commit_argument_errors(lib):
+    assert call_commit(lib, desc(D=80)) == tv.TV_EUNSUPPORTED
+    assert call_commit(lib, desc(dtype=3)) == tv.TV_EUNSUPPORTED
+    assert call_commit(lib, desc(Lmax=24)) == tv.TV_EINVAL
+    assert call_commit(lib, desc(n=0)) == tv.TV_EINVAL
+    assert call_commit(lib, desc(), new_len=None) == tv.TV_EINVAL                 # null output
+    assert call_commit(lib, desc(), ptrs=[None] * 8) == tv.TV_EINVAL              # null inputs
+    assert call_commit(lib, desc(paged=True, max_blocks=4, num_blocks=4),
+                       ptrs=[0x100000, 0x100000, None] + [0x100000] * 5) == tv.TV_EINVAL   # no block table
+    misaligned = [0x100008, 0x100000, 0x100000, 0x200000, 0x100000, 0x100000, 0x100000, 0x100000]
+    assert call_commit(lib, desc(), ptrs=misaligned) == tv.TV_EINVAL
+    assert call_commit(lib, desc(), new_len=0x200000) == tv.TV_EINVAL             # aliases prefix_len
+    assert call_commit(lib, desc(B=8), new_len=0x200000 + 28) == tv.TV_EINVAL     # overlaps it
+    assert "overlap" in tv.last_error()
+    assert lib.tree_commit_kv(ctypes.byref(desc(B=0)), *([None] * 10), None) == tv.TV_OK

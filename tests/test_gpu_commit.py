@@ -1,0 +1,181 @@
+"""GPU parity of tree_commit_kv against the oracle's commit, through the C ABI.
+
+A commit is a copy, so the caches must match the oracle's byte for byte,
+everywhere (unwritten NaN-filled slots included), and new lengths and statuses
+must match exactly.  Paths are chosen on the host from the tree (root paths to
+random nodes, the whole chain, empty) or come from the oracle's greedy
+verification, never from the GPU.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from token_tree_verification_02_amd import runner
+from token_tree_verification_02_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def root_path(parent, u):
+    out = [u]
+    while out[-1] != 0:
+        out.append(int(parent[out[-1]]))
+    return out[::-1]
+
+
+def random_paths(w, rng):
+    cfg = w["cfg"]
+    path = np.full((cfg.B, cfg.n), -1, np.int32)
+    plen = np.zeros(cfg.B, np.int32)
+    for b in range(cfg.B):
+        p = root_path(w["parent"][b], int(rng.integers(0, cfg.n)))
+        path[b, :len(p)] = p
+        plen[b] = len(p)
+    return path, plen
+
+
+def raw(t):
+    """Device cache -> host array of its raw bits (NaN patterns compare equal)."""
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy().view(np.uint32)
+
+
+def bits(a, dtype):
+    return a.view(np.uint16) if dtype == "bf16" else a.view(np.uint32)
+
+
+def commit_and_check(w, path, plen, d=None):
+    cfg = w["cfg"]
+    d = runner.upload(w) if d is None else d
+    pt = torch.from_numpy(np.ascontiguousarray(path, dtype=np.int32)).cuda()
+    lt = torch.from_numpy(np.ascontiguousarray(plen, dtype=np.int32)).cuda()
+    runner.commit(d, pt, lt)
+    torch.cuda.synchronize()
+    kc, vc, new_len, status = oracle.commit_kv(w, path, plen)
+    np.testing.assert_array_equal(d["commit_status"].cpu().numpy(), status)
+    np.testing.assert_array_equal(d["new_len"].cpu().numpy(), new_len)
+    assert np.array_equal(raw(d["k_cache"]), bits(kc, cfg.dtype)), "K cache differs"
+    assert np.array_equal(raw(d["v_cache"]), bits(vc, cfg.dtype)), "V cache differs"
+    log(f"  {cfg.name}: committed {list(plen[:8])} status {list(status[:8])}")
+    return d
+
+
+CASES = {
+    "llama_contig": W.config(2, B=3, L_lo=1000, L_hi=1000, vocab=0),
+    "merge_gqa": W.config(3, B=4, L_lo=5, L_hi=777, vocab=0),
+    "paged_ragged": W.config(4, B=5, L_lo=1, L_hi=300, vocab=0),
+    "paged_block_edge": W.config(4, B=3, L_lo=16, L_hi=16, vocab=0),
+    "wide_w2": W.config(5, B=3, L_lo=0, L_hi=200, Lmax=208, vocab=0),
+    "n256": W.config(3, B=2, n=256, Hq=8, Hkv=8, tree="random", max_depth=40, L_lo=50, L_hi=300, vocab=0),
+    "fp32_d64": W.config(1, B=3, L_lo=3, L_hi=100),
+    "fp32_paged": W.config(4, B=2, dtype="f32", L_lo=30, L_hi=70, n=12, vocab=0),
+    "bf16_d64_paged": W.config(4, B=3, D=64, L_lo=40, L_hi=150, vocab=0),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_commit_parity(name):
+    cfg = CASES[name]
+    log(f"case commit {name}")
+    w = W.make(cfg, seed=31, room=cfg.n)
+    path, plen = random_paths(w, np.random.default_rng(7))
+    commit_and_check(w, path, plen)
+
+
+def test_commit_whole_chain_and_empty():
+    log("case commit chain / empty")
+    cfg = W.config(4, B=4, tree="chain", n=40, L_lo=10, L_hi=60, vocab=0)
+    w = W.make(cfg, seed=2, room=cfg.n)
+    path = np.tile(np.arange(cfg.n, dtype=np.int32), (cfg.B, 1))
+    plen = np.array([cfg.n, 0, 1, cfg.n], np.int32)
+    path[1] = -1                                       # P = 0: the path is not read
+    commit_and_check(w, path, plen)
+
+
+def test_commit_fills_capacity_exactly():
+    log("case commit to capacity")
+    cfg = W.config(2, B=2, L_lo=1000, L_hi=1000, vocab=0)
+    w = W.make(cfg, seed=5, room=cfg.n)                  # Lmax = 1024: room for 24 tokens
+    cap = w["Lmax"]
+    w["prefix_len"] = np.array([cap - 9, cap - 8], np.int32)
+    path = np.full((cfg.B, cfg.n), -1, np.int32)
+    plen = np.zeros(cfg.B, np.int32)
+    deep = int(np.argmax(w["depth"][0]))                  # depth 8: 9 nodes
+    for b in range(cfg.B):
+        p = root_path(w["parent"][b], deep)
+        path[b, :len(p)] = p
+        plen[b] = len(p)
+    commit_and_check(w, path, plen)                        # b=0 fits exactly, b=1 is one past
+
+
+def test_commit_rejections_leave_the_sequence_untouched():
+    log("case commit rejections")
+    cfg = W.config(4, B=6, L_lo=20, L_hi=90, vocab=0)
+    w = W.make(cfg, seed=9, room=8)
+    path, plen = random_paths(w, np.random.default_rng(3))
+    plen = np.minimum(plen, 4)
+    plen[0] = cfg.n + 1                                   # longer than the tree
+    path[1, 0] = cfg.n                                    # node id out of range
+    plen[2] = -3                                          # negative length
+    L3 = int(w["prefix_len"][3])
+    w["block_table"] = w["block_table"].copy()
+    w["block_table"][3, (L3 + int(plen[3]) - 1) // 16] = w["num_blocks"] + 5   # bad block id
+    w["prefix_len"] = w["prefix_len"].copy()
+    w["prefix_len"][4] = -1                               # negative prefix length
+    commit_and_check(w, path, plen)                        # sequence 5 alone is written
+
+
+def test_commit_of_greedy_path_then_next_step():
+    """Verification's accepted path (the oracle's, equal to the GPU's bit for bit)
+    committed on the GPU; the next step's tree attention over the grown cache
+    matches the oracle on the oracle-committed cache."""
+    log("case commit after verify")
+    cfg = W.config(2, B=3, L_lo=200, L_hi=200)
+    w = W.make(cfg, seed=4, room=cfg.n)
+    am, path, plen, bonus = oracle.verify_greedy(w["logits"], w["tokens"], w["parent"], cfg.dtype)
+    d = runner.upload(w)
+    runner.step(d)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(d["path"].cpu().numpy(), path)
+    np.testing.assert_array_equal(d["path_len"].cpu().numpy(), plen)
+    runner.commit(d)                                      # the GPU's own path
+    torch.cuda.synchronize()
+    kc, vc, new_len, status = oracle.commit_kv(w, path, plen)
+    assert (status == 0).all()
+    assert np.array_equal(raw(d["k_cache"]), bits(kc, cfg.dtype))
+    assert np.array_equal(raw(d["v_cache"]), bits(vc, cfg.dtype))
+    # next step: a fresh tree over the grown prefix
+    w2 = W.make(cfg, seed=40, room=cfg.n)
+    w2.update(k_cache=kc, v_cache=vc, prefix_len=new_len)
+    d2 = runner.upload(w2)
+    d2["k_cache"], d2["v_cache"] = d["k_cache"], d["v_cache"]
+    d2["prefix_len"] = d["new_len"]
+    runner.build(d2)
+    runner.attention(d2)
+    torch.cuda.synchronize()
+    O_ref, _ = oracle.tree_attention(w2)
+    O = runner.out_f64(d2)
+    err = float(np.abs(O - O_ref).max())
+    log(f"  next step max|dO|={err:.3e}")
+    assert err <= 2e-2
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("index", [4, 5])
+def test_commit_full_size(index):
+    """Full-size workloads with room for the tree; every sequence commits a root path."""
+    cfg = W.config(index, vocab=0)
+    log(f"case commit full-size {cfg.name}: generating")
+    w = W.make(cfg, room=cfg.n, with_logits=False)
+    path, plen = random_paths(w, np.random.default_rng(index))
+    log("  running")
+    commit_and_check(w, path, plen)

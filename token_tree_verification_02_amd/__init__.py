@@ -1,10 +1,11 @@
 """Token-tree verification hot path for MI355X (gfx950).
 
 SpecInfer's tree attention (each tree node attends to the cached prefix plus its
-own root path, in one pass) and greedy tree verification, as hand-written HIP
-kernels behind the C ABI in include/tree_verify.h.  The functions here are the
+own root path, in one pass), greedy tree verification and the commit of the
+accepted path's keys and values to the cache, as hand-written HIP kernels behind
+the C ABI in include/tree_verify.h.  The functions here are the
 ctypes binding of that library; torch provides device memory and streams.
 """
 from ._lib import (TV_BF16, TV_EHIP, TV_EINVAL, TV_ETOPOLOGY, TV_EUNSUPPORTED, TV_EWORKSPACE,  # noqa: F401
                    TV_F32, TV_NMAX, TV_OK, TV_PAGE, TreeVerifyError, attn_desc, last_error, load,
-                   tree_attention, tree_build, tree_verify_greedy, validate_host, workspace_size)
+                   tree_attention, tree_build, tree_commit_kv, tree_verify_greedy, validate_host, workspace_size)

@@ -47,6 +47,8 @@ SIGNATURES = {
     "tree_attention": (_c_int, [ctypes.POINTER(AttnDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                 _vp, _vp, _size_t, _vp]),
     "tree_verify_greedy": (_c_int, [_c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "tree_commit_kv": (_c_int, [ctypes.POINTER(AttnDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                _vp]),
 }
 
 
@@ -114,7 +116,7 @@ def workspace_size(desc: AttnDesc) -> int:
     return int(load().tree_attention_workspace_size(ctypes.byref(desc)))
 
 
-# ----------------------------------------------------------------------------- the three calls
+# ----------------------------------------------------------------------------- the library calls
 def tree_build(parent, depth, prefix_len, *, mask=None, pos=None, status=None, stream=None):
     """parent, depth [B][n] int32, prefix_len [B] int32 -> (mask [B][n][W] int64 view of
     the uint64 words, pos [B][n] int32, status [B] int32)."""
@@ -173,3 +175,25 @@ def tree_verify_greedy(logits, tokens, parent, *, argmax=None, path=None, path_l
                                    _ptr(argmax), _ptr(path), _ptr(path_len), _ptr(bonus), _stream(stream))
     _check(rc, "tree_verify_greedy")
     return argmax, path, path_len, bonus
+
+
+def tree_commit_kv(k_cache, v_cache, prefix_len, k_tree, v_tree, path, path_len, *, block_table=None,
+                   num_blocks=0, new_prefix_len=None, status=None, stream=None):
+    """Write the accepted path's tree K/V into the cache (in place) at positions
+    prefix_len[b] + t.  Caches contiguous (k, v [B][Hkv][Lmax][D]) or paged when
+    block_table is given; k_tree, v_tree [B][n][Hkv][D]; path [B][n], path_len [B]
+    as from tree_verify_greedy.  Returns (new_prefix_len [B], status [B])."""
+    B, n, Hkv, D = k_tree.shape
+    dev = k_tree.device
+    if block_table is not None:
+        desc = attn_desc(B, n, Hkv, Hkv, D, _dtype_code(k_tree), paged=True, max_blocks=block_table.shape[1],
+                         num_blocks=num_blocks or k_cache.shape[0])
+    else:
+        desc = attn_desc(B, n, Hkv, Hkv, D, _dtype_code(k_tree), Lmax=k_cache.shape[2])
+    new_prefix_len = torch.empty((B,), dtype=torch.int32, device=dev) if new_prefix_len is None else new_prefix_len
+    status = torch.empty((B,), dtype=torch.int32, device=dev) if status is None else status
+    rc = load().tree_commit_kv(ctypes.byref(desc), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                               _ptr(prefix_len), _ptr(k_tree), _ptr(v_tree), _ptr(path), _ptr(path_len),
+                               _ptr(new_prefix_len), _ptr(status), _stream(stream))
+    _check(rc, "tree_commit_kv")
+    return new_prefix_len, status

@@ -258,4 +258,25 @@ int tree_verify_greedy(int B, int n, int V, int logits_dtype, const void* logits
   return TV_OK;
 }
 
+int tree_commit_kv(const tv_attn_desc* desc, void* k_cache, void* v_cache, const int32_t* block_table,
+                   const int32_t* prefix_len, const void* k_tree, const void* v_tree, const int32_t* path,
+                   const int32_t* path_len, int32_t* new_prefix_len, int32_t* status, void* stream) {
+  int rc = check_desc(desc);
+  if (rc != TV_OK) return rc;
+  if ((long long)desc->B * desc->n > 0x7fffffffLL) return fail(TV_EINVAL, "B*n too large");
+  if (desc->B == 0) return TV_OK;
+  if (!k_cache || !v_cache || !prefix_len || !k_tree || !v_tree || !path || !path_len || !new_prefix_len)
+    return fail(TV_EINVAL, "null pointer argument");
+  if (desc->paged && desc->max_blocks > 0 && !block_table) return fail(TV_EINVAL, "null block_table");
+  const uintptr_t al = (uintptr_t)k_cache | (uintptr_t)v_cache | (uintptr_t)k_tree | (uintptr_t)v_tree;
+  if (al & 15) return fail(TV_EINVAL, "device pointers must be 16-byte aligned");
+  const uintptr_t a0 = (uintptr_t)prefix_len, a1 = (uintptr_t)new_prefix_len;
+  const uintptr_t nb = (uintptr_t)desc->B * sizeof(int32_t);
+  if (a0 < a1 + nb && a1 < a0 + nb) return fail(TV_EINVAL, "new_prefix_len overlaps prefix_len");
+  hipError_t e = tv::launch_commit(desc, k_cache, v_cache, block_table, prefix_len, k_tree, v_tree, path, path_len,
+                                   new_prefix_len, status, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "tree_commit_kv launch");
+  return TV_OK;
+}
+
 }  // extern "C"

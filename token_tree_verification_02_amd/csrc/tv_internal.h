@@ -64,6 +64,9 @@ hipError_t launch_merge(const AttnArgs& a, const AttnPlan& p, bool bf16_out, hip
 hipError_t launch_tree_build(int B, int n, const int32_t* parent, const int32_t* depth,
                              const int32_t* plen, uint64_t* mask, int32_t* pos, int32_t* status,
                              hipStream_t s);
+hipError_t launch_commit(const tv_attn_desc* d, void* kc, void* vc, const int32_t* bt, const int32_t* plen,
+                         const void* kt, const void* vt, const int32_t* path, const int32_t* path_len,
+                         int32_t* new_len, int32_t* status, hipStream_t s);
 hipError_t launch_verify(int B, int n, int V, int bf16, const void* logits, const int32_t* tokens,
                          const int32_t* parent, int32_t* am, int32_t* path, int32_t* plen,
                          int32_t* bonus, hipStream_t s);

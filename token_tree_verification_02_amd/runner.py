@@ -35,6 +35,8 @@ def upload(w: dict, device="cuda") -> dict:
     d["out"] = torch.empty_like(d["q"])
     d["lse"] = torch.empty((B, n, cfg.Hq), dtype=torch.float32, device=device)
     d["attn_status"] = torch.empty((B,), dtype=torch.int32, device=device)
+    d["new_len"] = torch.empty((B,), dtype=torch.int32, device=device)
+    d["commit_status"] = torch.empty((B,), dtype=torch.int32, device=device)
     desc = attn_desc_of(d)
     ws = _lib.workspace_size(desc)
     d["workspace"] = torch.empty(max(ws, 1), dtype=torch.uint8, device=device) if ws else None
@@ -70,6 +72,15 @@ def attention(d, stream=None):
 def verify(d, stream=None):
     return _lib.tree_verify_greedy(d["logits"], d["tokens"], d["parent"], argmax=d["argmax"], path=d["path"],
                                    path_len=d["path_len"], bonus=d["bonus"], stream=stream)
+
+
+def commit(d, path=None, path_len=None, stream=None):
+    """Commit an accepted path (default: the one tree_verify_greedy wrote) into d's cache."""
+    path = d["path"] if path is None else path
+    path_len = d["path_len"] if path_len is None else path_len
+    return _lib.tree_commit_kv(d["k_cache"], d["v_cache"], d["prefix_len"], d["k_tree"], d["v_tree"], path,
+                               path_len, block_table=d["block_table"], num_blocks=d["num_blocks"],
+                               new_prefix_len=d["new_len"], status=d["commit_status"], stream=stream)
 
 
 def step(d, stream=None):
@@ -109,6 +120,18 @@ class Step:
             code = _lib.TV_BF16 if cfg.dtype == "bf16" else _lib.TV_F32
             self.verify_args = (cfg.B, cfg.n, cfg.vocab, code, P(d["logits"]), P(d["tokens"]), P(d["parent"]),
                                 P(d["argmax"]), P(d["path"]), P(d["path_len"]), P(d["bonus"]))
+
+    def commit_args(self, path, path_len):
+        """C-ABI arguments of tree_commit_kv for this batch and the given path tensors."""
+        P = _lib._ptr
+        d = self.d
+        return (self._desc_ref, P(d["k_cache"]), P(d["v_cache"]), P(d["block_table"]), P(d["prefix_len"]),
+                P(d["k_tree"]), P(d["v_tree"]), P(path), P(path_len), P(d["new_len"]), P(d["commit_status"]))
+
+    def commit(self, args, sh):
+        rc = self.lib.tree_commit_kv(*args, sh)
+        if rc:
+            _lib._check(rc, "tree_commit_kv")
 
     def build(self, sh):
         rc = self.lib.tree_build(*self.build_args, sh)
