@@ -25,6 +25,18 @@ from the stored input values (bf16 -> float64 and fp32 -> float64 are exact):
   the accept-up-to-first-mismatch-plus-one-target-token rule is the sequence
   case on the speculative-decoding explainer, technical mechanism section, and
   on the speculative-decoding operations guide's diagram, applied per branch.)
+* verify_stochastic: multi-step speculative sampling over the tree.  At the
+  current node the LLM distribution p (softmax of its logits) is compared with
+  each child c in node-id order: c's draft token x was drawn from q_c (softmax
+  of c's SSM logits) and is accepted with probability min(1, p(x)/q_c(x)),
+  i.e. iff u_c * q_c(x) < p(x) for c's uniform u_c in [0, 1); on rejection p
+  becomes the normalised residual max(0, p - q_c) and the next child is tried
+  against it.  An accepted child becomes the current node.  When every child
+  is rejected (or there is none) one token is drawn from p by inverse CDF with
+  the node's second uniform: the smallest y whose cumulative mass exceeds it.
+  (Explainer, tree-verification section: the acceptance probability and the
+  normalised residual equations, and the statement that the scheme samples
+  exactly from the LLM's distribution.)  The uniforms are inputs.
 * commit_kv: the keys and values of the accepted root path become ordinary
   prefix tokens: path node t goes to cache position L_b + t, so the cache
   again holds one linear sequence and the next step attends it like any
@@ -209,6 +221,91 @@ def verify_greedy(logits: np.ndarray, tokens: np.ndarray, parent: np.ndarray, dt
         plen[b] = len(p)
         bonus[b] = bo
     return am, path, plen, bonus
+
+
+def softmax64(row: np.ndarray, dtype: str) -> np.ndarray:
+    """softmax of one stored logits row, in float64 (-inf logits get probability 0)."""
+    x = to_f64(row, dtype)
+    m = x.max()
+    e = np.exp(x - m)
+    return e / e.sum()
+
+
+def mss_accepts(u: float, q: np.ndarray, p: np.ndarray, x: int):
+    """The acceptance test of draft token x: (accepted?, lhs, rhs) with accepted = lhs < rhs.
+
+    u < min(1, p(x)/q(x)) written without the division: u * q(x) < p(x), which
+    also covers q(x) == 0 (accepted iff p(x) > 0).
+    """
+    lhs, rhs = u * q[x], p[x]
+    return lhs < rhs, lhs, rhs
+
+
+def mss_residual(p: np.ndarray, q: np.ndarray):
+    """The distribution after a rejection: norm(max(0, p - q)); p itself if that is all zero.
+    Returns (new p, residual mass)."""
+    r = np.maximum(0.0, p - q)
+    tot = r.sum()
+    return (r / tot if tot > 0 else p), tot
+
+
+def mss_draw(p: np.ndarray, u: float):
+    """Inverse-CDF draw: the smallest y with cdf(y) > u (the last y with p(y) > 0 if
+    rounding leaves u >= cdf(V-1)).  Returns (y, cdf(y-1), cdf(y))."""
+    cdf = np.cumsum(p)
+    hit = np.nonzero(cdf > u)[0]
+    y = int(hit[0]) if len(hit) else int(np.nonzero(p > 0)[0][-1])
+    return y, (cdf[y - 1] if y > 0 else 0.0), cdf[y]
+
+
+def mss_walk(logits, ssm_logits, tokens, parent, u_acc, u_smp, dtype):
+    """Stochastic verification of one sequence's tree.
+
+    logits, ssm_logits [n][V] stored values; tokens, parent, u_acc, u_smp [n].
+    Returns (path, bonus, decisions): path = accepted node ids, root first;
+    bonus = the token drawn at the last node; decisions = every comparison the
+    walk made, as (lhs, rhs) pairs of a test lhs < rhs (a residual mass appears
+    as (0, mass)), for callers that need to know how close each decision was.
+    """
+    n = len(parent)
+    cur, path, decisions = 0, [0], []
+    while True:
+        p = softmax64(logits[cur], dtype)
+        moved = False
+        for c in [v for v in range(n) if parent[v] == cur]:     # children in node-id order
+            q = softmax64(ssm_logits[c], dtype)
+            ok, lhs, rhs = mss_accepts(float(u_acc[c]), q, p, int(tokens[c]))
+            decisions.append((lhs, rhs))
+            if ok:
+                cur = c
+                path.append(c)
+                moved = True
+                break
+            p, tot = mss_residual(p, q)
+            decisions.append((0.0, tot))
+        if not moved:
+            break
+    u = float(u_smp[cur])
+    bonus, lo, hi = mss_draw(p, u)
+    decisions.append((lo, u))                   # the draw: cdf(y-1) <= u < cdf(y)
+    decisions.append((u, hi))
+    return path, bonus, decisions
+
+
+def verify_stochastic(logits, ssm_logits, tokens, parent, u_acc, u_smp, dtype):
+    """Batched mss_walk: (path [B][n] -1 padded, path_len [B], bonus [B], decisions list per sequence)."""
+    B, n = tokens.shape
+    path = np.full((B, n), -1, np.int32)
+    plen = np.zeros(B, np.int32)
+    bonus = np.zeros(B, np.int32)
+    dec = []
+    for b in range(B):
+        p, bo, d = mss_walk(logits[b], ssm_logits[b], tokens[b], parent[b], u_acc[b], u_smp[b], dtype)
+        path[b, :len(p)] = p
+        plen[b] = len(p)
+        bonus[b] = bo
+        dec.append(d)
+    return path, plen, bonus, dec
 
 
 # ----------------------------------------------------------------------------- KV commit
