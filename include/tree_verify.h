@@ -5,8 +5,9 @@
  * single forward pass: every tree node u attends to the shared prefix KV cache
  * plus exactly the nodes on its own root-to-u path S_u, and greedy
  * verification then walks the tree from the root.  This library is that hot
- * path: three calls, all asynchronous on a caller-provided HIP stream, and a
- * fourth that commits the accepted path's keys and values to the cache.
+ * path: three calls, all asynchronous on a caller-provided HIP stream; a
+ * stochastic variant of verification; and a call that commits the accepted
+ * path's keys and values to the cache.
  *
  * Sources (the SpecInfer explainer at 0h-n0.github.io, "paper-2305-09781"):
  *   - token-tree structure section: a node per token, S_u = tokens on the path
@@ -169,6 +170,49 @@ int tree_verify_greedy(int B, int n, int V, int logits_dtype, const void* logits
                        const int32_t* tokens, const int32_t* parent,
                        int32_t* argmax_out, int32_t* path_out, int32_t* path_len,
                        int32_t* bonus, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * tree_verify_stochastic: stochastic verification by multi-step speculative
+ * sampling (the explainer's tree-verification section: a draft token x is
+ * accepted with probability min(1, P_LLM(x)/P_SSM(x)); after a rejection the
+ * LLM distribution becomes the normalised residual max(0, P_LLM - P_SSM); the
+ * emitted tokens then follow the LLM's own distribution).
+ *
+ * Walk, per sequence: cur = root, p = softmax(logits[cur]).  For each child c
+ * of cur in increasing node id, with x = tokens[c] and q = softmax(ssm[c]):
+ * accept iff u_accept[c] * q(x) < p(x); on acceptance cur = c and the walk
+ * restarts there with p = softmax(logits[c]); on rejection
+ * p = norm(max(0, p - q)) (p unchanged if that is all zero) and the next child
+ * is tried.  When no child is accepted, bonus = the smallest token y with
+ * sum_{t <= y} p(t) > u_sample[cur] (the last token with p > 0 if rounding
+ * leaves none), and the walk ends.  Softmax at temperature 1 (scale the logits
+ * beforehand for another temperature).
+ *
+ *   logits, ssm_logits [B][n][V] logits_dtype: the LLM's logits after each node
+ *                      and, for node c >= 1, the SSM logits its draft token was
+ *                      sampled from (row 0 of ssm_logits is not read)
+ *   tokens, parent [B][n] int32   as for tree_verify_greedy
+ *   u_accept, u_sample [B][n] float   uniforms in [0, 1) (entry 0 of u_accept
+ *                      is not read)
+ *   path_out [B][n], path_len [B], bonus [B] int32   out, as for the greedy call
+ *   status [B] int32 out (may be NULL): TV_OK, or TV_EINVAL for a sequence
+ *     whose parent array is not topological with root 0 or whose draft token
+ *     is outside [0, V); its path_len is then 0, path -1 and bonus -1.
+ *   workspace: tree_verify_stochastic_workspace_size(B, V) bytes (fp32
+ *     residual rows), 16-byte aligned; contents on entry do not matter.
+ * Every logits row needs a finite maximum; NaN is out of contract.
+ * Decisions are taken in fp32 (softmax with fp32 sums): a draw whose margin
+ * to a decision boundary is below that rounding may differ from an exact
+ * evaluation.  1 <= n <= TV_NMAX, 1 <= V <= TV_MSS_VMAX.
+ * ------------------------------------------------------------------------- */
+#define TV_MSS_VMAX (1 << 20)
+size_t tree_verify_stochastic_workspace_size(int B, int V);
+int tree_verify_stochastic(int B, int n, int V, int logits_dtype, const void* logits,
+                           const void* ssm_logits, const int32_t* tokens,
+                           const int32_t* parent, const float* u_accept,
+                           const float* u_sample, int32_t* path_out,
+                           int32_t* path_len, int32_t* bonus, int32_t* status,
+                           void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * tree_commit_kv: the accepted path's keys and values become prefix tokens.

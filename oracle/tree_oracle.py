@@ -293,19 +293,28 @@ def mss_walk(logits, ssm_logits, tokens, parent, u_acc, u_smp, dtype):
 
 
 def verify_stochastic(logits, ssm_logits, tokens, parent, u_acc, u_smp, dtype):
-    """Batched mss_walk: (path [B][n] -1 padded, path_len [B], bonus [B], decisions list per sequence)."""
+    """Batched mss_walk: (path [B][n] -1 padded, path_len [B], bonus [B], status [B], decisions
+    list per sequence).  A sequence whose parent array is not topological with root 0, or
+    with a draft token outside [0, V), gets status TV_EINVAL, path_len 0 and bonus -1."""
     B, n = tokens.shape
+    V = logits.shape[-1]
     path = np.full((B, n), -1, np.int32)
     plen = np.zeros(B, np.int32)
-    bonus = np.zeros(B, np.int32)
+    bonus = np.full(B, -1, np.int32)
+    status = np.full(B, TV_OK, np.int32)
     dec = []
     for b in range(B):
+        par, tok = parent[b], tokens[b]
+        if par[0] != -1 or any(not (0 <= par[v] < v) or not (0 <= tok[v] < V) for v in range(1, n)):
+            status[b] = TV_EINVAL                 # not a tree in topological order, or a token outside the vocab
+            dec.append([])
+            continue
         p, bo, d = mss_walk(logits[b], ssm_logits[b], tokens[b], parent[b], u_acc[b], u_smp[b], dtype)
         path[b, :len(p)] = p
         plen[b] = len(p)
         bonus[b] = bo
         dec.append(d)
-    return path, plen, bonus, dec
+    return path, plen, bonus, status, dec
 
 
 # ----------------------------------------------------------------------------- KV commit

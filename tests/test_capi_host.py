@@ -152,3 +152,23 @@ def test_commit_argument_errors(lib):
     assert call_commit(lib, desc(B=8), new_len=0x200000 + 28) == tv.TV_EINVAL     # overlaps it
     assert "overlap" in tv.last_error()
     assert lib.tree_commit_kv(ctypes.byref(desc(B=0)), *([None] * 10), None) == tv.TV_OK
+
+
+def test_stochastic_argument_errors(lib):
+    ws = lib.tree_verify_stochastic_workspace_size
+    assert ws(8, 32000) == 8 * 2 * 32768 * 4          # two fp32 rows per sequence, padded to 8192
+    assert ws(0, 5) == 0
+    assert ws(-1, 5) == SIZE_MAX and ws(2, 0) == SIZE_MAX and ws(2, tv.TV_MSS_VMAX + 1) == SIZE_MAX
+    p = [0x100000] * 10
+    call = lambda B, n, V, dt, ptrs=p, w=0x100000, wb=1 << 30: lib.tree_verify_stochastic(
+        B, n, V, dt, *ptrs, w, wb, None)
+    assert call(2, 7, 0, tv.TV_BF16) == tv.TV_EINVAL
+    assert call(2, 7, tv.TV_MSS_VMAX + 1, tv.TV_BF16) == tv.TV_EINVAL
+    assert call(2, 0, 10, tv.TV_BF16) == tv.TV_EINVAL
+    assert call(2, 300, 10, tv.TV_BF16) == tv.TV_EINVAL
+    assert call(2, 7, 10, 4) == tv.TV_EUNSUPPORTED
+    assert call(2, 7, 10, tv.TV_F32, ptrs=[None] * 10) == tv.TV_EINVAL
+    assert call(2, 7, 10, tv.TV_F32, w=None) == tv.TV_EWORKSPACE
+    assert call(2, 7, 10, tv.TV_F32, wb=ws(2, 10) - 1) == tv.TV_EWORKSPACE
+    assert call(2, 7, 10, tv.TV_F32, ptrs=[0x100004] + [0x100000] * 9) == tv.TV_EINVAL   # misaligned logits
+    assert call(0, 7, 10, tv.TV_F32, ptrs=[None] * 10, w=None, wb=0) == tv.TV_OK

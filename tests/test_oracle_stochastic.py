@@ -169,10 +169,10 @@ def test_one_hot_limit_is_greedy_verification():
                 ssm[b, v, :] = -1e4
                 ssm[b, v, tokens[b, v]] = 0.0
     rng = np.random.default_rng(0)
-    path, plen, bonus, _ = oracle.verify_stochastic(logits, ssm, tokens, w["parent"], rng.random((B, n)),
+    path, plen, bonus, status, _ = oracle.verify_stochastic(logits, ssm, tokens, w["parent"], rng.random((B, n)),
                                                     rng.random((B, n)), "f32")
     g_am, g_path, g_plen, g_bonus = oracle.verify_greedy(logits, tokens, w["parent"], "f32")
     np.testing.assert_array_equal(plen, g_plen)
     np.testing.assert_array_equal(path, g_path)
     np.testing.assert_array_equal(bonus, g_bonus)
-    assert (plen > 1).any()
+    assert (plen > 1).any() and (status == 0).all()

@@ -7,5 +7,6 @@ the C ABI in include/tree_verify.h.  The functions here are the
 ctypes binding of that library; torch provides device memory and streams.
 """
 from ._lib import (TV_BF16, TV_EHIP, TV_EINVAL, TV_ETOPOLOGY, TV_EUNSUPPORTED, TV_EWORKSPACE,  # noqa: F401
-                   TV_F32, TV_NMAX, TV_OK, TV_PAGE, TreeVerifyError, attn_desc, last_error, load,
-                   tree_attention, tree_build, tree_commit_kv, tree_verify_greedy, validate_host, workspace_size)
+                   TV_F32, TV_MSS_VMAX, TV_NMAX, TV_OK, TV_PAGE, TreeVerifyError, attn_desc, last_error, load,
+                   tree_attention, tree_build, tree_commit_kv, tree_verify_greedy,
+                   tree_verify_stochastic, stochastic_workspace_size, validate_host, workspace_size)

@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_PKG, "libtreeverify.so")
 
 TV_OK, TV_EINVAL, TV_ETOPOLOGY, TV_EUNSUPPORTED, TV_EWORKSPACE, TV_EHIP = range(6)
 TV_F32, TV_BF16 = 0, 1
-TV_NMAX, TV_PAGE = 256, 16
+TV_NMAX, TV_PAGE, TV_MSS_VMAX = 256, 16, 1 << 20
 
 _c_int, _c_float, _vp, _size_t = ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
 
@@ -47,6 +47,8 @@ SIGNATURES = {
     "tree_attention": (_c_int, [ctypes.POINTER(AttnDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                 _vp, _vp, _size_t, _vp]),
     "tree_verify_greedy": (_c_int, [_c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "tree_verify_stochastic_workspace_size": (_size_t, [_c_int, _c_int]),
+    "tree_verify_stochastic": (_c_int, [_c_int, _c_int, _c_int, _c_int] + [_vp] * 11 + [_size_t, _vp]),
     "tree_commit_kv": (_c_int, [ctypes.POINTER(AttnDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                 _vp]),
 }
@@ -175,6 +177,32 @@ def tree_verify_greedy(logits, tokens, parent, *, argmax=None, path=None, path_l
                                    _ptr(argmax), _ptr(path), _ptr(path_len), _ptr(bonus), _stream(stream))
     _check(rc, "tree_verify_greedy")
     return argmax, path, path_len, bonus
+
+
+def stochastic_workspace_size(B: int, V: int) -> int:
+    return int(load().tree_verify_stochastic_workspace_size(B, V))
+
+
+def tree_verify_stochastic(logits, ssm_logits, tokens, parent, u_accept, u_sample, *, path=None, path_len=None,
+                           bonus=None, status=None, workspace=None, stream=None):
+    """Stochastic (multi-step speculative sampling) verification.  logits, ssm_logits
+    [B][n][V]; tokens, parent [B][n] int32; u_accept, u_sample [B][n] float32 uniforms.
+    Returns (path [B][n], path_len [B], bonus [B], status [B]) int32."""
+    B, n, V = logits.shape
+    dev = logits.device
+    path = torch.empty((B, n), dtype=torch.int32, device=dev) if path is None else path
+    path_len = torch.empty((B,), dtype=torch.int32, device=dev) if path_len is None else path_len
+    bonus = torch.empty((B,), dtype=torch.int32, device=dev) if bonus is None else bonus
+    status = torch.empty((B,), dtype=torch.int32, device=dev) if status is None else status
+    need = stochastic_workspace_size(B, V)
+    if workspace is None and need != (1 << 64) - 1:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = load().tree_verify_stochastic(B, n, V, _dtype_code(logits), _ptr(logits), _ptr(ssm_logits), _ptr(tokens),
+                                       _ptr(parent), _ptr(u_accept), _ptr(u_sample), _ptr(path), _ptr(path_len),
+                                       _ptr(bonus), _ptr(status), _ptr(workspace), wbytes, _stream(stream))
+    _check(rc, "tree_verify_stochastic")
+    return path, path_len, bonus, status
 
 
 def tree_commit_kv(k_cache, v_cache, prefix_len, k_tree, v_tree, path, path_len, *, block_table=None,

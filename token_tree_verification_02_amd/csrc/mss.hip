@@ -1,0 +1,654 @@
+// Stochastic tree verification: multi-step speculative sampling over the tree.
+//
+// SpecInfer explainer, tree-verification section: a child's draft token x is
+// accepted with probability min(1, P_LLM(x) / P_SSM(x)); after a rejection the
+// LLM distribution is replaced by the normalised residual max(0, P_LLM - P_SSM),
+// and the scheme then samples exactly from the LLM's distribution.  At the
+// current node the children are tried in node-id order, each against the
+// residual left by its rejected elder siblings; an accepted child becomes the
+// current node; when all are rejected (or there are none) one token is drawn
+// from the current distribution by inverse CDF.  The uniforms are inputs.
+//
+// The walk is sequential per sequence and touches only the rows of the nodes it
+// visits, so it runs as one 512-thread workgroup per sequence that streams
+// just those vocab rows (the rows of a node already visited stay in L2/MALL):
+//   node entry     one pass: online (max, sum) of the node's LLM logits and of
+//                  its first child's SSM logits
+//   child test     scalar loads of the two logits at the draft token
+//   rejection      one pass writing the residual r = max(0, p - q) to an fp32
+//                  workspace row (and its sum), fused with the next child's
+//                  SSM statistics; the next child's p(x) is caught in LDS by the
+//                  thread that owns x
+//   final draw     one pass of per-segment sums (512 elements per segment),
+//                  a prefix over segments in fp64 by one wave, and a scan
+//                  inside the chosen segment
+// Element e of a row belongs to thread (e % 4096) / 8 in every pass, so a thread
+// only ever reads back residual values it wrote itself.
+#include <limits.h>
+
+#include "tv_internal.h"
+
+namespace tv {
+namespace {
+
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / 64;
+constexpr int kEPT = 8;                      // elements per thread per chunk
+constexpr int kChunk = kThreads * kEPT;      // 4096
+constexpr int kSeg = 64 * kEPT;              // 512 elements: one wave's share of a chunk
+constexpr int kMaxSeg = TV_MSS_VMAX / kSeg;  // 2048
+// A pass over a row visits chunks in groups of kU whose loads are all issued
+// before any of them is used, so a workgroup keeps kU * 8 KB of each
+// row in flight instead of waiting out one memory latency per chunk.
+template <bool BF16>
+constexpr int kGroup = BF16 ? 8 : 4;
+
+template <bool BF16>
+__device__ __forceinline__ void load8(const void* row, int e0, int V, bool vec, float (&v)[kEPT]) {
+  if (BF16) {
+    const uint16_t* r = (const uint16_t*)row;
+    if (vec && e0 + kEPT <= V) {
+      const uint4 w = *(const uint4*)(r + e0);
+      v[0] = bf16lo(w.x), v[1] = bf16hi(w.x), v[2] = bf16lo(w.y), v[3] = bf16hi(w.y);
+      v[4] = bf16lo(w.z), v[5] = bf16hi(w.z), v[6] = bf16lo(w.w), v[7] = bf16hi(w.w);
+    } else {
+#pragma unroll
+      for (int j = 0; j < kEPT; ++j) v[j] = e0 + j < V ? bf16_to_f32(r[e0 + j]) : -INFINITY;
+    }
+  } else {
+    const float* r = (const float*)row;
+    if (vec && e0 + kEPT <= V) {
+      const float4 a = *(const float4*)(r + e0);
+      const float4 b = *(const float4*)(r + e0 + 4);
+      v[0] = a.x, v[1] = a.y, v[2] = a.z, v[3] = a.w, v[4] = b.x, v[5] = b.y, v[6] = b.z, v[7] = b.w;
+    } else {
+#pragma unroll
+      for (int j = 0; j < kEPT; ++j) v[j] = e0 + j < V ? r[e0 + j] : -INFINITY;
+    }
+  }
+}
+
+// Eight elements known to lie inside the row, loaded as raw 16-byte words and
+// unpacked only when used, so a group of chunks in flight costs 4 VGPRs per
+// chunk for bf16 rows (8 for fp32).
+template <bool BF16>
+struct Raw {
+  uint4 w[BF16 ? 1 : 2];
+  __device__ __forceinline__ void load(const void* row, int e0) {
+    const uint4* p = (const uint4*)((const char*)row + (size_t)e0 * (BF16 ? 2 : 4));
+    w[0] = p[0];
+    if (!BF16) w[1] = p[1];
+  }
+  __device__ __forceinline__ void unpack(float (&v)[kEPT]) const {
+    if (BF16) {
+      v[0] = bf16lo(w[0].x), v[1] = bf16hi(w[0].x), v[2] = bf16lo(w[0].y), v[3] = bf16hi(w[0].y);
+      v[4] = bf16lo(w[0].z), v[5] = bf16hi(w[0].z), v[6] = bf16lo(w[0].w), v[7] = bf16hi(w[0].w);
+    } else {
+      v[0] = __uint_as_float(w[0].x), v[1] = __uint_as_float(w[0].y), v[2] = __uint_as_float(w[0].z);
+      v[3] = __uint_as_float(w[0].w), v[4] = __uint_as_float(w[1].x), v[5] = __uint_as_float(w[1].y);
+      v[6] = __uint_as_float(w[1].z), v[7] = __uint_as_float(w[1].w);
+    }
+  }
+};
+
+template <bool BF16>
+__device__ __forceinline__ float load1(const void* row, int x) {
+  return BF16 ? bf16_to_f32(((const uint16_t*)row)[x]) : ((const float*)row)[x];
+}
+
+// exp(v - r / log2(e)) as exp2(v * log2(e) - r): one FMA and the hardware exp2;
+// the FMA rounds the argument once, so a value carries about 1e-7 relative error.
+__device__ __forceinline__ float ex(float v, float nr) { return __builtin_amdgcn_exp2f(fmaf(v, kLog2e, nr)); }
+
+__device__ __forceinline__ float max8(const float (&v)[kEPT]) {
+  float m = v[0];
+#pragma unroll
+  for (int j = 1; j < kEPT; ++j) m = fmaxf(m, v[j]);
+  return m;
+}
+
+// Softmax statistics of a row, gathered in one pass: the terms exp2(v*log2(e) - R)
+// summed in fp64, with R a whole number at least max(v)*log2(e), so no term
+// exceeds 1.  R only ever moves by whole numbers and the sum follows it by
+// ldexp, which is exact: the online pass adds no rounding beyond the terms' own,
+// and p(v) = exp2(v*log2(e) - R) / S.
+struct Stat {
+  float R = -INFINITY;
+  double S = 0.0;
+};
+
+__device__ __forceinline__ double shift(double s, float from, float to) {  // s * 2^(from - to), to >= from
+  return ldexp(s, (int)fmaxf(from - to, -2000.f));
+}
+
+__device__ __forceinline__ void stat_add8(Stat& st, const float (&v)[kEPT]) {
+  const float cm = max8(v);
+  if (cm == -INFINITY) return;
+  const float r = ceilf(cm * kLog2e);
+  if (r > st.R) {
+    st.S = st.R == -INFINITY ? 0.0 : shift(st.S, st.R, r);
+    st.R = r;
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < kEPT; ++j) s += ex(v[j], -st.R);
+  st.S += (double)s;
+}
+
+__device__ __forceinline__ void stat_merge(Stat& a, float R, double S) {
+  if (R == -INFINITY) return;
+  if (a.R == -INFINITY) {
+    a.R = R, a.S = S;
+    return;
+  }
+  const float M = fmaxf(a.R, R);
+  a.S = shift(a.S, a.R, M) + shift(S, R, M);
+  a.R = M;
+}
+
+struct Shared {
+  int par[TV_NMAX];
+  int tok[TV_NMAX];
+  float uacc[TV_NMAX];
+  int child[TV_NMAX];
+  int path[TV_NMAX];
+  unsigned long long ball[4];
+  float rR[2][2][kWaves];
+  double rS[2][3][kWaves];
+  float cap_prev[2], cap_r[2];  // by pass parity: a pass never overwrites what the last one caught
+  double segd[kMaxSeg];
+  int result;
+};
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+__device__ __forceinline__ double wave_sum(double x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+// a wave's statistics: the largest reference, every lane's sum moved onto it
+// (exactly), then one plain fp64 sum
+__device__ __forceinline__ Stat wave_stat(Stat a) {
+  const float R = wave_max(a.R);
+  const double s = a.R == -INFINITY ? 0.0 : shift(a.S, a.R, R);
+  return Stat{R, wave_sum(s)};
+}
+
+// Workgroup-wide merge of two row statistics and one plain fp64 sum per thread.
+// Every thread ends with the same values, merged in the same order from LDS.
+// One barrier; alternating LDS slots so back-to-back calls never overwrite
+// values another wave is still reading.
+__device__ __forceinline__ void block_reduce(Shared& S, int& slot, Stat& a, Stat& b, double& t) {
+  const Stat wa = wave_stat(a), wb = wave_stat(b);
+  const double wt = wave_sum(t);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    S.rR[slot][0][w] = wa.R, S.rS[slot][0][w] = wa.S;
+    S.rR[slot][1][w] = wb.R, S.rS[slot][1][w] = wb.S;
+    S.rS[slot][2][w] = wt;
+  }
+  __syncthreads();
+  a = Stat{}, b = Stat{}, t = 0.0;
+  for (int k = 0; k < kWaves; ++k) {
+    stat_merge(a, S.rR[slot][0][k], S.rS[slot][0][k]);
+    stat_merge(b, S.rR[slot][1][k], S.rS[slot][1][k]);
+    t += S.rS[slot][2][k];
+  }
+  slot ^= 1;
+}
+
+// One chunk of a residual pass: p (from raw logits via max/normaliser, or from
+// the previous unnormalised residual via its sum), minus q from its logits;
+// writes r = max(0, p - q) to the output row, catches p and r at the next
+// child's token, returns the chunk's sum of r.
+struct Resid {
+  bool from_logits;
+  float nm;   // -R of the LLM row's statistics
+  float sp_hi, sp_lo;  // scale of p (1/S or 1/T) as a two-float sum
+  float nmq;  // -R of the SSM row's
+  float sq_hi, sq_lo;  // 1/S of the SSM row likewise
+  float* rout;
+  int xn;
+  float* cap_prev;
+  float* cap_r;
+  __device__ __forceinline__ float chunk(int e0, float (&pv)[kEPT], const float (&qv)[kEPT]) const {
+#pragma unroll
+    for (int j = 0; j < kEPT; ++j) {
+      const float e = from_logits ? ex(pv[j], nm) : pv[j];
+      pv[j] = fmaf(e, sp_hi, e * sp_lo);
+    }
+    float r[kEPT];
+    float sm = 0.f;
+#pragma unroll
+    for (int j = 0; j < kEPT; ++j) {
+      const float e = ex(qv[j], nmq);
+      r[j] = fmaxf(0.f, pv[j] - fmaf(e, sq_hi, e * sq_lo));
+      sm += r[j];
+    }
+    *(float4*)(rout + e0) = make_float4(r[0], r[1], r[2], r[3]);
+    *(float4*)(rout + e0 + 4) = make_float4(r[4], r[5], r[6], r[7]);
+    if ((unsigned)(xn - e0) < (unsigned)kEPT) {
+      const int j = xn - e0;
+      float pj = pv[0], rj = r[0];
+#pragma unroll
+      for (int jj = 1; jj < kEPT; ++jj) {
+        pj = jj == j ? pv[jj] : pj;
+        rj = jj == j ? r[jj] : rj;
+      }
+      *cap_prev = pj;
+      *cap_r = rj;
+    }
+    return sm;
+  }
+};
+
+// a double as hi + lo floats (the product e * hi + e * lo then rounds once per
+// element instead of carrying one shared rounding of the scale)
+__device__ __forceinline__ void split2(double d, float& hi, float& lo) {
+  hi = (float)d;
+  lo = (float)(d - (double)hi);
+}
+
+// fp64 sum of one wave's 512 values of a chunk into its segment slot
+__device__ __forceinline__ void seg_store(Shared& S, int ch, const float (&v)[kEPT]) {
+  double sd = 0.0;
+#pragma unroll
+  for (int j = 0; j < kEPT; ++j) sd += (double)v[j];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) sd += __shfl_xor(sd, o);
+  if ((threadIdx.x & 63) == 0) S.segd[ch * kWaves + (threadIdx.x >> 6)] = sd;
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void mss_kernel(int n, int V, int vec, const void* __restrict__ logits,
+                                                       const void* __restrict__ ssm,
+                                                       const int32_t* __restrict__ tokens,
+                                                       const int32_t* __restrict__ parent,
+                                                       const float* __restrict__ u_acc,
+                                                       const float* __restrict__ u_smp, float* __restrict__ ws,
+                                                       int Vpad, int32_t* __restrict__ path_out,
+                                                       int32_t* __restrict__ plen_out, int32_t* __restrict__ bonus,
+                                                       int32_t* __restrict__ status) {
+  __shared__ Shared S;
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const size_t es = BF16 ? 2 : 4;
+  const char* lbase = (const char*)logits + (size_t)b * n * V * es;
+  const char* sbase = (const char*)ssm + (size_t)b * n * V * es;
+  float* const rbase = ws + (size_t)b * 2 * Vpad;  // two residual rows: rbase + ib * Vpad
+  const int nch = (V + kChunk - 1) / kChunk;
+  const int nfull = vec ? V / kChunk : 0;  // chunks wholly inside the row, read with vector loads
+  constexpr int kU = kGroup<BF16>;
+
+  // ---- load and check the tree: parents before children, tokens inside the vocabulary
+  int bad = 0;
+  if (tid < n) {
+    const int p = parent[(size_t)b * n + tid];
+    const int t = tokens[(size_t)b * n + tid];
+    S.par[tid] = p;
+    S.tok[tid] = t;
+    S.uacc[tid] = u_acc[(size_t)b * n + tid];
+    bad = tid == 0 ? p != -1 : (p < 0 || p >= tid || t < 0 || t >= V);
+  }
+  bad = __syncthreads_or(bad);
+  int32_t* pr = path_out + (size_t)b * n;
+  if (bad) {
+    if (tid < n) pr[tid] = -1;
+    if (tid == 0) {
+      plen_out[b] = 0;
+      bonus[b] = -1;
+      if (status) status[b] = TV_EINVAL;
+    }
+    return;
+  }
+
+  int slot = 0;
+  int cur = 0, len = 1;
+  if (tid == 0) S.path[0] = 0;
+  for (;;) {
+    // ---- children of cur in node-id order (ballot over node ids)
+    const bool isc = tid < n && tid > cur && S.par[tid] == cur;
+    const unsigned long long bl = __ballot(isc);
+    if (tid < 256 && lane == 0) S.ball[wv] = bl;
+    __syncthreads();
+    int k = 0;
+    for (int w = 0; w < 4; ++w) {
+      unsigned long long msk = S.ball[w];
+      while (msk) {
+        const int v = w * 64 + __builtin_ctzll(msk);
+        msk &= msk - 1;
+        if (tid == 0) S.child[k] = v;
+        ++k;
+      }
+    }
+    __syncthreads();  // S.child visible
+    const char* lrow = lbase + (size_t)cur * V * es;
+    const int c1 = k > 0 ? S.child[0] : -1;
+    const char* srow = c1 >= 0 ? sbase + (size_t)c1 * V * es : nullptr;
+
+    // ---- node entry: one pass of statistics of the LLM row and the first child's SSM row
+    Stat sl, sq;
+    {
+      int c = 0;
+      for (; c + kU <= nfull; c += kU) {
+        Raw<BF16> a[kU], q[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) a[u].load(lrow, (c + u) * kChunk + tid * kEPT);
+        if (srow) {
+#pragma unroll
+          for (int u = 0; u < kU; ++u) q[u].load(srow, (c + u) * kChunk + tid * kEPT);
+#pragma unroll
+          for (int u = 0; u < kU; ++u) {
+            float v[kEPT];
+            q[u].unpack(v);
+            stat_add8(sq, v);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          float v[kEPT];
+          a[u].unpack(v);
+          stat_add8(sl, v);
+        }
+      }
+      for (; c < nch; ++c) {
+        const int e0 = c * kChunk + tid * kEPT;
+        float v[kEPT];
+        load8<BF16>(lrow, e0, V, vec, v);
+        stat_add8(sl, v);
+        if (srow) {
+          load8<BF16>(srow, e0, V, vec, v);
+          stat_add8(sq, v);
+        }
+      }
+      double unused = 0.0;
+      block_reduce(S, slot, sl, sq, unused);
+    }
+
+    // ---- children in order
+    bool from_logits = true;  // the current distribution is softmax of lrow (else rb[ib] / T)
+    int ib = 0;
+    double T = 1.0;
+    double pnext = 0.0;  // p at the next child's token, when not from logits
+    int accepted = -1;
+    for (int i = 0; i < k; ++i) {
+      const int c = S.child[i];
+      const int x = S.tok[c];
+      const char* crow = sbase + (size_t)c * V * es;
+      const double px = from_logits ? (double)ex(load1<BF16>(lrow, x), -sl.R) / sl.S : pnext;
+      const double qx = (double)ex(load1<BF16>(crow, x), -sq.R) / sq.S;
+      if ((double)S.uacc[c] * qx < px) {
+        accepted = c;
+        break;
+      }
+      // rejected: residual r = max(0, p - q_c) into the other workspace row, its
+      // sum, and the next child's SSM maximum
+      const int cn = i + 1 < k ? S.child[i + 1] : -1;
+      const char* nrow = cn >= 0 ? sbase + (size_t)cn * V * es : nullptr;
+      const int xn = cn >= 0 ? S.tok[cn] : -1;
+      const float* rin = rbase + (size_t)ib * Vpad;
+      float* rout = rbase + (size_t)(ib ^ 1) * Vpad;
+      Resid R{from_logits, -sl.R, 0.f, 0.f, -sq.R, 0.f, 0.f, rout, xn, S.cap_prev + (i & 1), S.cap_r + (i & 1)};
+      split2(from_logits ? 1.0 / sl.S : 1.0 / T, R.sp_hi, R.sp_lo);
+      split2(1.0 / sq.S, R.sq_hi, R.sq_lo);
+      double tsum = 0.0;
+      Stat sn, unused;  // the next child's SSM row
+      {
+        int ch = 0;
+        constexpr int kR = BF16 ? 4 : 2;  // three rows in flight here, so a smaller group
+        for (; ch + kR <= nfull; ch += kR) {
+          Raw<false> pq[kR];  // the current distribution: raw logits (bf16 uses half) or residual
+          Raw<BF16> qq[kR], nq[kR];
+#pragma unroll
+          for (int u = 0; u < kR; ++u) {
+            const int e0 = (ch + u) * kChunk + tid * kEPT;
+            if (from_logits) {
+              if (BF16)
+                pq[u].w[0] = *(const uint4*)((const uint16_t*)lrow + e0);
+              else
+                pq[u].load(lrow, e0);
+            } else {
+              pq[u].load(rin, e0);
+            }
+          }
+#pragma unroll
+          for (int u = 0; u < kR; ++u) qq[u].load(crow, (ch + u) * kChunk + tid * kEPT);
+          if (nrow) {
+#pragma unroll
+            for (int u = 0; u < kR; ++u) nq[u].load(nrow, (ch + u) * kChunk + tid * kEPT);
+#pragma unroll
+            for (int u = 0; u < kR; ++u) {
+              float v[kEPT];
+              nq[u].unpack(v);
+              stat_add8(sn, v);
+            }
+          }
+#pragma unroll
+          for (int u = 0; u < kR; ++u) {
+            float pv[kEPT], qv[kEPT];
+            if (from_logits && BF16) {
+              Raw<true> t;
+              t.w[0] = pq[u].w[0];
+              t.unpack(pv);
+            } else {
+              pq[u].unpack(pv);
+            }
+            qq[u].unpack(qv);
+            tsum += (double)R.chunk((ch + u) * kChunk + tid * kEPT, pv, qv);
+          }
+        }
+        for (; ch < nch; ++ch) {
+          const int e0 = ch * kChunk + tid * kEPT;
+          float pv[kEPT], qv[kEPT];
+          if (from_logits) {
+            load8<BF16>(lrow, e0, V, vec, pv);
+          } else {
+            Raw<false> r1;
+            r1.load(rin, e0);
+            r1.unpack(pv);
+          }
+          load8<BF16>(crow, e0, V, vec, qv);
+          tsum += (double)R.chunk(e0, pv, qv);
+          if (nrow) {
+            load8<BF16>(nrow, e0, V, vec, qv);
+            stat_add8(sn, qv);
+          }
+        }
+      }
+      block_reduce(S, slot, sn, unused, tsum);
+      if (tsum > 0.0) {
+        pnext = cn >= 0 ? (double)S.cap_r[i & 1] / tsum : 0.0;
+        from_logits = false;
+        ib ^= 1;
+        T = tsum;
+      } else {
+        pnext = cn >= 0 ? (double)S.cap_prev[i & 1] : 0.0;
+      }
+      sq = sn;
+    }
+    if (accepted >= 0) {
+      if (tid == 0) S.path[len] = accepted;
+      ++len;
+      cur = accepted;
+      continue;
+    }
+
+    // ---- final draw from the current distribution (unnormalised values v)
+    const float* rin = rbase + (size_t)ib * Vpad;
+    {
+      int ch = 0;
+      for (; ch + kU <= nfull; ch += kU) {
+        Raw<BF16> lq[kU];
+        Raw<false> rq[kU];
+        if (from_logits) {
+#pragma unroll
+          for (int u = 0; u < kU; ++u) lq[u].load(lrow, (ch + u) * kChunk + tid * kEPT);
+        } else {
+#pragma unroll
+          for (int u = 0; u < kU; ++u) rq[u].load(rin, (ch + u) * kChunk + tid * kEPT);
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          float v[kEPT];
+          if (from_logits) {
+            lq[u].unpack(v);
+#pragma unroll
+            for (int j = 0; j < kEPT; ++j) v[j] = ex(v[j], -sl.R);
+          } else {
+            rq[u].unpack(v);
+          }
+          seg_store(S, ch + u, v);
+        }
+      }
+      for (; ch < nch; ++ch) {
+        const int e0 = ch * kChunk + tid * kEPT;
+        float v[kEPT];
+        if (from_logits) {
+          load8<BF16>(lrow, e0, V, vec, v);
+#pragma unroll
+          for (int j = 0; j < kEPT; ++j) v[j] = ex(v[j], -sl.R);
+        } else {
+          Raw<false> r1;
+          r1.load(rin, e0);
+          r1.unpack(v);
+        }
+        seg_store(S, ch, v);
+      }
+    }
+    __syncthreads();
+    if (wv == 0) {
+      const int nseg = nch * kWaves;
+      const float u = u_smp[(size_t)b * n + cur];
+      // total mass, then the first segment whose running sum passes u * total
+      double tot = 0.0;
+      for (int s0 = 0; s0 < nseg; s0 += 64) {
+        double x = s0 + lane < nseg ? S.segd[s0 + lane] : 0.0;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+        tot += x;
+      }
+      const double target = (double)u * tot;
+      double run = 0.0;
+      int seg = -1;
+      for (int s0 = 0; s0 < nseg && seg < 0; s0 += 64) {
+        const double x = s0 + lane < nseg ? S.segd[s0 + lane] : 0.0;
+        double inc = x;  // inclusive prefix over the lanes
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const double y = __shfl_up(inc, o);
+          if (lane >= o) inc += y;
+        }
+        const unsigned long long hit = __ballot(run + inc > target);
+        if (hit) {
+          const int l = __builtin_ctzll(hit);
+          seg = s0 + l;
+          run += __shfl(inc - x, l);  // mass before the chosen segment
+        } else {
+          run += __shfl(inc, 63);
+        }
+      }
+      int y = -1;
+      if (seg >= 0) {
+        // the segment's 512 elements: lane l holds elements seg_base + l*8 .. +8
+        const int ch = seg / kWaves, w = seg % kWaves;
+        const int e0 = ch * kChunk + (w * 64 + lane) * kEPT;
+        float v[kEPT];
+        if (from_logits) {
+          load8<BF16>(lrow, e0, V, vec, v);
+#pragma unroll
+          for (int j = 0; j < kEPT; ++j) v[j] = ex(v[j], -sl.R);
+        } else {
+#pragma unroll
+          for (int j = 0; j < kEPT; ++j) v[j] = rin[e0 + j];
+        }
+        double ls = 0.0;
+#pragma unroll
+        for (int j = 0; j < kEPT; ++j) ls += (double)v[j];
+        double inc = ls;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const double t = __shfl_up(inc, o);
+          if (lane >= o) inc += t;
+        }
+        double acc = run + (inc - ls);
+        int mine = -1, lastpos = -1;
+#pragma unroll
+        for (int j = 0; j < kEPT; ++j) {
+          acc += (double)v[j];
+          if (mine < 0 && acc > target) mine = e0 + j;
+          if (v[j] > 0.f && e0 + j < V) lastpos = e0 + j;
+        }
+        const unsigned long long hit = __ballot(mine >= 0);
+        if (hit) {
+          y = __shfl(mine, __builtin_ctzll(hit));
+        } else {  // the segment sum passed the target but the element sums (another order) did not
+#pragma unroll
+          for (int o = 32; o > 0; o >>= 1) lastpos = max(lastpos, __shfl_xor(lastpos, o));
+          y = lastpos;
+        }
+      }
+      if (y < 0) {
+        // rounding left u * total at or past the end: the last element with mass
+        int last = -1;
+        for (int ch = nch - 1; ch >= 0 && last < 0; --ch) {
+          for (int part = 0; part < kWaves && last < 0; ++part) {
+            const int e0 = ch * kChunk + ((kWaves - 1 - part) * 64 + lane) * kEPT;
+            float v[kEPT];
+            if (from_logits) {
+              load8<BF16>(lrow, e0, V, vec, v);
+#pragma unroll
+              for (int j = 0; j < kEPT; ++j) v[j] = ex(v[j], -sl.R);
+            } else {
+#pragma unroll
+              for (int j = 0; j < kEPT; ++j) v[j] = rin[e0 + j];
+            }
+            int mine = -1;
+#pragma unroll
+            for (int j = 0; j < kEPT; ++j) mine = v[j] > 0.f && e0 + j < V ? e0 + j : mine;
+            int best = mine;
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) best = max(best, __shfl_xor(best, o));
+            last = best;
+          }
+        }
+        y = last;
+      }
+      if (lane == 0) S.result = y;
+    }
+    __syncthreads();
+    if (tid < n) pr[tid] = tid < len ? S.path[tid] : -1;
+    if (tid == 0) {
+      plen_out[b] = len;
+      bonus[b] = S.result;
+      if (status) status[b] = TV_OK;
+    }
+    return;
+  }
+}
+
+}  // namespace
+
+size_t mss_workspace_bytes(int B, int V) {
+  const size_t vpad = (size_t)(V + kChunk - 1) / kChunk * kChunk;
+  return (size_t)B * 2 * vpad * sizeof(float);
+}
+
+hipError_t launch_mss(int B, int n, int V, int bf16, const void* logits, const void* ssm, const int32_t* tokens,
+                      const int32_t* parent, const float* u_acc, const float* u_smp, float* ws, int32_t* path,
+                      int32_t* plen, int32_t* bonus, int32_t* status, hipStream_t s) {
+  if (B == 0) return hipSuccess;
+  const int vpad = (V + kChunk - 1) / kChunk * kChunk;
+  const int vec = ((size_t)V * (bf16 ? 2 : 4)) % 16 == 0;
+  if (bf16)
+    hipLaunchKernelGGL(mss_kernel<true>, dim3(B), dim3(kThreads), 0, s, n, V, vec, logits, ssm, tokens, parent,
+                       u_acc, u_smp, ws, vpad, path, plen, bonus, status);
+  else
+    hipLaunchKernelGGL(mss_kernel<false>, dim3(B), dim3(kThreads), 0, s, n, V, vec, logits, ssm, tokens, parent,
+                       u_acc, u_smp, ws, vpad, path, plen, bonus, status);
+  return hipGetLastError();
+}
+
+}  // namespace tv

@@ -36,6 +36,7 @@ F32_NAN = np.float32(np.nan)
 
 # stream ids for the counter-keyed generator
 _S_TREE, _S_LEN, _S_PERM, _S_Q, _S_K, _S_V, _S_KT, _S_VT, _S_LOGIT, _S_TOK, _S_PLANT, _S_VAR = range(12)
+_S_SSM, _S_UNIF = range(12, 14)
 _CHUNK = 1 << 22
 _THREADS = max(1, min(16, len(os.sched_getaffinity(0))))
 
@@ -401,6 +402,51 @@ def make(cfg: Config, seed: int | None = None, *, variant: str = "plain", plant:
         if plant:
             plan = _plant(cfg, parent, tokens, logits, _rng(seed, _S_PLANT))
         out.update(logits=logits, tokens=tokens, planted=plan)
+    return out
+
+
+def make_stochastic(cfg: Config, seed: int | None = None, *, ssm_noise: float = 1.0, w: dict | None = None) -> dict:
+    """Inputs of stochastic verification for a workload with a vocabulary.
+
+    LLM logits ~ N(0, logit_sigma) per node (as for greedy verification).  The SSM
+    logits of node c are its parent's LLM logits plus N(0, ssm_noise) noise, so
+    the draft distributions resemble the LLM's and acceptance is common but not
+    certain.  Each draft token is drawn from its SSM row's softmax by inverse CDF
+    with a uniform of its own, as a sampling draft model would.  Uniforms given
+    to the verifier are multiples of 2^-24 in [0, 1), exact in float32 and
+    float64.  Sequences are generated in parallel, each from its own stream.
+    Returns the workload dict with ssm_logits, tokens, u_accept, u_sample added.
+    """
+    from concurrent.futures import ThreadPoolExecutor
+
+    seed = cfg.index if seed is None else seed
+    w = make(cfg, seed, plant=False) if w is None else w
+    B, n, V, dt = cfg.B, cfg.n, cfg.vocab, cfg.dtype
+    edt = np.uint16 if dt == "bf16" else np.float32
+    ssm_st = np.empty((B, n, V), edt)
+    tokens = np.zeros((B, n), np.int32)
+
+    def one(b):
+        rng = _rng(seed, _S_SSM, b)
+        llm = bf16_bits_to_f32(w["logits"][b]) if dt == "bf16" else w["logits"][b]
+        par = np.maximum(w["parent"][b], 0)
+        row = llm[par] + rng.standard_normal((n, V), dtype=np.float32) * np.float32(ssm_noise)
+        row[0] = 0.0                                 # the root has no draft distribution
+        ssm_st[b] = _store(row, dt)
+        rf = bf16_bits_to_f32(ssm_st[b]) if dt == "bf16" else ssm_st[b]
+        e = np.exp((rf - rf.max(axis=1, keepdims=True)).astype(np.float64))
+        cdf = np.cumsum(e, axis=1)
+        u = rng.random(n) * cdf[:, -1]
+        tokens[b] = [min(int(np.searchsorted(cdf[v], u[v], side="right")), V - 1) for v in range(n)]
+
+    with ThreadPoolExecutor(_THREADS) as ex:
+        list(ex.map(one, range(B)))
+    tokens[:, 0] = 0
+    urng = _rng(seed, _S_UNIF)
+    u_acc = (urng.integers(0, 1 << 24, size=(B, n)) / float(1 << 24)).astype(np.float32)
+    u_smp = (urng.integers(0, 1 << 24, size=(B, n)) / float(1 << 24)).astype(np.float32)
+    out = dict(w)
+    out.update(ssm_logits=ssm_st, tokens=tokens, u_accept=u_acc, u_sample=u_smp)
     return out
 
 
