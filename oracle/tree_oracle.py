@@ -37,6 +37,17 @@ from the stored input values (bf16 -> float64 and fp32 -> float64 are exact):
   (Explainer, tree-verification section: the acceptance probability and the
   normalised residual equations, and the statement that the scheme samples
   exactly from the LLM's distribution.)  The uniforms are inputs.
+* topk_lowest, expand_topk: the expansion-based construction step: each
+  frontier node gets as children the k tokens of its SSM logits row with the
+  largest values (ties to the lower token id), numbered after the existing
+  nodes in (frontier order, rank) order.  (Explainer, multi-draft section: one
+  SSM proposes its top-k tokens at each step and the tree grows in depth,
+  configuration <k1, ..., km>.)
+* merge_drafts: the merge-based construction: each draft token sequence is
+  inserted from the root, reusing the child with the same token where one
+  exists and creating one otherwise, drafts in order; node ids follow
+  creation.  (Explainer, multi-draft section: the outputs of several SSMs are
+  merged into one token tree, as in its figure.)
 * commit_kv: the keys and values of the accepted root path become ordinary
   prefix tokens: path node t goes to cache position L_b + t, so the cache
   again holds one linear sequence and the next step attends it like any
@@ -315,6 +326,97 @@ def verify_stochastic(logits, ssm_logits, tokens, parent, u_acc, u_smp, dtype):
         bonus[b] = bo
         dec.append(d)
     return path, plen, bonus, status, dec
+
+
+# ----------------------------------------------------------------------------- tree construction
+def topk_lowest(row: np.ndarray, k: int, dtype: str):
+    """The k largest entries of one row, largest first, ties to the lower index:
+    (indices, values) as int32 / float64."""
+    x = to_f64(row, dtype)
+    order = np.lexsort((np.arange(len(x)), -x))   # primary key: value descending; then index ascending
+    sel = order[:k]
+    return sel.astype(np.int32), x[sel]
+
+
+def expand_topk(parent, depth, tokens, n_cur, frontier, ssm_logits, k: int, n_max: int, dtype: str):
+    """One expansion step for a batch.
+
+    parent, depth, tokens [B][n_max] (entries u < n_cur[b] hold the tree);
+    frontier [B][F] node ids (-1 = unused slot); ssm_logits [B][F][V].
+    Frontier entry f (the r-th valid one) gets children n_cur + r*k + j, j < k,
+    with the j-th largest token of its row.  A sequence with a frontier id
+    outside [0, n_cur), or n_cur outside [1, n_max], or more than n_max nodes
+    after the step, is left unchanged with status TV_EINVAL.
+    Returns (parent, depth, tokens, scores, n_new, status); scores [B][n_max]
+    holds the chosen logits at the new nodes (NaN elsewhere).
+    """
+    parent, depth, tokens = parent.copy(), depth.copy(), tokens.copy()
+    B, F = frontier.shape
+    scores = np.full(parent.shape, np.nan)
+    n_new = np.asarray(n_cur, np.int32).copy()
+    status = np.full(B, TV_OK, np.int32)
+    for b in range(B):
+        nc = int(n_cur[b])
+        valid = [f for f in range(F) if frontier[b][f] >= 0]
+        if not (1 <= nc <= n_max) or any(frontier[b][f] >= nc for f in valid) or nc + len(valid) * k > n_max:
+            status[b] = TV_EINVAL
+            continue
+        for r, f in enumerate(valid):
+            p = int(frontier[b][f])
+            idx, val = topk_lowest(ssm_logits[b][f], k, dtype)
+            for j in range(k):
+                u = nc + r * k + j
+                parent[b][u] = p
+                depth[b][u] = depth[b][p] + 1
+                tokens[b][u] = idx[j]
+                scores[b][u] = val[j]
+        n_new[b] = nc + len(valid) * k
+    return parent, depth, tokens, scores, n_new, status
+
+
+def merge_drafts(drafts, draft_len, root_token, n_max: int):
+    """Merge draft token sequences into one token tree per sequence (a trie).
+
+    drafts [B][M][Ld] int32, draft_len [B][M]; root_token [B] (the token of node 0).
+    Returns (parent, depth, tokens [B][n_max] with -1 past the tree, n [B],
+    node_of [B][M][Ld] = node id of each draft position (-1 past its length),
+    status [B]).  A sequence with a length outside [0, Ld], or needing more than
+    n_max nodes, gets status TV_EINVAL, n = 0 and -1 everywhere.
+    """
+    B, M, Ld = drafts.shape
+    parent = np.full((B, n_max), -1, np.int32)
+    depth = np.full((B, n_max), -1, np.int32)
+    tokens = np.full((B, n_max), -1, np.int32)
+    node_of = np.full((B, M, Ld), -1, np.int32)
+    n = np.zeros(B, np.int32)
+    status = np.full(B, TV_OK, np.int32)
+    for b in range(B):
+        if any(not (0 <= draft_len[b][m] <= Ld) for m in range(M)):
+            status[b] = TV_EINVAL
+            continue
+        par, dep, tok = [-1], [0], [int(root_token[b])]
+        child = {}                                # (parent node, token) -> node
+        where = np.full((M, Ld), -1, np.int32)
+        for m in range(M):
+            cur = 0
+            for d in range(int(draft_len[b][m])):
+                key = (cur, int(drafts[b][m][d]))
+                if key not in child:
+                    child[key] = len(par)
+                    par.append(cur)
+                    dep.append(d + 1)
+                    tok.append(key[1])
+                cur = child[key]
+                where[m][d] = cur
+        if len(par) > n_max:
+            status[b] = TV_EINVAL
+            continue
+        n[b] = len(par)
+        parent[b, :n[b]] = par
+        depth[b, :n[b]] = dep
+        tokens[b, :n[b]] = tok
+        node_of[b] = where
+    return parent, depth, tokens, n, node_of, status
 
 
 # ----------------------------------------------------------------------------- KV commit
