@@ -9,9 +9,10 @@ Each timed step uses the next of R input copies (R chosen so the copies exceed
 twice the 256 MB last-level cache), the way consecutive layers each bring their
 own KV cache: a step never finds its inputs already cached.
 
-tree_commit_kv (writing the accepted path's K/V into the cache) and
+tree_commit_kv (writing the accepted path's K/V into the cache),
 tree_verify_stochastic (multi-step speculative sampling, the alternative to the
-greedy walk) are not part of the timed step; their own kernel times are reported
+greedy walk) and the construction calls (tree_expand_topk, tree_merge_drafts)
+are not part of the timed step; their own kernel times are reported
 under kernel_us.  The commit writes the path verification accepted (or, on
 workloads without a vocabulary, the root path to each tree's deepest node) into
 cache room left after each prefix; stochastic verification runs on SSM logits
@@ -240,6 +241,39 @@ def main():
         es_l = 2 if cfg.dtype == "bf16" else 4
         mss_out = {"us": round(t_mss * 1e6, 2), "mean_path_len": round(float(plen_h.mean()), 3),
                    "rows_read": rows, "hbm_gbs": round(rows * cfg.vocab * es_l / t_mss / 1e9, 1)}
+    # tree construction: one expansion step (4 frontier nodes per sequence, k = 4,
+    # on the SSM rows) and a merge of 8 drafts of 8 tokens per sequence
+    cons_out = None
+    if mss is not None:
+        Fx, kx = min(4, cfg.n), 4
+        nmx = cfg.n + Fx * kx
+        pad = lambda a: np.pad(a, ((0, 0), (0, nmx - cfg.n)), constant_values=-1).astype(np.int32)
+        ex_par = torch.from_numpy(pad(w["parent"])).cuda()
+        ex_dep = torch.from_numpy(pad(w["depth"])).cuda()
+        ex_tok = torch.from_numpy(pad(w["tokens"])).cuda()
+        ex_rows = mss[0]["ssm"][:, :Fx].contiguous()
+        ex_front = torch.arange(Fx, dtype=torch.int32, device="cuda").repeat(cfg.B, 1).contiguous()
+        ex_ncur = torch.full((cfg.B,), cfg.n, dtype=torch.int32, device="cuda")
+        ex_nout = torch.empty(cfg.B, dtype=torch.int32, device="cuda")
+        ex_st = torch.empty(cfg.B, dtype=torch.int32, device="cuda")
+        t_exp = timed_graph(lambda i, h: _lib.tree_expand_topk(ex_rows, ex_front, ex_ncur, ex_par, ex_dep, ex_tok, kx,
+                                                               n_out=ex_nout, status=ex_st,
+                                                               stream=torch.cuda.ExternalStream(h)))
+        drng = np.random.default_rng(1)
+        Md, Ldd = 8, 8
+        mg_dr = torch.from_numpy(drng.integers(0, 4, size=(cfg.B, Md, Ldd)).astype(np.int32)).cuda()
+        mg_len = torch.full((cfg.B, Md), Ldd, dtype=torch.int32, device="cuda")
+        mg_out = [torch.empty(sh_, dtype=torch.int32, device="cuda")
+                  for sh_ in ((cfg.B, 256), (cfg.B, 256), (cfg.B, 256), (cfg.B,), (cfg.B, Md, Ldd), (cfg.B,))]
+        t_mrg = timed_graph(lambda i, h: _lib.tree_merge_drafts(mg_dr, mg_len, 256, parent=mg_out[0], depth=mg_out[1],
+                                                                tokens=mg_out[2], n_out=mg_out[3], node_of=mg_out[4],
+                                                                status=mg_out[5], stream=torch.cuda.ExternalStream(h)))
+        if not ((ex_st == 0).all().item() and (mg_out[5] == 0).all().item()):
+            raise RuntimeError("tree construction rejected a sequence of the benchmark batch")
+        es_l = 2 if cfg.dtype == "bf16" else 4
+        cons_out = {"expand_us": round(t_exp * 1e6, 2), "expand_rows": cfg.B * Fx, "k": kx,
+                    "expand_hbm_gbs": round(cfg.B * Fx * cfg.vocab * es_l / t_exp / 1e9, 1),
+                    "merge_us": round(t_mrg * 1e6, 2), "merge_drafts": [Md, Ldd]}
 
     # throughput: K whole steps back to back.  Default: one HIP graph holding one step
     # per input copy (R steps), replayed K/R times; --eager launches each call.
@@ -291,6 +325,7 @@ def main():
                       "tree_verify_greedy": round(t_ver * 1e6, 2), "tree_commit_kv": round(t_commit * 1e6, 2),
                       "tree_verify_stochastic": mss_out["us"] if mss_out else None},
         "stochastic": mss_out,
+        "construct": cons_out,
         "commit": {"tokens": committed, "hbm_gbs": round(4 * committed * cfg.Hkv * cfg.D * es / t_commit / 1e9, 1)},
         "verify_hbm_gbs": round(refb["verify_bytes"] / t_ver / 1e9, 1) if cfg.vocab and t_ver else None,
     }

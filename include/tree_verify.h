@@ -6,8 +6,9 @@
  * plus exactly the nodes on its own root-to-u path S_u, and greedy
  * verification then walks the tree from the root.  This library is that hot
  * path: three calls, all asynchronous on a caller-provided HIP stream; a
- * stochastic variant of verification; and a call that commits the accepted
- * path's keys and values to the cache.
+ * stochastic variant of verification; the construction of the tree (top-k
+ * expansion, merge of drafts); and a call that commits the accepted path's
+ * keys and values to the cache.
  *
  * Sources (the SpecInfer explainer at 0h-n0.github.io, "paper-2305-09781"):
  *   - token-tree structure section: a node per token, S_u = tokens on the path
@@ -213,6 +214,60 @@ int tree_verify_stochastic(int B, int n, int V, int logits_dtype, const void* lo
                            const float* u_sample, int32_t* path_out,
                            int32_t* path_len, int32_t* bonus, int32_t* status,
                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Token-tree construction (the explainer's multi-draft section): the
+ * expansion-based strategy grows the tree by one SSM's top-k tokens per step
+ * (configuration <k1, ..., km>); the merge-based strategy merges several SSMs'
+ * drafts into one token tree.  Both produce the parent/depth/tokens arrays
+ * tree_build and the verification calls take.
+ *
+ * tree_expand_topk: one expansion step.
+ *   ssm_logits [B][F][V] logits_dtype: the SSM's logits after each frontier node
+ *   frontier   [B][F] int32  node ids to expand, -1 = unused slot (1 <= F <= 256)
+ *   n_cur      [B]    int32  nodes already in each tree (1 <= n_cur <= n_max)
+ *   parent, depth, tokens [B][n_max] int32  in/out: entries u < n_cur hold the
+ *              tree; the step appends nodes n_cur .. n_cur + r*k - 1 (r = valid
+ *              frontier slots), the r-th valid slot's children at
+ *              n_cur + r*k + j, j < k, with token = the j-th largest entry of its
+ *              row (ties to the lower token id), parent = the frontier node,
+ *              depth = its depth + 1.  Other entries are not written.
+ *   scores     [B][n_max] float out (may be NULL): the chosen logit of each new node
+ *   n_out      [B] int32 out: n_cur + r*k
+ *   status     [B] int32 out: TV_OK, or TV_EINVAL (nothing appended, n_out =
+ *              n_cur) for a frontier id outside [0, n_cur), n_cur outside
+ *              [1, n_max], or more than n_max nodes after the step.
+ * 1 <= k <= TV_TOPK_MAX, k <= V, n_max <= TV_NMAX.  NaN logits are out of
+ * contract.  The appended rows must not alias the frontier's own rows.
+ * ------------------------------------------------------------------------- */
+#define TV_TOPK_MAX 16
+int tree_expand_topk(int B, int F, int V, int k, int n_max, int logits_dtype,
+                     const void* ssm_logits, const int32_t* frontier,
+                     const int32_t* n_cur, int32_t* parent, int32_t* depth,
+                     int32_t* tokens, float* scores, int32_t* n_out,
+                     int32_t* status, void* stream);
+
+/* tree_merge_drafts: the trie of each sequence's drafts.
+ *   drafts     [B][M][Ld] int32  draft token sequences (any int32 tokens)
+ *   draft_len  [B][M]     int32  tokens in each draft (0 <= len <= Ld)
+ *   root_token [B]        int32  token of node 0 (may be NULL: 0)
+ *   parent, depth, tokens [B][n_max] int32 out: the tree; every draft is inserted
+ *              from the root, reusing the child with the same token where there
+ *              is one, drafts in order and positions in order; node ids follow
+ *              creation.  Entries from n on are -1.
+ *   n_out      [B] int32 out: nodes, root included
+ *   node_of    [B][M][Ld] int32 out (may be NULL): the node of each draft
+ *              position, -1 past the draft's length
+ *   status     [B] int32 out: TV_OK, or TV_EINVAL (n_out = 0, all -1) for a
+ *              length outside [0, Ld] or a tree of more than n_max nodes.
+ * 1 <= M <= TV_MERGE_MMAX, 1 <= Ld < TV_NMAX, 1 <= n_max <= TV_NMAX.
+ * ------------------------------------------------------------------------- */
+#define TV_MERGE_MMAX 64
+int tree_merge_drafts(int B, int M, int Ld, int n_max, const int32_t* drafts,
+                      const int32_t* draft_len, const int32_t* root_token,
+                      int32_t* parent, int32_t* depth, int32_t* tokens,
+                      int32_t* n_out, int32_t* node_of, int32_t* status,
+                      void* stream);
 
 /* ---------------------------------------------------------------------------
  * tree_commit_kv: the accepted path's keys and values become prefix tokens.

@@ -172,3 +172,25 @@ def test_stochastic_argument_errors(lib):
     assert call(2, 7, 10, tv.TV_F32, wb=ws(2, 10) - 1) == tv.TV_EWORKSPACE
     assert call(2, 7, 10, tv.TV_F32, ptrs=[0x100004] + [0x100000] * 9) == tv.TV_EINVAL   # misaligned logits
     assert call(0, 7, 10, tv.TV_F32, ptrs=[None] * 10, w=None, wb=0) == tv.TV_OK
+
+
+def test_construction_argument_errors(lib):
+    P = [0x100000] * 9
+    ex = lambda B, F, V, k, n_max, dt=tv.TV_BF16, ptrs=P: lib.tree_expand_topk(B, F, V, k, n_max, dt, *ptrs, None)
+    assert ex(2, 0, 100, 2, 64) == tv.TV_EINVAL
+    assert ex(2, 257, 100, 2, 64) == tv.TV_EINVAL
+    assert ex(2, 3, 100, 0, 64) == tv.TV_EINVAL
+    assert ex(2, 3, 100, tv.TV_TOPK_MAX + 1, 64) == tv.TV_EINVAL
+    assert ex(2, 3, 4, 5, 64) == tv.TV_EINVAL                           # k > V
+    assert ex(2, 3, 100, 2, tv.TV_NMAX + 1) == tv.TV_EINVAL
+    assert ex(2, 3, 100, 2, 64, dt=7) == tv.TV_EUNSUPPORTED
+    assert ex(2, 3, 100, 2, 64, ptrs=[None] * 9) == tv.TV_EINVAL
+    assert ex(0, 3, 100, 2, 64, ptrs=[None] * 9) == tv.TV_OK
+    mg = lambda B, M, Ld, n_max, ptrs=[0x100000] * 9: lib.tree_merge_drafts(B, M, Ld, n_max, *ptrs, None)
+    assert mg(2, 0, 8, 64) == tv.TV_EINVAL
+    assert mg(2, tv.TV_MERGE_MMAX + 1, 8, 64) == tv.TV_EINVAL
+    assert mg(2, 3, 0, 64) == tv.TV_EINVAL
+    assert mg(2, 3, tv.TV_NMAX, 64) == tv.TV_EINVAL
+    assert mg(2, 3, 8, 0) == tv.TV_EINVAL
+    assert mg(2, 3, 8, 64, ptrs=[None] * 9) == tv.TV_EINVAL
+    assert mg(0, 3, 8, 64, ptrs=[None] * 9) == tv.TV_OK

@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_PKG, "libtreeverify.so")
 
 TV_OK, TV_EINVAL, TV_ETOPOLOGY, TV_EUNSUPPORTED, TV_EWORKSPACE, TV_EHIP = range(6)
 TV_F32, TV_BF16 = 0, 1
-TV_NMAX, TV_PAGE, TV_MSS_VMAX = 256, 16, 1 << 20
+TV_NMAX, TV_PAGE, TV_MSS_VMAX, TV_TOPK_MAX, TV_MERGE_MMAX = 256, 16, 1 << 20, 16, 64
 
 _c_int, _c_float, _vp, _size_t = ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
 
@@ -49,6 +49,8 @@ SIGNATURES = {
     "tree_verify_greedy": (_c_int, [_c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "tree_verify_stochastic_workspace_size": (_size_t, [_c_int, _c_int]),
     "tree_verify_stochastic": (_c_int, [_c_int, _c_int, _c_int, _c_int] + [_vp] * 11 + [_size_t, _vp]),
+    "tree_expand_topk": (_c_int, [_c_int] * 6 + [_vp] * 9 + [_vp]),
+    "tree_merge_drafts": (_c_int, [_c_int] * 4 + [_vp] * 9 + [_vp]),
     "tree_commit_kv": (_c_int, [ctypes.POINTER(AttnDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                 _vp]),
 }
@@ -203,6 +205,42 @@ def tree_verify_stochastic(logits, ssm_logits, tokens, parent, u_accept, u_sampl
                                        _ptr(bonus), _ptr(status), _ptr(workspace), wbytes, _stream(stream))
     _check(rc, "tree_verify_stochastic")
     return path, path_len, bonus, status
+
+
+def tree_expand_topk(ssm_logits, frontier, n_cur, parent, depth, tokens, k, *, scores=None, n_out=None, status=None,
+                     stream=None):
+    """One expansion step: frontier slot f of sequence b gets the k best tokens of
+    ssm_logits[b][f] as children, appended in place to parent/depth/tokens
+    [B][n_max].  Returns (n_out [B], status [B])."""
+    B, F, V = ssm_logits.shape
+    n_max = parent.shape[1]
+    dev = ssm_logits.device
+    n_out = torch.empty((B,), dtype=torch.int32, device=dev) if n_out is None else n_out
+    status = torch.empty((B,), dtype=torch.int32, device=dev) if status is None else status
+    rc = load().tree_expand_topk(B, F, V, k, n_max, _dtype_code(ssm_logits), _ptr(ssm_logits), _ptr(frontier),
+                                 _ptr(n_cur), _ptr(parent), _ptr(depth), _ptr(tokens), _ptr(scores), _ptr(n_out),
+                                 _ptr(status), _stream(stream))
+    _check(rc, "tree_expand_topk")
+    return n_out, status
+
+
+def tree_merge_drafts(drafts, draft_len, n_max, *, root_token=None, parent=None, depth=None, tokens=None, n_out=None,
+                      node_of=None, status=None, stream=None):
+    """Trie of each sequence's drafts [B][M][Ld] (lengths [B][M]).  Returns
+    (parent, depth, tokens [B][n_max], n_out [B], node_of [B][M][Ld], status [B])."""
+    B, M, Ld = drafts.shape
+    dev = drafts.device
+    mk = lambda shape: torch.empty(shape, dtype=torch.int32, device=dev)
+    parent = mk((B, n_max)) if parent is None else parent
+    depth = mk((B, n_max)) if depth is None else depth
+    tokens = mk((B, n_max)) if tokens is None else tokens
+    n_out = mk((B,)) if n_out is None else n_out
+    node_of = mk((B, M, Ld)) if node_of is None else node_of
+    status = mk((B,)) if status is None else status
+    rc = load().tree_merge_drafts(B, M, Ld, n_max, _ptr(drafts), _ptr(draft_len), _ptr(root_token), _ptr(parent),
+                                  _ptr(depth), _ptr(tokens), _ptr(n_out), _ptr(node_of), _ptr(status), _stream(stream))
+    _check(rc, "tree_merge_drafts")
+    return parent, depth, tokens, n_out, node_of, status
 
 
 def tree_commit_kv(k_cache, v_cache, prefix_len, k_tree, v_tree, path, path_len, *, block_table=None,

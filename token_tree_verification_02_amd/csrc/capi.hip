@@ -286,6 +286,42 @@ int tree_verify_stochastic(int B, int n, int V, int logits_dtype, const void* lo
   return TV_OK;
 }
 
+int tree_expand_topk(int B, int F, int V, int k, int n_max, int logits_dtype, const void* ssm_logits,
+                     const int32_t* frontier, const int32_t* n_cur, int32_t* parent, int32_t* depth, int32_t* tokens,
+                     float* scores, int32_t* n_out, int32_t* status, void* stream) {
+  if (B < 0) return fail(TV_EINVAL, "B=%d < 0", B);
+  if (F < 1 || F > 256) return fail(TV_EINVAL, "F=%d outside [1, 256]", F);
+  if (V < 1) return fail(TV_EINVAL, "V=%d < 1", V);
+  if (k < 1 || k > TV_TOPK_MAX || k > V) return fail(TV_EINVAL, "k=%d outside [1, min(%d, V)]", k, TV_TOPK_MAX);
+  if (n_max < 1 || n_max > TV_NMAX) return fail(TV_EINVAL, "n_max=%d outside [1, %d]", n_max, TV_NMAX);
+  if (logits_dtype != TV_F32 && logits_dtype != TV_BF16)
+    return fail(TV_EUNSUPPORTED, "logits dtype %d", logits_dtype);
+  if ((long long)B * F > 0x7fffffffLL) return fail(TV_EINVAL, "B*F too large");
+  if (B == 0) return TV_OK;
+  if (!ssm_logits || !frontier || !n_cur || !parent || !depth || !tokens || !n_out || !status)
+    return fail(TV_EINVAL, "null pointer argument");
+  hipError_t e = tv::launch_expand(B, F, V, k, n_max, logits_dtype == TV_BF16, ssm_logits, frontier, n_cur, parent,
+                                   depth, tokens, scores, n_out, status, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "tree_expand_topk launch");
+  return TV_OK;
+}
+
+int tree_merge_drafts(int B, int M, int Ld, int n_max, const int32_t* drafts, const int32_t* draft_len,
+                      const int32_t* root_token, int32_t* parent, int32_t* depth, int32_t* tokens, int32_t* n_out,
+                      int32_t* node_of, int32_t* status, void* stream) {
+  if (B < 0) return fail(TV_EINVAL, "B=%d < 0", B);
+  if (M < 1 || M > TV_MERGE_MMAX) return fail(TV_EINVAL, "M=%d outside [1, %d]", M, TV_MERGE_MMAX);
+  if (Ld < 1 || Ld >= TV_NMAX) return fail(TV_EINVAL, "Ld=%d outside [1, %d]", Ld, TV_NMAX - 1);
+  if (n_max < 1 || n_max > TV_NMAX) return fail(TV_EINVAL, "n_max=%d outside [1, %d]", n_max, TV_NMAX);
+  if (B == 0) return TV_OK;
+  if (!drafts || !draft_len || !parent || !depth || !tokens || !n_out || !status)
+    return fail(TV_EINVAL, "null pointer argument");
+  hipError_t e = tv::launch_merge_drafts(B, M, Ld, n_max, drafts, draft_len, root_token, parent, depth, tokens, n_out,
+                                         node_of, status, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "tree_merge_drafts launch");
+  return TV_OK;
+}
+
 int tree_commit_kv(const tv_attn_desc* desc, void* k_cache, void* v_cache, const int32_t* block_table,
                    const int32_t* prefix_len, const void* k_tree, const void* v_tree, const int32_t* path,
                    const int32_t* path_len, int32_t* new_prefix_len, int32_t* status, void* stream) {

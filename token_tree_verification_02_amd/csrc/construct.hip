@@ -1,0 +1,293 @@
+// Token-tree construction: the expansion step (top-k children per frontier node)
+// and the merge of several drafts into one tree.
+//
+// SpecInfer explainer, multi-draft section: in the expansion-based strategy one
+// SSM proposes its top-k tokens at each step and the tree grows in depth
+// (configuration <k1, ..., km>); in the merge-based strategy the outputs of
+// several SSMs are merged into one token tree (its figure: two SSMs' drafts
+// sharing their first token's node).
+//
+// topk_kernel reads one SSM logits row per workgroup in two passes of 16-byte
+// vectors.  The first takes each thread's maximum; the k-th largest of those
+// 256 maxima bounds the row's k-th largest value from below.  The second pass
+// (mostly cache hits) keeps, per thread, its best 16 (value desc, index asc)
+// among the entries at or above that bound, which are few, so the insertion
+// code rarely runs and waves do not diverge on it.  k rounds of a workgroup
+// argmax over the threads' heads then pick the row's top k.  The children are written straight into the caller's tree
+// arrays after the existing nodes.
+//
+// merge_kernel builds the trie of one sequence's drafts without sequential
+// insertion: position d of draft m names the node of prefix drafts[m][0..d];
+// that node belongs to the first draft sharing the prefix, draft m creates the
+// nodes from its longest overlap with any earlier draft onward, and a prefix
+// sum over the drafts' counts places them in creation order.
+#include <limits.h>
+
+#include "tv_internal.h"
+
+namespace tv {
+namespace {
+
+constexpr int kKeep = TV_TOPK_MAX;  // per-thread list length (>= k)
+
+// (value desc, index asc): does (v2, i2) rank before (v1, i1)?
+__device__ __forceinline__ bool before(float v2, int i2, float v1, int i1) {
+  return v2 > v1 || (v2 == v1 && i2 < i1) || (i1 == INT_MAX && i2 != INT_MAX);
+}
+
+// insert (v, i) into a sorted list; i is larger than every index already kept,
+// so it goes after every entry with value >= v
+__device__ __forceinline__ void keep_insert(float (&lv)[kKeep], int (&li)[kKeep], float v, int i) {
+  if (!(v > lv[kKeep - 1]) && li[kKeep - 1] != INT_MAX) return;
+#pragma unroll
+  for (int s = kKeep - 1; s > 0; --s) {
+    const bool shift = v > lv[s - 1] || li[s - 1] == INT_MAX;  // the new entry goes at or above s-1
+    const bool here = !shift && (v > lv[s] || li[s] == INT_MAX);
+    lv[s] = shift ? lv[s - 1] : (here ? v : lv[s]);
+    li[s] = shift ? li[s - 1] : (here ? i : li[s]);
+  }
+  if (v > lv[0] || li[0] == INT_MAX) {
+    lv[0] = v;
+    li[0] = i;
+  }
+}
+
+// One workgroup of 256 threads per (sequence, frontier slot).  Every workgroup
+// checks its sequence's frontier (ids in [0, n_cur), room for the children)
+// before writing; slot 0 reports status and the new node count.
+template <bool BF16>
+__global__ __launch_bounds__(256) void topk_kernel(int F, int V, int k, int n_max, const void* __restrict__ logits,
+                                                   const int32_t* __restrict__ frontier,
+                                                   const int32_t* __restrict__ n_cur, int32_t* __restrict__ parent,
+                                                   int32_t* __restrict__ depth, int32_t* __restrict__ tokens,
+                                                   float* __restrict__ scores, int32_t* __restrict__ n_out,
+                                                   int32_t* __restrict__ status) {
+  __shared__ float sv[4];
+  __shared__ int si[4];
+  __shared__ unsigned long long sb[4];
+  __shared__ int s_win;
+  __shared__ float sv_all[256];
+  __shared__ float s_thr;
+  const int b = blockIdx.x / F, f = blockIdx.x - b * F;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int nc = n_cur[b];
+  // ---- the sequence's frontier (F <= 256: one slot per thread): valid slots, this slot's rank
+  const int fr = tid < F ? frontier[(size_t)b * F + tid] : -1;
+  const bool valid = fr >= 0;
+  int bad = valid && fr >= nc;
+  const unsigned long long bl = __ballot(valid);
+  if (lane == 0) sb[wv] = bl;
+  bad = __syncthreads_or(bad);
+  int nvalid = 0, valid_before = 0;
+  for (int w = 0; w < 4; ++w) {
+    nvalid += __popcll(sb[w]);
+    if (w < (f >> 6)) valid_before += __popcll(sb[w]);
+  }
+  valid_before += __popcll(sb[f >> 6] & ((1ull << (f & 63)) - 1));
+  bad = bad || nc < 1 || nc > n_max || (long long)nc + (long long)nvalid * k > n_max;
+  if (f == 0 && tid == 0) {
+    status[b] = bad ? TV_EINVAL : TV_OK;
+    n_out[b] = bad ? nc : nc + nvalid * k;
+  }
+  const int p = frontier[(size_t)b * F + f];
+  if (bad || p < 0) return;
+
+  const size_t es = BF16 ? 2 : 4;
+  const char* row = (const char*)logits + ((size_t)b * F + f) * V * es;
+  constexpr int EPV = BF16 ? 8 : 4;
+  constexpr int R = 4;
+  const bool aligned = ((uintptr_t)row & 15) == 0;
+  const int nv = aligned ? V / EPV : 0;
+  const uint4* vp = (const uint4*)row;
+  // Visit every element of this thread's share in increasing index order:
+  // 16-byte vectors first, then the unaligned tail one by one.
+  auto sweep = [&](auto&& fn) {
+    for (int base = 0; base < nv; base += R * 256) {
+      uint4 w[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) w[r] = vp[min(base + r * 256 + tid, nv - 1)];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int vi = base + r * 256 + tid;
+        if (vi >= nv) continue;
+        const uint32_t q[4] = {w[r].x, w[r].y, w[r].z, w[r].w};
+#pragma unroll
+        for (int e = 0; e < EPV; ++e)
+          fn(BF16 ? ((e & 1) ? bf16hi(q[e >> 1]) : bf16lo(q[e >> 1])) : __uint_as_float(q[e]), vi * EPV + e);
+      }
+    }
+    for (int i = nv * EPV + tid; i < V; i += 256)
+      fn(BF16 ? bf16_to_f32(((const uint16_t*)row)[i]) : ((const float*)row)[i], i);
+  };
+
+  // ---- pass 1: each thread's maximum; the k-th largest of these 256 maxima is
+  // a lower bound on the row's k-th largest value (they are k real entries)
+  float tmax = -INFINITY;
+  sweep([&](float x, int) { tmax = fmaxf(tmax, x); });
+  sv_all[tid] = tmax;
+  __syncthreads();
+  {
+    int above = 0;  // maxima ranked before mine: larger, or equal from a lower thread
+    for (int t = 0; t < 256; ++t) {
+      const float o = sv_all[t];
+      above += o > tmax || (o == tmax && t < tid);
+    }
+    if (above == k - 1) s_thr = tmax;
+  }
+  __syncthreads();
+  const float thr = s_thr;
+
+  // ---- pass 2 (mostly cache hits): each thread's best 16 among entries >= thr
+  float lv[kKeep];
+  int li[kKeep];
+#pragma unroll
+  for (int s = 0; s < kKeep; ++s) lv[s] = -INFINITY, li[s] = INT_MAX;
+  sweep([&](float x, int i) {
+    if (x >= thr) keep_insert(lv, li, x, i);
+  });
+
+  // ---- k rounds: the best head among all threads; its owner drops it
+  const int dp = depth[(size_t)b * n_max + p];
+  const int u0 = nc + valid_before * k;
+  for (int j = 0; j < k; ++j) {
+    float bv = lv[0];
+    int bi = li[0];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float ov = __shfl_xor(bv, o);
+      const int oi = __shfl_xor(bi, o);
+      if (before(ov, oi, bv, bi)) bv = ov, bi = oi;
+    }
+    if (lane == 0) sv[wv] = bv, si[wv] = bi;
+    __syncthreads();
+    if (tid == 0) {
+      float v = sv[0];
+      int i = si[0];
+      for (int w = 1; w < 4; ++w)
+        if (before(sv[w], si[w], v, i)) v = sv[w], i = si[w];
+      const int u = u0 + j;
+      parent[(size_t)b * n_max + u] = p;
+      depth[(size_t)b * n_max + u] = dp + 1;
+      tokens[(size_t)b * n_max + u] = i;
+      if (scores) scores[(size_t)b * n_max + u] = v;
+      s_win = i;
+    }
+    __syncthreads();
+    if (li[0] == s_win) {  // indices are unique, so exactly one thread owns the winner
+#pragma unroll
+      for (int s = 0; s < kKeep - 1; ++s) lv[s] = lv[s + 1], li[s] = li[s + 1];
+      lv[kKeep - 1] = -INFINITY, li[kKeep - 1] = INT_MAX;
+    }
+  }
+}
+
+// One workgroup of 256 threads per sequence.
+__global__ __launch_bounds__(256) void merge_kernel(int M, int Ld, int n_max, const int32_t* __restrict__ drafts,
+                                                    const int32_t* __restrict__ draft_len,
+                                                    const int32_t* __restrict__ root_token,
+                                                    int32_t* __restrict__ parent, int32_t* __restrict__ depth,
+                                                    int32_t* __restrict__ tokens, int32_t* __restrict__ n_out,
+                                                    int32_t* __restrict__ node_of, int32_t* __restrict__ status) {
+  __shared__ int len[TV_MERGE_MMAX];
+  __shared__ int lcp[TV_MERGE_MMAX][TV_MERGE_MMAX];  // lcp[a][m] for a < m
+  __shared__ int start[TV_MERGE_MMAX], base[TV_MERGE_MMAX];
+  __shared__ int s_n;
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int32_t* dr = drafts + (size_t)b * M * Ld;
+  int bad = 0;
+  if (tid < M) {
+    len[tid] = draft_len[(size_t)b * M + tid];
+    bad = len[tid] < 0 || len[tid] > Ld;
+  }
+  bad = __syncthreads_or(bad);
+  if (!bad) {
+    // common-prefix length of every pair of drafts (a < m)
+    for (int pq = tid; pq < M * M; pq += 256) {
+      const int a = pq / M, m = pq - a * M;
+      if (a >= m) continue;
+      const int lim = min(len[a], len[m]);
+      int l = 0;
+      while (l < lim && dr[(size_t)a * Ld + l] == dr[(size_t)m * Ld + l]) ++l;
+      lcp[a][m] = l;
+    }
+    __syncthreads();
+    if (tid < M) {  // draft m creates the nodes of its positions from its longest overlap on
+      int s = 0;
+      for (int a = 0; a < tid; ++a) s = max(s, lcp[a][tid]);
+      start[tid] = s;
+    }
+    __syncthreads();
+    if (tid == 0) {  // creation order: drafts in order, positions in order
+      int acc = 1;
+      for (int m = 0; m < M; ++m) {
+        base[m] = acc;
+        acc += len[m] - start[m];
+      }
+      s_n = acc;
+    }
+    __syncthreads();
+    bad = s_n > n_max;
+  }
+  int32_t* par = parent + (size_t)b * n_max;
+  int32_t* dep = depth + (size_t)b * n_max;
+  int32_t* tok = tokens + (size_t)b * n_max;
+  int32_t* nof = node_of ? node_of + (size_t)b * M * Ld : nullptr;
+  const int n = bad ? 0 : s_n;
+  for (int u = tid; u < n_max; u += 256) {
+    if (u >= n) par[u] = -1, dep[u] = -1, tok[u] = -1;
+  }
+  if (tid == 0) {
+    n_out[b] = n;
+    status[b] = bad ? TV_EINVAL : TV_OK;
+    if (!bad) {
+      par[0] = -1, dep[0] = 0;
+      tok[0] = root_token ? root_token[b] : 0;
+    }
+  }
+  // node id of position d of draft m: created by the first draft sharing the prefix
+  auto node = [&](int m, int d) {
+    int a = 0;
+    while (a < m && lcp[a][m] <= d) ++a;
+    return base[a] + (d - start[a]);
+  };
+  for (int pos = tid; pos < M * Ld; pos += 256) {
+    const int m = pos / Ld, d = pos - m * Ld;
+    if (bad || d >= len[m]) {
+      if (nof) nof[pos] = -1;
+      continue;
+    }
+    const int u = node(m, d);
+    if (nof) nof[pos] = u;
+    if (d >= start[m]) {  // this draft created the node
+      par[u] = d == 0 ? 0 : node(m, d - 1);
+      dep[u] = d + 1;
+      tok[u] = dr[(size_t)m * Ld + d];
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_expand(int B, int F, int V, int k, int n_max, int bf16, const void* logits, const int32_t* frontier,
+                         const int32_t* n_cur, int32_t* parent, int32_t* depth, int32_t* tokens, float* scores,
+                         int32_t* n_out, int32_t* status, hipStream_t s) {
+  if (B == 0) return hipSuccess;
+  if (bf16)
+    hipLaunchKernelGGL(topk_kernel<true>, dim3(B * F), dim3(256), 0, s, F, V, k, n_max, logits, frontier, n_cur,
+                       parent, depth, tokens, scores, n_out, status);
+  else
+    hipLaunchKernelGGL(topk_kernel<false>, dim3(B * F), dim3(256), 0, s, F, V, k, n_max, logits, frontier, n_cur,
+                       parent, depth, tokens, scores, n_out, status);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge_drafts(int B, int M, int Ld, int n_max, const int32_t* drafts, const int32_t* draft_len,
+                               const int32_t* root_token, int32_t* parent, int32_t* depth, int32_t* tokens,
+                               int32_t* n_out, int32_t* node_of, int32_t* status, hipStream_t s) {
+  if (B == 0) return hipSuccess;
+  hipLaunchKernelGGL(merge_kernel, dim3(B), dim3(256), 0, s, M, Ld, n_max, drafts, draft_len, root_token, parent,
+                     depth, tokens, n_out, node_of, status);
+  return hipGetLastError();
+}
+
+}  // namespace tv

@@ -71,6 +71,12 @@ size_t mss_workspace_bytes(int B, int V);
 hipError_t launch_mss(int B, int n, int V, int bf16, const void* logits, const void* ssm, const int32_t* tokens,
                       const int32_t* parent, const float* u_acc, const float* u_smp, float* ws, int32_t* path,
                       int32_t* plen, int32_t* bonus, int32_t* status, hipStream_t s);
+hipError_t launch_expand(int B, int F, int V, int k, int n_max, int bf16, const void* logits, const int32_t* frontier,
+                         const int32_t* n_cur, int32_t* parent, int32_t* depth, int32_t* tokens, float* scores,
+                         int32_t* n_out, int32_t* status, hipStream_t s);
+hipError_t launch_merge_drafts(int B, int M, int Ld, int n_max, const int32_t* drafts, const int32_t* draft_len,
+                               const int32_t* root_token, int32_t* parent, int32_t* depth, int32_t* tokens,
+                               int32_t* n_out, int32_t* node_of, int32_t* status, hipStream_t s);
 hipError_t launch_verify(int B, int n, int V, int bf16, const void* logits, const int32_t* tokens,
                          const int32_t* parent, int32_t* am, int32_t* path, int32_t* plen,
                          int32_t* bonus, hipStream_t s);
