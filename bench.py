@@ -98,6 +98,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--dtype", choices=["bf16", "f16"], default=None,
+                    help="element type of q/K/V/out/logits (default: the workload's)")
     ap.add_argument("--copies", type=int, default=0, help="input copies to rotate (0 = auto)")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--eager", action="store_true", help="launch each step eagerly instead of replaying a HIP graph")
@@ -128,10 +130,11 @@ def main():
     from token_tree_verification_02_amd import runner
     from token_tree_verification_02_amd import workloads as W
 
-    cfg = W.config(args.config)
+    cfg = W.config(args.config, **({"dtype": args.dtype} if args.dtype else {}))
     t_gen = time.perf_counter()
     w = W.make(cfg, room=cfg.n)
-    ws = W.make_stochastic(cfg, w=w) if cfg.vocab else None
+    # stochastic verification and top-k expansion take bf16 or fp32 logits
+    ws = W.make_stochastic(cfg, w=w) if cfg.vocab and cfg.dtype != "f16" else None
     t_gen = time.perf_counter() - t_gen
     refb = W.reference_bytes(w)
     per_copy = refb["attn_bytes"] + refb["verify_bytes"]
@@ -155,8 +158,7 @@ def main():
     mss = None
     if ws is not None:
         from token_tree_verification_02_amd import _lib
-        bf = cfg.dtype == "bf16"
-        mss = [dict(ssm=runner._t(ws["ssm_logits"], "cuda", bf16=bf), tok=runner._t(ws["tokens"], "cuda"),
+        mss = [dict(ssm=runner._t(ws["ssm_logits"], "cuda", dtype=cfg.dtype), tok=runner._t(ws["tokens"], "cuda"),
                     ua=runner._t(ws["u_accept"], "cuda"), us=runner._t(ws["u_sample"], "cuda"),
                     path=torch.empty((cfg.B, cfg.n), dtype=torch.int32, device="cuda"),
                     plen=torch.empty(cfg.B, dtype=torch.int32, device="cuda"),
@@ -238,7 +240,7 @@ def main():
             for j, u in enumerate(vis):
                 ch = [v for v in range(cfg.n) if par[v] == u]
                 rows += 1 + (ch.index(vis[j + 1]) + 1 if j + 1 < len(vis) else len(ch))
-        es_l = 2 if cfg.dtype == "bf16" else 4
+        es_l = 2 if W.is16(cfg.dtype) else 4
         mss_out = {"us": round(t_mss * 1e6, 2), "mean_path_len": round(float(plen_h.mean()), 3),
                    "rows_read": rows, "hbm_gbs": round(rows * cfg.vocab * es_l / t_mss / 1e9, 1)}
     # tree construction: one expansion step (4 frontier nodes per sequence, k = 4,
@@ -270,7 +272,7 @@ def main():
                                                                 status=mg_out[5], stream=torch.cuda.ExternalStream(h)))
         if not ((ex_st == 0).all().item() and (mg_out[5] == 0).all().item()):
             raise RuntimeError("tree construction rejected a sequence of the benchmark batch")
-        es_l = 2 if cfg.dtype == "bf16" else 4
+        es_l = 2 if W.is16(cfg.dtype) else 4
         cons_out = {"expand_us": round(t_exp * 1e6, 2), "expand_rows": cfg.B * Fx, "k": kx,
                     "expand_hbm_gbs": round(cfg.B * Fx * cfg.vocab * es_l / t_exp / 1e9, 1),
                     "merge_us": round(t_mrg * 1e6, 2), "merge_drafts": [Md, Ldd]}
@@ -301,9 +303,9 @@ def main():
     tokens = cfg.B * cfg.n
     value = tokens / (wall / K)
 
-    es = 2 if cfg.dtype == "bf16" else 4
+    es = 2 if W.is16(cfg.dtype) else 4
     attn_gbs = refb["attn_bytes"] / t_attn / 1e9
-    peak_tf = BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else FP32_PEAK_TFLOPS
+    peak_tf = BF16_PEAK_TFLOPS if W.is16(cfg.dtype) else FP32_PEAK_TFLOPS  # fp16 dense MFMA peak = bf16's
     mfma_pct = refb["attn_flops"] / t_attn / 1e12 / peak_tf * 100
     traffic = load_traffic(cfg.name)
     roofline = {"bound": "hbm", "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -67,7 +67,7 @@ typedef enum {
   TV_EHIP = 5           /* a HIP runtime call failed; see tv_last_error()        */
 } tv_status;
 
-typedef enum { TV_F32 = 0, TV_BF16 = 1 } tv_dtype;
+typedef enum { TV_F32 = 0, TV_BF16 = 1, TV_F16 = 2 } tv_dtype;
 
 /* Static text for a status code; never NULL. */
 const char* tv_status_string(int status);
@@ -116,7 +116,9 @@ int tree_validate_host(int n, const int32_t* parent, const int32_t* depth);
  *     block_table [B][max_blocks] int32
  *   anc_mask [B][n][W] from tree_build;  lse [B][n][Hq] float (may be NULL).
  *
- * Supported: dtype TV_BF16 (fp32 accumulation, bf16 output) or TV_F32;
+ * Supported: dtype TV_BF16 or TV_F16 (fp32 accumulation; the probabilities
+ * entering the PV product and the output are rounded to the same 16-bit type;
+ * FP16 is the precision of the explainer's implementation points) or TV_F32;
  * D in {64, 128}; Hq % Hkv == 0; 1 <= n <= TV_NMAX; Lmax % 16 == 0.
  * 0 <= prefix_len[b] <= capacity (Lmax, or max_blocks*16); paged block ids in
  * [0, num_blocks).  Out-of-range device values are not trusted: a length is
@@ -153,7 +155,7 @@ int tree_attention(const tv_attn_desc* desc, const void* q,
 /* ---------------------------------------------------------------------------
  * tree_verify_greedy: greedy verification of the token tree.
  *
- *   logits  [B][n][V]  logits_dtype (TV_BF16 or TV_F32): the target model's
+ *   logits  [B][n][V]  logits_dtype (TV_BF16, TV_F16 or TV_F32): the target model's
  *                      next-token logits after each node
  *   tokens  [B][n] int32  draft token of each node (tokens[b][0] is ignored)
  *   parent  [B][n] int32  as for tree_build (assumed valid)

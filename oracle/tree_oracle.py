@@ -72,9 +72,11 @@ PAGE = 16
 
 # ----------------------------------------------------------------------------- values
 def to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
-    """Stored values -> float64.  bf16 arrays are raw uint16 bit patterns."""
+    """Stored values -> float64.  bf16 and f16 arrays are raw uint16 bit patterns."""
     if dtype == "bf16":
         return (np.asarray(a).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    if dtype == "f16":
+        return np.asarray(a, dtype=np.uint16).view(np.float16).astype(np.float64)
     return np.asarray(a, dtype=np.float32).astype(np.float64)
 
 

@@ -194,3 +194,8 @@ def test_construction_argument_errors(lib):
     assert mg(2, 3, 8, 0) == tv.TV_EINVAL
     assert mg(2, 3, 8, 64, ptrs=[None] * 9) == tv.TV_EINVAL
     assert mg(0, 3, 8, 64, ptrs=[None] * 9) == tv.TV_OK
+
+
+def test_f16_descriptor_plans_like_bf16():
+    for kw in (dict(), dict(B=32, n=32, Hq=64, Hkv=8, paged=True, max_blocks=2048, num_blocks=41000)):
+        assert tv.workspace_size(desc(dtype=tv.TV_F16, **kw)) == tv.workspace_size(desc(dtype=tv.TV_BF16, **kw))

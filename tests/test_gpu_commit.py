@@ -44,13 +44,13 @@ def random_paths(w, rng):
 
 def raw(t):
     """Device cache -> host array of its raw bits (NaN patterns compare equal)."""
-    if t.dtype == torch.bfloat16:
+    if t.dtype in (torch.bfloat16, torch.float16):
         return t.view(torch.int16).cpu().numpy().view(np.uint16)
     return t.cpu().numpy().view(np.uint32)
 
 
 def bits(a, dtype):
-    return a.view(np.uint16) if dtype == "bf16" else a.view(np.uint32)
+    return a.view(np.uint16) if dtype in ("bf16", "f16") else a.view(np.uint32)
 
 
 def commit_and_check(w, path, plen, d=None):
@@ -79,6 +79,7 @@ CASES = {
     "fp32_d64": W.config(1, B=3, L_lo=3, L_hi=100),
     "fp32_paged": W.config(4, B=2, dtype="f32", L_lo=30, L_hi=70, n=12, vocab=0),
     "bf16_d64_paged": W.config(4, B=3, D=64, L_lo=40, L_hi=150, vocab=0),
+    "f16_paged": W.config(4, B=3, dtype="f16", L_lo=40, L_hi=150, vocab=0),
 }
 
 

@@ -4,7 +4,11 @@ Integers (masks, positions, statuses, argmax indices, accepted paths, bonus
 tokens) must match bit for bit.  Attention outputs must match within the stated
 tolerance: max |O - O_ref| <= 1e-4 for fp32 workloads and <= 2e-2 for bf16
 (fp32 accumulation, bf16 output); the error relative to max |O_ref| is also
-bounded (1e-5 / 1e-2) so that small outputs cannot hide a wrong kernel.  The
+bounded (1e-5 / 1e-2) so that small outputs cannot hide a wrong kernel.  fp16
+(the explainer's precision) takes 4e-3 / 2e-3, derived from its rounding: the
+inputs decode exactly, fp16 products are exact in fp32 accumulation, and P and
+O are rounded once each to fp16 (relative 2^-12), so |dO| stays near
+2 * 2^-12 * max|V|, about 2e-3 for N(0,1) values.  The
 "balanced" inputs give the tree keys a large share of the softmax mass, so a
 wrong mask bit or a lost prefix moves the output well past the tolerance, and
 "needle" inputs put a dominant key at the last prefix slot, next to NaN-filled
@@ -22,8 +26,8 @@ from token_tree_verification_02_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"f32": 1e-4, "bf16": 2e-2}
-NTOL = {"f32": 1e-5, "bf16": 1e-2}
+TOL = {"f32": 1e-4, "bf16": 2e-2, "f16": 4e-3}
+NTOL = {"f32": 1e-5, "bf16": 1e-2, "f16": 2e-3}
 
 
 def log(msg):
@@ -83,6 +87,10 @@ SMALL = {
     "merge_L2900_split": W.config(3, B=2, L_lo=2900, L_hi=2900),
     "paged_ragged_split": W.config(4, B=3, L_lo=100, L_hi=3000),
     "wide_w2": W.config(5, B=3, L_lo=1, L_hi=2000, Lmax=2048),
+    "llama_f16": W.config(2, B=2, dtype="f16", L_lo=1000, L_hi=1000),
+    "merge_f16_split": W.config(3, B=2, dtype="f16", L_lo=2900, L_hi=2900),
+    "paged_f16": W.config(4, B=3, dtype="f16", L_lo=100, L_hi=3000),
+    "d64_f16_chunks": W.config(2, B=1, D=64, dtype="f16", L_lo=9000, L_hi=9000, Lmax=9008, vocab=0),
 }
 
 

@@ -16,7 +16,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libtreeverify.so")
 
 TV_OK, TV_EINVAL, TV_ETOPOLOGY, TV_EUNSUPPORTED, TV_EWORKSPACE, TV_EHIP = range(6)
-TV_F32, TV_BF16 = 0, 1
+TV_F32, TV_BF16, TV_F16 = 0, 1, 2
 TV_NMAX, TV_PAGE, TV_MSS_VMAX, TV_TOPK_MAX, TV_MERGE_MMAX = 256, 16, 1 << 20, 16, 64
 
 _c_int, _c_float, _vp, _size_t = ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
@@ -97,6 +97,8 @@ def _stream(stream):
 def _dtype_code(t) -> int:
     if t.dtype == torch.bfloat16:
         return TV_BF16
+    if t.dtype == torch.float16:
+        return TV_F16
     if t.dtype == torch.float32:
         return TV_F32
     raise ValueError(f"unsupported dtype {t.dtype}")

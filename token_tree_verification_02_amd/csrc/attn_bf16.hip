@@ -1,4 +1,4 @@
-// Tree attention for bf16 inputs on CDNA4 (gfx950): prefix phase, tree phase and
+// Tree attention for bf16 or fp16 inputs on CDNA4 (gfx950): prefix phase, tree phase and
 // their online-softmax combination in one kernel, with MFMA for both contractions.
 //
 // What is computed (SpecInfer explainer, token-tree structure section, attention
@@ -17,14 +17,14 @@
 // per-lane addresses, and lanes whose key lies past the prefix (or whose block
 // id is bad) fetch a zero page, so NaN-filled unused cache slots are never read.
 //
-// Matrix cores (v_mfma_f32_32x32x16_bf16, 64-wide waves), one 32-query block per
+// Matrix cores (v_mfma_f32_32x32x16_bf16 or _f16, 64-wide waves), one 32-query block per
 // wave:
 //   S^T = K * Q^T : A = 32 keys x 16 d (ds_read_b128 from the K tile), B = Q^T in
 //                   registers; a lane holds the scores of ONE query for 16 keys,
 //                   so the softmax max/sum is lane-local plus one lane^32 swap.
 //   O^T = V^T * P^T : A = V^T read with ds_read_b64_tr_b16 (the transposing LDS
 //                   read of gfx950) straight from the token-major V tile, B = P^T
-//                   from the score registers after bf16 rounding.
+//                   from the score registers after rounding to the 16-bit type.
 //   The QK^T products of a tile's key blocks run as independent accumulator
 //   chains stepped together, so back-to-back MFMAs do not wait on each other;
 //   the softmax and PV product then go block by block.
@@ -78,10 +78,12 @@ __device__ __forceinline__ uint32_t pick32(uint64_t w0, uint64_t w1, uint64_t w2
   return (half & 1) ? (uint32_t)(x >> 32) : (uint32_t)x;
 }
 
-template <int D, int RB, int KS, int TK, int S>
+template <bool F16, int D, int RB, int KS, int TK, int S>
 __global__ __launch_bounds__(64 * RB * KS) void attn_bf16_kernel(AttnArgs a, int rsplit, int nchunks,
                                                                  int chunk_len, int cap) {
   using C = Cfg<D, RB, KS, TK, S>;
+  using E = Elt<F16>;
+  using V8 = typename E::V8;
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -221,7 +223,7 @@ __global__ __launch_bounds__(64 * RB * KS) void attn_bf16_kernel(AttnArgs a, int
   // ---- this lane's query column: operand registers and ancestor mask
   const int qrow = rs * 32 * RB + 32 * rb + col;
   const bool qvalid = qrow < rows;
-  bf16x8 qop[C::SD];
+  V8 qop[C::SD];
   uint64_t mw0 = 0, mw1 = 0, mw2 = 0, mw3 = 0;
   {
     const int u = qvalid ? qrow / G : 0, gi = qvalid ? qrow % G : 0;
@@ -230,7 +232,7 @@ __global__ __launch_bounds__(64 * RB * KS) void attn_bf16_kernel(AttnArgs a, int
     for (int sd = 0; sd < C::SD; ++sd) {
       u32x4 v = {0, 0, 0, 0};
       if (qvalid) v = *(const u32x4*)(qp + 16 * sd + 8 * hh);
-      qop[sd] = __builtin_bit_cast(bf16x8, v);
+      qop[sd] = __builtin_bit_cast(V8, v);
     }
     if (qvalid) {
       const uint64_t* mp = a.mask + ((size_t)b * n + u) * a.W;
@@ -302,12 +304,12 @@ __global__ __launch_bounds__(64 * RB * KS) void attn_bf16_kernel(AttnArgs a, int
         if constexpr (C::KB > 1) {
 #pragma unroll
           for (int kb = 0; kb < C::KB; ++kb) {
-            const bf16x8 kop = *(const bf16x8 AS3*)(Kr + kb * 32 * C::ROWB + kofs[sd]);
-            Sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[sd], Sacc[kb], 0, 0, 0);
+            const V8 kop = *(const V8 AS3*)(Kr + kb * 32 * C::ROWB + kofs[sd]);
+            Sacc[kb] = E::mfma(kop, qop[sd], Sacc[kb]);
           }
         } else {
-          const bf16x8 kop = *(const bf16x8 AS3*)(Kr + kofs[sd]);
-          Sacc[sd & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[sd], Sacc[sd & 1], 0, 0, 0);
+          const V8 kop = *(const V8 AS3*)(Kr + kofs[sd]);
+          Sacc[sd & 1] = E::mfma(kop, qop[sd], Sacc[sd & 1]);
         }
       }
       if constexpr (C::KB == 1) {
@@ -352,12 +354,12 @@ __global__ __launch_bounds__(64 * RB * KS) void attn_bf16_kernel(AttnArgs a, int
           m_run = m_new;
         }
         const float msub = (m_run == -INFINITY) ? 0.f : m_run;
-        bf16x8 pop[2];
+        V8 pop[2];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(Scur[r], sl2, -msub));
           lsum += p;
-          pop[r >> 3][r & 7] = (__bf16)p;
+          pop[r >> 3][r & 7] = E::cvt(p);
         }
 #pragma unroll
         for (int half = 0; half < 2; ++half)
@@ -367,8 +369,7 @@ __global__ __launch_bounds__(64 * RB * KS) void attn_bf16_kernel(AttnArgs a, int
             const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 AS3*)vp);
             const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 AS3*)(vp + 4 * C::ROWB));
             const s16x8 v8 = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-            O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v8), pop[half], O[db], 0,
-                                                            0, 0);
+            O[db] = E::mfma(__builtin_bit_cast(V8, v8), pop[half], O[db]);
           }
       }
     }
@@ -418,9 +419,8 @@ __global__ __launch_bounds__(64 * RB * KS) void attn_bf16_kernel(AttnArgs a, int
       for (int rq = 0; rq < 4; ++rq) {
         const int d0 = 32 * db + 8 * rq + 4 * hh;
         uint2 w;
-        w.x = (uint32_t)f32_to_bf16(O[db][4 * rq] * inv) | ((uint32_t)f32_to_bf16(O[db][4 * rq + 1] * inv) << 16);
-        w.y = (uint32_t)f32_to_bf16(O[db][4 * rq + 2] * inv) |
-              ((uint32_t)f32_to_bf16(O[db][4 * rq + 3] * inv) << 16);
+        w.x = E::bits(O[db][4 * rq] * inv) | (E::bits(O[db][4 * rq + 1] * inv) << 16);
+        w.y = E::bits(O[db][4 * rq + 2] * inv) | (E::bits(O[db][4 * rq + 3] * inv) << 16);
         *(uint2*)(op + d0) = w;
       }
     if (a.lse != nullptr && hh == 0) a.lse[(size_t)(b * n + u) * a.Hq + h] = (m_run + __log2f(ltot)) * kLn2;
@@ -445,8 +445,12 @@ template <int D, int RB, int KS, int TK, int S>
 hipError_t launch_cfg(const AttnArgs& a, const AttnPlan& p, hipStream_t s) {
   const int grid = a.B * a.Hkv * p.nchunks * p.rsplit;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((attn_bf16_kernel<D, RB, KS, TK, S>), dim3(grid), dim3(64 * RB * KS), 0, s, a, p.rsplit,
-                     p.nchunks, p.chunk_len, p.cap);
+  if (a.f16)
+    hipLaunchKernelGGL((attn_bf16_kernel<true, D, RB, KS, TK, S>), dim3(grid), dim3(64 * RB * KS), 0, s, a, p.rsplit,
+                       p.nchunks, p.chunk_len, p.cap);
+  else
+    hipLaunchKernelGGL((attn_bf16_kernel<false, D, RB, KS, TK, S>), dim3(grid), dim3(64 * RB * KS), 0, s, a,
+                       p.rsplit, p.nchunks, p.chunk_len, p.cap);
   return hipGetLastError();
 }
 

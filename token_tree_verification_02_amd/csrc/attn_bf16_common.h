@@ -15,6 +15,43 @@ typedef short s16x8 __attribute__((ext_vector_type(8)));
 
 constexpr float kTau = 8.0f;  // lazy-rescale threshold in the log2 domain
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// The 16-bit element type of q, K, V, out and of the P operand: bf16 or fp16
+// (the explainer's implementation points run everything in FP16).  Both use the
+// same 16-bit data paths (DMA, LDS layouts, transposing reads); only the matrix
+// instruction, the roundings and the row-sum dot product differ.
+template <bool F16>
+struct Elt;
+template <>
+struct Elt<false> {
+  typedef __bf16 T;
+  typedef bf16x8 V8;
+  typedef bf16x2 V2;
+  static __device__ __forceinline__ f32x16 mfma(V8 a, V8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ T cvt(float x) { return (__bf16)x; }
+  static __device__ __forceinline__ uint32_t bits(float x) { return f32_to_bf16(x); }
+  static __device__ __forceinline__ float dot2(V2 a, V2 b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(a, b, c, false);
+  }
+};
+template <>
+struct Elt<true> {
+  typedef _Float16 T;
+  typedef f16x8 V8;
+  typedef f16x2 V2;
+  static __device__ __forceinline__ f32x16 mfma(V8 a, V8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ T cvt(float x) { return (_Float16)x; }
+  static __device__ __forceinline__ uint32_t bits(float x) { return __builtin_bit_cast(uint16_t, (_Float16)x); }
+  static __device__ __forceinline__ float dot2(V2 a, V2 b, float c) { return __builtin_amdgcn_fdot2(a, b, c, false); }
+};
+
 __device__ __forceinline__ int perm_row(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
 
 // Granule swizzles (16-byte granules within a token row of the tile).

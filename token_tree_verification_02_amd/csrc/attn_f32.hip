@@ -139,7 +139,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a, int cap) {
 }
 
 // One thread per (row, 4 head-dim entries) of a (sequence, KV head).
-template <bool BF16OUT>
+template <int OUT>  // tv_dtype of the output
 __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a, int nchunks, int chunk_len, int cap,
                                                     int row_blocks) {
   const int D = a.D, rows = a.n * a.G;
@@ -174,10 +174,16 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a, int nchunks, int
   const float inv = 1.f / lt;
   const int u = row / a.G, gi = row % a.G, h = g * a.G + gi;
   const size_t oi = ((size_t)(b * a.n + u) * a.Hq + h) * D + d0;
-  if (BF16OUT) {
+  if (OUT == TV_BF16) {
     uint2 w;
     w.x = (uint32_t)f32_to_bf16(acc.x * inv) | ((uint32_t)f32_to_bf16(acc.y * inv) << 16);
     w.y = (uint32_t)f32_to_bf16(acc.z * inv) | ((uint32_t)f32_to_bf16(acc.w * inv) << 16);
+    *(uint2*)((uint16_t*)a.out + oi) = w;
+  } else if (OUT == TV_F16) {
+    const auto h = [](float x) { return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x); };
+    uint2 w;
+    w.x = h(acc.x * inv) | (h(acc.y * inv) << 16);
+    w.y = h(acc.z * inv) | (h(acc.w * inv) << 16);
     *(uint2*)((uint16_t*)a.out + oi) = w;
   } else {
     *(float4*)((float*)a.out + oi) = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
@@ -197,16 +203,19 @@ hipError_t launch_attn_f32(const AttnArgs& a, const AttnPlan& p, hipStream_t s) 
   return hipGetLastError();
 }
 
-hipError_t launch_merge(const AttnArgs& a, const AttnPlan& p, bool bf16_out, hipStream_t s) {
+hipError_t launch_merge(const AttnArgs& a, const AttnPlan& p, int out_dtype, hipStream_t s) {
   if (p.nchunks <= 1 || a.B == 0) return hipSuccess;
   const int rpb = 256 / (a.D / 4);
   const int row_blocks = (p.rows + rpb - 1) / rpb;
   const int grid = a.B * a.Hkv * row_blocks;
-  if (bf16_out)
-    hipLaunchKernelGGL(merge_kernel<true>, dim3(grid), dim3(256), 0, s, a, p.nchunks, p.chunk_len, p.cap,
+  if (out_dtype == TV_BF16)
+    hipLaunchKernelGGL(merge_kernel<TV_BF16>, dim3(grid), dim3(256), 0, s, a, p.nchunks, p.chunk_len, p.cap,
+                       row_blocks);
+  else if (out_dtype == TV_F16)
+    hipLaunchKernelGGL(merge_kernel<TV_F16>, dim3(grid), dim3(256), 0, s, a, p.nchunks, p.chunk_len, p.cap,
                        row_blocks);
   else
-    hipLaunchKernelGGL(merge_kernel<false>, dim3(grid), dim3(256), 0, s, a, p.nchunks, p.chunk_len, p.cap,
+    hipLaunchKernelGGL(merge_kernel<TV_F32>, dim3(grid), dim3(256), 0, s, a, p.nchunks, p.chunk_len, p.cap,
                        row_blocks);
   return hipGetLastError();
 }

@@ -1,4 +1,4 @@
-// Tree attention for bf16 inputs with many query rows per KV head (GQA groups
+// Tree attention for bf16 or fp16 inputs with many query rows per KV head (GQA groups
 // times tree nodes > 128): a persistent, load-balanced variant of the fused
 // prefix + tree kernel.
 //
@@ -46,7 +46,6 @@ constexpr int kTK = 64;  // keys per tile
 #define TV_SK_QB 1
 #endif
 constexpr int kSkQB = TV_SK_QB;  // 32-row query blocks per wave (256 rows per workgroup)
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __attribute__((aligned(4096))) uint4 sk_zero_page[256];
 
@@ -184,17 +183,19 @@ __device__ __forceinline__ float sk_colmax(const f32x16& s) {
 }
 
 // Probabilities of 16 scores against the running max (log2 domain), rounded to
-// bf16 (the PV operand); their sum is added to l with a bf16 dot product.
-__device__ __forceinline__ void sk_probs(const f32x16& s, bf16x8 (&P)[2], float& l, float sl2, float msub) {
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+// the 16-bit type (the PV operand); their sum is added to l with a 16-bit dot
+// product.
+template <class E>
+__device__ __forceinline__ void sk_probs(const f32x16& s, typename E::V8 (&P)[2], float& l, float sl2, float msub) {
+  const typename E::V2 ones = {E::cvt(1.0f), E::cvt(1.0f)};
 #pragma unroll
   for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
-      bf16x2 pr;
-      pr[0] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * h2 + e], sl2, -msub));
-      pr[1] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * h2 + e + 1], sl2, -msub));
-      l = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l, false);
+      typename E::V2 pr;
+      pr[0] = E::cvt(__builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * h2 + e], sl2, -msub)));
+      pr[1] = E::cvt(__builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * h2 + e + 1], sl2, -msub)));
+      l = E::dot2(pr, ones, l);
       P[h2][e] = pr[0];
       P[h2][e + 1] = pr[1];
     }
@@ -218,33 +219,34 @@ __device__ __forceinline__ void sk_rescale(f32x16 (&Oq)[D / 32], float& m_run, f
 
 // O^T += V^T P^T for one 32-key block: each V operand (two transposing LDS
 // reads) feeds all QB query blocks.
-template <int D, int QB>
-__device__ __forceinline__ void sk_pv(const char AS3* Vr, int kb, const bf16x8 (&P)[QB][2], f32x16 (&O)[QB][D / 32],
+template <class E, int D, int QB>
+__device__ __forceinline__ void sk_pv(const char AS3* Vr, int kb, const typename E::V8 (&P)[QB][2],
+                                      f32x16 (&O)[QB][D / 32],
                                       const uint32_t (&vofs)[D / 32]) {
   constexpr int DB = D / 32, ROWB = 2 * D;
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
-    bf16x8 vop[DB];  // the half block's operand reads first, then its products
+    typename E::V8 vop[DB];  // the half block's operand reads first, then its products
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       const char AS3* vp = Vr + (kb * 32 + 16 * half) * ROWB + vofs[db];
       const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 AS3*)vp);
       const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 AS3*)(vp + 4 * ROWB));
-      vop[db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      vop[db] = __builtin_bit_cast(typename E::V8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
-        O[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[db], P[qb][half], O[qb][db], 0, 0, 0);
+        O[qb][db] = E::mfma(vop[db], P[qb][half], O[qb][db]);
   }
 }
 
 // S^T = K Q^T for one 32-key block and all QB query blocks (each K operand read
 // once for all of them).
-template <int D, int QB>
-__device__ __forceinline__ void sk_qk(const char AS3* Kr, int kb, const bf16x8 (&qop)[QB][D / 16],
+template <class E, int D, int QB>
+__device__ __forceinline__ void sk_qk(const char AS3* Kr, int kb, const typename E::V8 (&qop)[QB][D / 16],
                                       const uint32_t (&kofs)[D / 16], f32x16 (&Sa)[QB]) {
   constexpr int SD = D / 16, ROWB = 2 * D;
 #pragma unroll
@@ -253,15 +255,15 @@ __device__ __forceinline__ void sk_qk(const char AS3* Kr, int kb, const bf16x8 (
     for (int r = 0; r < 16; ++r) Sa[qb][r] = 0.f;
   // all operand reads of the block first (they pipeline in the LDS), then the
   // products: the scheduler may not pair each read with its product
-  bf16x8 kop[SD];
+  typename E::V8 kop[SD];
 #pragma unroll
-  for (int sd = 0; sd < SD; ++sd) kop[sd] = *(const bf16x8 AS3*)(Kr + kb * 32 * ROWB + kofs[sd]);
+  for (int sd = 0; sd < SD; ++sd) kop[sd] = *(const typename E::V8 AS3*)(Kr + kb * 32 * ROWB + kofs[sd]);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int sd = 0; sd < SD; ++sd)
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
-      Sa[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[sd], qop[qb][sd], Sa[qb], 0, 0, 0);
+      Sa[qb] = E::mfma(kop[sd], qop[qb][sd], Sa[qb]);
 }
 
 // One 64-key tile for one wave holding QB 32-row query blocks.  MASKED: key
@@ -272,8 +274,9 @@ __device__ __forceinline__ void sk_qk(const char AS3* Kr, int kb, const bf16x8 (
 //   QB == 2 (one wave per SIMD): QK of both key blocks first, ONE max check per
 //     tile, then softmax and PV of both blocks as one branch-free stretch that
 //     the scheduler can overlap.
-template <int D, int QB, bool MASKED>
-__device__ __forceinline__ void sk_tile(const char AS3* Kr, const char AS3* Vr, const bf16x8 (&qop)[QB][D / 16],
+template <class E, int D, int QB, bool MASKED>
+__device__ __forceinline__ void sk_tile(const char AS3* Kr, const char AS3* Vr,
+                                        const typename E::V8 (&qop)[QB][D / 16],
                                         f32x16 (&O)[QB][D / 32], float (&m_run)[QB], float (&lsum)[QB],
                                         const uint32_t (&kofs)[D / 16], const uint32_t (&vofs)[D / 32], float sl2,
                                         int lim, bool tree, const uint64_t (&bits)[QB], int hh) {
@@ -282,21 +285,21 @@ __device__ __forceinline__ void sk_tile(const char AS3* Kr, const char AS3* Vr, 
     // matrix core while block 0's softmax executes on the VALU (in-flight MFMAs
     // overlap later independent instructions, across the rescale branch too).
     f32x16 Sa[2][1];
-    sk_qk<D, 1>(Kr, 0, qop, kofs, Sa[0]);
-    sk_qk<D, 1>(Kr, 1, qop, kofs, Sa[1]);
+    sk_qk<E, D, 1>(Kr, 0, qop, kofs, Sa[0]);
+    sk_qk<E, D, 1>(Kr, 1, qop, kofs, Sa[1]);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       if constexpr (MASKED) sk_mask(Sa[kb][0], kb, lim, tree, bits[0], hh);
       const float mx = sk_colmax(Sa[kb][0]) * sl2;  // scale > 0 commutes with max
       if (__builtin_expect(__any(mx > m_run[0] + kTau), 0)) sk_rescale<D>(O[0], m_run[0], lsum[0], mx);
-      bf16x8 P[1][2];
-      sk_probs(Sa[kb][0], P[0], lsum[0], sl2, (m_run[0] == -INFINITY) ? 0.f : m_run[0]);
-      sk_pv<D, 1>(Vr, kb, P, O, vofs);
+      typename E::V8 P[1][2];
+      sk_probs<E>(Sa[kb][0], P[0], lsum[0], sl2, (m_run[0] == -INFINITY) ? 0.f : m_run[0]);
+      sk_pv<E, D, 1>(Vr, kb, P, O, vofs);
     }
   } else {
     f32x16 Sa[2][QB];  // [key block][query block]
-    sk_qk<D, QB>(Kr, 0, qop, kofs, Sa[0]);
-    sk_qk<D, QB>(Kr, 1, qop, kofs, Sa[1]);
+    sk_qk<E, D, QB>(Kr, 0, qop, kofs, Sa[0]);
+    sk_qk<E, D, QB>(Kr, 1, qop, kofs, Sa[1]);
     float mx[QB];
     bool up = false;
 #pragma unroll
@@ -317,16 +320,17 @@ __device__ __forceinline__ void sk_tile(const char AS3* Kr, const char AS3* Vr, 
     for (int qb = 0; qb < QB; ++qb) msub[qb] = (m_run[qb] == -INFINITY) ? 0.f : m_run[qb];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      bf16x8 P[QB][2];
+      typename E::V8 P[QB][2];
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) sk_probs(Sa[kb][qb], P[qb], lsum[qb], sl2, msub[qb]);
-      sk_pv<D, QB>(Vr, kb, P, O, vofs);
+      for (int qb = 0; qb < QB; ++qb) sk_probs<E>(Sa[kb][qb], P[qb], lsum[qb], sl2, msub[qb]);
+      sk_pv<E, D, QB>(Vr, kb, P, O, vofs);
     }
   }
 }
 
-template <int D, int QB, int RB, int S>
+template <bool F16, int D, int QB, int RB, int S>
 __global__ __launch_bounds__(64 * RB) void attn_sk_kernel(AttnArgs a, SkArgs k) {
+  using E = Elt<F16>;
   constexpr int RW = 32 * QB * RB;          // query rows per workgroup
   constexpr int ROWB = 2 * D;               // bytes per token row
   constexpr int REG = kTK * ROWB;           // K (or V) region of a stage
@@ -497,7 +501,7 @@ __global__ __launch_bounds__(64 * RB) void attn_sk_kernel(AttnArgs a, SkArgs k) 
     const bool seg_whole = cc.off == 0;
     const int seg_len = min(cc.titem - cc.off, ntiles - it);
     const bool item_end = cc.off + seg_len == cc.titem;
-    bf16x8 qop[QB][SD];
+    typename E::V8 qop[QB][SD];
     uint64_t mw[QB][4];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -509,7 +513,7 @@ __global__ __launch_bounds__(64 * RB) void attn_sk_kernel(AttnArgs a, SkArgs k) 
       for (int sd = 0; sd < SD; ++sd) {
         u32x4 x = {0, 0, 0, 0};
         if (ok) x = *(const u32x4*)(qp + 16 * sd + 8 * hh);
-        qop[qb][sd] = __builtin_bit_cast(bf16x8, x);
+        qop[qb][sd] = __builtin_bit_cast(typename E::V8, x);
       }
       const uint64_t* mp = a.mask + ((size_t)cc.b * n + u) * a.W;
 #pragma unroll
@@ -560,7 +564,7 @@ __global__ __launch_bounds__(64 * RB) void attn_sk_kernel(AttnArgs a, SkArgs k) 
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) bits[qb] = 0ull;
       }
-      sk_tile<D, QB, MASKED>(Kr, Vr, qop, O, m_run, lsum, kofs, vofs, sl2, lim, tree, bits, hh);
+      sk_tile<E, D, QB, MASKED>(Kr, Vr, qop, O, m_run, lsum, kofs, vofs, sl2, lim, tree, bits, hh);
       ++it;
     };
     const int nfull = max(0, min(seg_len, cc.L / kTK - cc.off));  // full prefix tiles come first
@@ -587,10 +591,8 @@ __global__ __launch_bounds__(64 * RB) void attn_sk_kernel(AttnArgs a, SkArgs k) 
           for (int rq = 0; rq < 4; ++rq) {
             const int d0 = 32 * db + 8 * rq + 4 * hh;
             uint2 w;
-            w.x = (uint32_t)f32_to_bf16(O[qb][db][4 * rq] * inv) |
-                  ((uint32_t)f32_to_bf16(O[qb][db][4 * rq + 1] * inv) << 16);
-            w.y = (uint32_t)f32_to_bf16(O[qb][db][4 * rq + 2] * inv) |
-                  ((uint32_t)f32_to_bf16(O[qb][db][4 * rq + 3] * inv) << 16);
+            w.x = E::bits(O[qb][db][4 * rq] * inv) | (E::bits(O[qb][db][4 * rq + 1] * inv) << 16);
+            w.y = E::bits(O[qb][db][4 * rq + 2] * inv) | (E::bits(O[qb][db][4 * rq + 3] * inv) << 16);
             *(uint2*)(op + d0) = w;
           }
         if (a.lse != nullptr && hh == 0)
@@ -624,7 +626,7 @@ __global__ __launch_bounds__(64 * RB) void attn_sk_kernel(AttnArgs a, SkArgs k) 
 
 // Combines the pieces of items that were split between ranges, and reports bad
 // prefix lengths and block ids.  One workgroup per (item, row slice, 64 rows).
-template <bool BF16OUT>
+template <bool F16>
 __global__ __launch_bounds__(256) void sk_merge_kernel(AttnArgs a, SkArgs k, int RW, int chunks) {
   const int D = a.D, rows = a.n * a.G, Hkv = a.Hkv;
   int t = blockIdx.x;
@@ -687,13 +689,12 @@ __global__ __launch_bounds__(256) void sk_merge_kernel(AttnArgs a, SkArgs k, int
     const float inv = 1.f / lt;
     const int u = row / a.G, gi = row % a.G, h = g * a.G + gi;
     const size_t oi = ((size_t)(b * a.n + u) * a.Hq + h) * D + d0;
-    if (BF16OUT) {
+    {
+      using E = Elt<F16>;
       uint2 wv;
-      wv.x = (uint32_t)f32_to_bf16(acc.x * inv) | ((uint32_t)f32_to_bf16(acc.y * inv) << 16);
-      wv.y = (uint32_t)f32_to_bf16(acc.z * inv) | ((uint32_t)f32_to_bf16(acc.w * inv) << 16);
+      wv.x = E::bits(acc.x * inv) | (E::bits(acc.y * inv) << 16);
+      wv.y = E::bits(acc.z * inv) | (E::bits(acc.w * inv) << 16);
       *(uint2*)((uint16_t*)a.out + oi) = wv;
-    } else {
-      *(float4*)((float*)a.out + oi) = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
     }
     if (a.lse != nullptr && d0 == 0) a.lse[(size_t)(b * a.n + u) * a.Hq + h] = (M + log2f(lt)) * kLn2;
   }
@@ -721,16 +722,23 @@ hipError_t launch_attn_sk(const AttnArgs& a, const AttnPlan& p, void* ws, hipStr
                      (int32_t*)ws);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (a.D == 64)
-    hipLaunchKernelGGL((attn_sk_kernel<64, kSkQB, 8 / kSkQB, 4>), dim3(NV * rsplit), dim3(512 / kSkQB), 0, s, a, k);
+  const dim3 grid(NV * rsplit), block(512 / kSkQB);
+  if (a.D == 64 && a.f16)
+    hipLaunchKernelGGL((attn_sk_kernel<true, 64, kSkQB, 8 / kSkQB, 4>), grid, block, 0, s, a, k);
+  else if (a.D == 64)
+    hipLaunchKernelGGL((attn_sk_kernel<false, 64, kSkQB, 8 / kSkQB, 4>), grid, block, 0, s, a, k);
+  else if (a.f16)
+    hipLaunchKernelGGL((attn_sk_kernel<true, 128, kSkQB, 8 / kSkQB, 4>), grid, block, 0, s, a, k);
   else
-    hipLaunchKernelGGL((attn_sk_kernel<128, kSkQB, 8 / kSkQB, 4>), dim3(NV * rsplit), dim3(512 / kSkQB), 0, s, a,
-                       k);
+    hipLaunchKernelGGL((attn_sk_kernel<false, 128, kSkQB, 8 / kSkQB, 4>), grid, block, 0, s, a, k);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int chunks = RW / 64;
-  hipLaunchKernelGGL(sk_merge_kernel<true>, dim3(a.B * a.Hkv * rsplit * chunks), dim3(256), 0, s, a, k, RW,
-                     chunks);
+  if (a.f16)
+    hipLaunchKernelGGL(sk_merge_kernel<true>, dim3(a.B * a.Hkv * rsplit * chunks), dim3(256), 0, s, a, k, RW, chunks);
+  else
+    hipLaunchKernelGGL(sk_merge_kernel<false>, dim3(a.B * a.Hkv * rsplit * chunks), dim3(256), 0, s, a, k, RW,
+                       chunks);
   return hipGetLastError();
 }
 

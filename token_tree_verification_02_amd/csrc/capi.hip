@@ -40,7 +40,8 @@ int check_desc(const tv_attn_desc* d) {
   if (d->Hq < 1 || d->Hkv < 1) return fail(TV_EINVAL, "Hq=%d, Hkv=%d must be >= 1", d->Hq, d->Hkv);
   if (d->Hq % d->Hkv) return fail(TV_EUNSUPPORTED, "Hq=%d is not a multiple of Hkv=%d", d->Hq, d->Hkv);
   if (d->D != 64 && d->D != 128) return fail(TV_EUNSUPPORTED, "head dim %d (supported: 64, 128)", d->D);
-  if (d->dtype != TV_F32 && d->dtype != TV_BF16) return fail(TV_EUNSUPPORTED, "dtype %d", d->dtype);
+  if (d->dtype != TV_F32 && d->dtype != TV_BF16 && d->dtype != TV_F16)
+    return fail(TV_EUNSUPPORTED, "dtype %d", d->dtype);
   if (!(d->scale >= 0.f) || isinf(d->scale)) return fail(TV_EINVAL, "scale must be finite and >= 0");
   if (d->paged != 0 && d->paged != 1) return fail(TV_EINVAL, "paged must be 0 or 1");
   if (d->paged) {
@@ -216,6 +217,7 @@ int tree_attention(const tv_attn_desc* desc, const void* q, const void* k_cache,
   a.Lmax = desc->Lmax;
   a.max_blocks = desc->max_blocks;
   a.num_blocks = desc->num_blocks;
+  a.f16 = desc->dtype == TV_F16;
   const float scale = desc->scale > 0.f ? desc->scale : 1.f / sqrtf((float)desc->D);
   a.scale_log2 = scale * tv::kLog2e;
   a.ws_o = nullptr;
@@ -231,10 +233,10 @@ int tree_attention(const tv_attn_desc* desc, const void* q, const void* k_cache,
   if (p.sk_nv > 0)
     e = tv::launch_attn_sk(a, p, workspace, s);
   else
-    e = desc->dtype == TV_BF16 ? tv::launch_attn_bf16(a, p, s) : tv::launch_attn_f32(a, p, s);
+    e = desc->dtype != TV_F32 ? tv::launch_attn_bf16(a, p, s) : tv::launch_attn_f32(a, p, s);
   if (e != hipSuccess) return hip_fail(e, "tree_attention launch");
-  if (desc->dtype == TV_BF16 && p.sk_nv == 0 && p.nchunks > 1) {
-    e = tv::launch_merge(a, p, true, s);
+  if (desc->dtype != TV_F32 && p.sk_nv == 0 && p.nchunks > 1) {
+    e = tv::launch_merge(a, p, desc->dtype, s);
     if (e != hipSuccess) return hip_fail(e, "tree_attention merge launch");
   }
   return TV_OK;
@@ -246,13 +248,13 @@ int tree_verify_greedy(int B, int n, int V, int logits_dtype, const void* logits
   if (B < 0) return fail(TV_EINVAL, "B=%d < 0", B);
   if (n < 1 || n > TV_NMAX) return fail(TV_EINVAL, "n=%d outside [1, %d]", n, TV_NMAX);
   if (V < 1) return fail(TV_EINVAL, "V=%d < 1", V);
-  if (logits_dtype != TV_F32 && logits_dtype != TV_BF16)
+  if (logits_dtype != TV_F32 && logits_dtype != TV_BF16 && logits_dtype != TV_F16)
     return fail(TV_EUNSUPPORTED, "logits dtype %d", logits_dtype);
   if ((long long)B * n > 0x7fffffffLL) return fail(TV_EINVAL, "B*n too large");
   if (B == 0) return TV_OK;
   if (!logits || !tokens || !parent || !argmax_out || !path_out || !path_len || !bonus)
     return fail(TV_EINVAL, "null pointer argument");
-  hipError_t e = tv::launch_verify(B, n, V, logits_dtype == TV_BF16, logits, tokens, parent, argmax_out, path_out,
+  hipError_t e = tv::launch_verify(B, n, V, logits_dtype, logits, tokens, parent, argmax_out, path_out,
                                    path_len, bonus, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "tree_verify_greedy launch");
   return TV_OK;

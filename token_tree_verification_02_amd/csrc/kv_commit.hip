@@ -80,7 +80,7 @@ hipError_t launch_commit(const tv_attn_desc* d, void* kc, void* vc, const int32_
                          const void* kt, const void* vt, const int32_t* path, const int32_t* path_len,
                          int32_t* new_len, int32_t* status, hipStream_t s) {
   if (d->B == 0) return hipSuccess;
-  const int es = d->dtype == TV_BF16 ? 2 : 4;
+  const int es = d->dtype == TV_F32 ? 4 : 2;
   const int rowv = d->D * es / 16;  // 8, 16 or 32
   const int row_shift = __builtin_ctz(rowv);
   hipLaunchKernelGGL(commit_kernel, dim3(d->B * d->n), dim3(256), 0, s, d->n, d->Hkv, row_shift, d->paged,

@@ -86,14 +86,26 @@ __device__ __forceinline__ bool beats(float v2, int i2, float v1, int i1) {
 // vector whose maximum beats its running best, and at the end re-reads that one
 // vector (a cache hit) to find the lowest index of the maximum inside it; a wave
 // shuffle and an LDS step then reduce (value, index) pairs.
-template <bool BF16>
+// the low / high 16-bit element of a 32-bit word, as float (exact)
+template <int DT>
+__device__ __forceinline__ float lo16(uint32_t w) {
+  return DT == TV_BF16 ? bf16lo(w) : f16_to_f32((uint16_t)w);
+}
+template <int DT>
+__device__ __forceinline__ float hi16(uint32_t w) {
+  return DT == TV_BF16 ? bf16hi(w) : f16_to_f32((uint16_t)(w >> 16));
+}
+
+// DT: tv_dtype of the logits (16-bit types decode exactly to float)
+template <int DT>
 __global__ __launch_bounds__(256) void argmax_kernel(const void* __restrict__ logits, int V,
                                                      int32_t* __restrict__ am) {
-  constexpr int EPV = BF16 ? 8 : 4;  // elements per 16-byte vector
+  constexpr bool W16 = DT != TV_F32;
+  constexpr int EPV = W16 ? 8 : 4;  // elements per 16-byte vector
   constexpr int R = 8;               // vectors in flight per thread
   const size_t row = blockIdx.x;
   const int tid = threadIdx.x;
-  const size_t es = BF16 ? 2 : 4;
+  const size_t es = W16 ? 2 : 4;
   const char* rp = (const char*)logits + row * (size_t)V * es;
   float bv = -INFINITY;
   int bi = INT_MAX;
@@ -112,9 +124,9 @@ __global__ __launch_bounds__(256) void argmax_kernel(const void* __restrict__ lo
       for (int k = 0; k < R; ++k) {
         const int i = base + k * 256 + tid;
         float m;
-        if (BF16) {
-          m = fmaxf(fmaxf(fmaxf(bf16lo(w[k].x), bf16hi(w[k].x)), fmaxf(bf16lo(w[k].y), bf16hi(w[k].y))),
-                    fmaxf(fmaxf(bf16lo(w[k].z), bf16hi(w[k].z)), fmaxf(bf16lo(w[k].w), bf16hi(w[k].w))));
+        if (W16) {
+          m = fmaxf(fmaxf(fmaxf(lo16<DT>(w[k].x), hi16<DT>(w[k].x)), fmaxf(lo16<DT>(w[k].y), hi16<DT>(w[k].y))),
+                    fmaxf(fmaxf(lo16<DT>(w[k].z), hi16<DT>(w[k].z)), fmaxf(lo16<DT>(w[k].w), hi16<DT>(w[k].w))));
         } else {
           m = fmaxf(fmaxf(__uint_as_float(w[k].x), __uint_as_float(w[k].y)),
                     fmaxf(__uint_as_float(w[k].z), __uint_as_float(w[k].w)));
@@ -129,15 +141,15 @@ __global__ __launch_bounds__(256) void argmax_kernel(const void* __restrict__ lo
       const uint4 v = vp[vidx];
       const uint32_t w0 = v.x, w1 = v.y, w2 = v.z, w3 = v.w;
       int e = EPV;
-      if (BF16) {
-        e = bf16hi(w3) == vbest ? 7 : e;
-        e = bf16lo(w3) == vbest ? 6 : e;
-        e = bf16hi(w2) == vbest ? 5 : e;
-        e = bf16lo(w2) == vbest ? 4 : e;
-        e = bf16hi(w1) == vbest ? 3 : e;
-        e = bf16lo(w1) == vbest ? 2 : e;
-        e = bf16hi(w0) == vbest ? 1 : e;
-        e = bf16lo(w0) == vbest ? 0 : e;
+      if (W16) {
+        e = hi16<DT>(w3) == vbest ? 7 : e;
+        e = lo16<DT>(w3) == vbest ? 6 : e;
+        e = hi16<DT>(w2) == vbest ? 5 : e;
+        e = lo16<DT>(w2) == vbest ? 4 : e;
+        e = hi16<DT>(w1) == vbest ? 3 : e;
+        e = lo16<DT>(w1) == vbest ? 2 : e;
+        e = hi16<DT>(w0) == vbest ? 1 : e;
+        e = lo16<DT>(w0) == vbest ? 0 : e;
       } else {
         e = __uint_as_float(w3) == vbest ? 3 : e;
         e = __uint_as_float(w2) == vbest ? 2 : e;
@@ -150,7 +162,7 @@ __global__ __launch_bounds__(256) void argmax_kernel(const void* __restrict__ lo
     done = nv * EPV;
   }
   for (int i = done + tid; i < V; i += 256) {  // unaligned rows and the tail
-    const float x = BF16 ? bf16_to_f32(((const uint16_t*)rp)[i]) : ((const float*)rp)[i];
+    const float x = W16 ? lo16<DT>(((const uint16_t*)rp)[i]) : ((const float*)rp)[i];
     if (x > bv || bi == INT_MAX) {
       bv = x;
       bi = i;
@@ -232,14 +244,16 @@ hipError_t launch_tree_build(int B, int n, const int32_t* parent, const int32_t*
   return hipGetLastError();
 }
 
-hipError_t launch_verify(int B, int n, int V, int bf16, const void* logits, const int32_t* tokens,
+hipError_t launch_verify(int B, int n, int V, int dtype, const void* logits, const int32_t* tokens,
                          const int32_t* parent, int32_t* am, int32_t* path, int32_t* plen, int32_t* bonus,
                          hipStream_t s) {
   if (B == 0) return hipSuccess;
-  if (bf16)
-    hipLaunchKernelGGL(argmax_kernel<true>, dim3(B * n), dim3(256), 0, s, logits, V, am);
+  if (dtype == TV_BF16)
+    hipLaunchKernelGGL(argmax_kernel<TV_BF16>, dim3(B * n), dim3(256), 0, s, logits, V, am);
+  else if (dtype == TV_F16)
+    hipLaunchKernelGGL(argmax_kernel<TV_F16>, dim3(B * n), dim3(256), 0, s, logits, V, am);
   else
-    hipLaunchKernelGGL(argmax_kernel<false>, dim3(B * n), dim3(256), 0, s, logits, V, am);
+    hipLaunchKernelGGL(argmax_kernel<TV_F32>, dim3(B * n), dim3(256), 0, s, logits, V, am);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(walk_kernel, dim3(B), dim3(((n + 63) / 64) * 64), 0, s, n, am, tokens, parent, path, plen,

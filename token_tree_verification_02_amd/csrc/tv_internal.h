@@ -15,6 +15,9 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_floa
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+// fp16 bit pattern -> float (exact)
+__device__ __forceinline__ float f16_to_f32(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
+
 // float -> bf16 bits, round to nearest even (finite inputs; NaN stays NaN)
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   __bf16 h = (__bf16)f;
@@ -53,6 +56,7 @@ struct AttnArgs {
   float* ws_ml;    // [B][Hkv][nchunks][rows][2] running max (log2 domain), sum
   int B, n, Hq, Hkv, G, D, W;
   int paged, Lmax, max_blocks, num_blocks;
+  int f16;           // 16-bit element type: 0 bf16, 1 fp16
   float scale_log2;  // softmax scale * log2(e)
 };
 
@@ -60,7 +64,7 @@ hipError_t launch_attn_bf16(const AttnArgs& a, const AttnPlan& p, hipStream_t s)
 hipError_t launch_attn_f32(const AttnArgs& a, const AttnPlan& p, hipStream_t s);
 size_t sk_sched_bytes(int B, int NV);
 hipError_t launch_attn_sk(const AttnArgs& a, const AttnPlan& p, void* ws, hipStream_t s);
-hipError_t launch_merge(const AttnArgs& a, const AttnPlan& p, bool bf16_out, hipStream_t s);
+hipError_t launch_merge(const AttnArgs& a, const AttnPlan& p, int out_dtype, hipStream_t s);
 hipError_t launch_tree_build(int B, int n, const int32_t* parent, const int32_t* depth,
                              const int32_t* plen, uint64_t* mask, int32_t* pos, int32_t* status,
                              hipStream_t s);
@@ -77,7 +81,7 @@ hipError_t launch_expand(int B, int F, int V, int k, int n_max, int bf16, const 
 hipError_t launch_merge_drafts(int B, int M, int Ld, int n_max, const int32_t* drafts, const int32_t* draft_len,
                                const int32_t* root_token, int32_t* parent, int32_t* depth, int32_t* tokens,
                                int32_t* n_out, int32_t* node_of, int32_t* status, hipStream_t s);
-hipError_t launch_verify(int B, int n, int V, int bf16, const void* logits, const int32_t* tokens,
+hipError_t launch_verify(int B, int n, int V, int dtype, const void* logits, const int32_t* tokens,
                          const int32_t* parent, int32_t* am, int32_t* path, int32_t* plen,
                          int32_t* bonus, hipStream_t s);
 

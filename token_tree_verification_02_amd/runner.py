@@ -11,23 +11,30 @@ import torch
 from . import _lib
 
 
-def _t(a, device, bf16=False):
+def _t(a, device, bf16=False, dtype=None):
+    """Host array -> device tensor; 16-bit types arrive as raw uint16 bits."""
     if a is None:
         return None
     a = np.ascontiguousarray(a)
-    if bf16:
+    if bf16 or dtype == "bf16":
         return torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
+    if dtype == "f16":
+        return torch.from_numpy(a.view(np.int16)).to(device).view(torch.float16)
     return torch.from_numpy(a).to(device)
+
+
+def dtype_code(dtype: str) -> int:
+    return {"f32": _lib.TV_F32, "bf16": _lib.TV_BF16, "f16": _lib.TV_F16}[dtype]
 
 
 def upload(w: dict, device="cuda") -> dict:
     cfg = w["cfg"]
-    bf = cfg.dtype == "bf16"
+    dt = cfg.dtype
     d = dict(cfg=cfg, paged=cfg.paged, num_blocks=int(w.get("num_blocks", 0)))
     for k in ("parent", "depth", "prefix_len", "block_table", "tokens"):
         d[k] = _t(w.get(k), device)
     for k in ("q", "k_cache", "v_cache", "k_tree", "v_tree", "logits"):
-        d[k] = _t(w.get(k), device, bf16=bf)
+        d[k] = _t(w.get(k), device, dtype=dt)
     B, n = cfg.B, cfg.n
     d["mask"] = torch.empty((B, n, (n + 63) // 64), dtype=torch.int64, device=device)
     d["pos"] = torch.empty((B, n), dtype=torch.int32, device=device)
@@ -50,7 +57,7 @@ def upload(w: dict, device="cuda") -> dict:
 
 def attn_desc_of(d):
     cfg = d["cfg"]
-    code = _lib.TV_BF16 if cfg.dtype == "bf16" else _lib.TV_F32
+    code = dtype_code(cfg.dtype)
     if d["paged"]:
         return _lib.attn_desc(cfg.B, cfg.n, cfg.Hq, cfg.Hkv, cfg.D, code, paged=True,
                               max_blocks=d["block_table"].shape[1], num_blocks=d["num_blocks"])
@@ -117,7 +124,7 @@ class Step:
                           P(d["lse"]), P(d["attn_status"]), P(ws), wbytes)
         self.verify_args = None
         if "argmax" in d:
-            code = _lib.TV_BF16 if cfg.dtype == "bf16" else _lib.TV_F32
+            code = dtype_code(cfg.dtype)
             self.verify_args = (cfg.B, cfg.n, cfg.vocab, code, P(d["logits"]), P(d["tokens"]), P(d["parent"]),
                                 P(d["argmax"]), P(d["path"]), P(d["path_len"]), P(d["bonus"]))
 
@@ -187,4 +194,4 @@ def capture_steps(steps) -> "torch.cuda.CUDAGraph":
 
 def out_f64(d) -> np.ndarray:
     o = d["out"]
-    return o.float().double().cpu().numpy() if o.dtype == torch.bfloat16 else o.double().cpu().numpy()
+    return o.float().double().cpu().numpy() if o.dtype in (torch.bfloat16, torch.float16) else o.double().cpu().numpy()

@@ -32,6 +32,7 @@ import numpy as np
 
 PAGE = 16
 BF16_NAN = np.uint16(0x7FC0)
+F16_NAN = np.uint16(0x7E00)
 F32_NAN = np.float32(np.nan)
 
 # stream ids for the counter-keyed generator
@@ -49,7 +50,7 @@ class Config:
     Hq: int
     Hkv: int
     D: int
-    dtype: str          # "f32" or "bf16" (q, k, v, out and logits share it)
+    dtype: str          # "f32", "bf16" or "f16" (q, k, v, out and logits share it)
     L_lo: int           # prefix length range, inclusive
     L_hi: int
     paged: bool
@@ -103,9 +104,23 @@ def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
     return (bits.astype(np.uint32) << 16).view(np.float32)
 
 
+def is16(dtype: str) -> bool:
+    """16-bit types are stored as raw uint16 bit patterns."""
+    return dtype in ("bf16", "f16")
+
+
+def to_f32(a: np.ndarray, dtype: str) -> np.ndarray:
+    """Stored values (raw bits for 16-bit types) -> float32 (exact)."""
+    if dtype == "bf16":
+        return bf16_bits_to_f32(a)
+    if dtype == "f16":
+        return np.asarray(a, dtype=np.uint16).view(np.float16).astype(np.float32)
+    return a
+
+
 def _normal(seed: int, stream: int, count: int, sigma: float, dtype: str) -> np.ndarray:
-    """count N(0, sigma^2) draws, chunked and threaded; uint16 bf16 bits or float32."""
-    out = np.empty(count, dtype=np.uint16 if dtype == "bf16" else np.float32)
+    """count N(0, sigma^2) draws, chunked and threaded; raw uint16 bits (16-bit types) or float32."""
+    out = np.empty(count, dtype=np.uint16 if is16(dtype) else np.float32)
     nchunks = (count + _CHUNK - 1) // _CHUNK
 
     def job(c):
@@ -114,7 +129,7 @@ def _normal(seed: int, stream: int, count: int, sigma: float, dtype: str) -> np.
         x = _rng(seed, stream, c).standard_normal(hi - lo, dtype=np.float32)
         if sigma != 1.0:
             x *= np.float32(sigma)
-        out[lo:hi] = f32_to_bf16_bits(x) if dtype == "bf16" else x
+        out[lo:hi] = _store(x, dtype)
 
     if nchunks <= 1:
         for c in range(nchunks):
@@ -126,12 +141,16 @@ def _normal(seed: int, stream: int, count: int, sigma: float, dtype: str) -> np.
 
 
 def _nan(dtype: str):
-    return BF16_NAN if dtype == "bf16" else F32_NAN
+    return BF16_NAN if dtype == "bf16" else (F16_NAN if dtype == "f16" else F32_NAN)
 
 
 def _store(x: np.ndarray, dtype: str) -> np.ndarray:
     x = np.asarray(x, dtype=np.float32)
-    return f32_to_bf16_bits(x) if dtype == "bf16" else x
+    if dtype == "bf16":
+        return f32_to_bf16_bits(x)
+    if dtype == "f16":
+        return x.astype(np.float16).view(np.uint16)     # round to nearest even
+    return x
 
 
 # ----------------------------------------------------------------------------- trees
@@ -306,7 +325,7 @@ def make(cfg: Config, seed: int | None = None, *, variant: str = "plain", plant:
     kvals = _normal(seed, _S_K, tot_valid * Hkv * D, 1.0, dt)
     vvals = _normal(seed, _S_V, tot_valid * Hkv * D, 1.0, dt)
     offs = np.concatenate([[0], np.cumsum(prefix_len.astype(np.int64))])
-    edt = np.uint16 if dt == "bf16" else np.float32
+    edt = np.uint16 if is16(dt) else np.float32
     if cfg.paged:
         nblk = (prefix_len + room + PAGE - 1) // PAGE
         total_blocks = int(nblk.sum())
@@ -346,9 +365,9 @@ def make(cfg: Config, seed: int | None = None, *, variant: str = "plain", plant:
         out.update(block_table=None, max_blocks=0, num_blocks=0, Lmax=Lmax)
     del kvals, vvals
     if not poison:
-        bad = np.isnan(bf16_bits_to_f32(k_cache) if dt == "bf16" else k_cache)
+        bad = np.isnan(to_f32(k_cache, dt))
         k_cache[bad] = 0
-        bad = np.isnan(bf16_bits_to_f32(v_cache) if dt == "bf16" else v_cache)
+        bad = np.isnan(to_f32(v_cache, dt))
         v_cache[bad] = 0
 
     # ---- variants (input shaping only)
@@ -422,18 +441,18 @@ def make_stochastic(cfg: Config, seed: int | None = None, *, ssm_noise: float = 
     seed = cfg.index if seed is None else seed
     w = make(cfg, seed, plant=False) if w is None else w
     B, n, V, dt = cfg.B, cfg.n, cfg.vocab, cfg.dtype
-    edt = np.uint16 if dt == "bf16" else np.float32
+    edt = np.uint16 if is16(dt) else np.float32
     ssm_st = np.empty((B, n, V), edt)
     tokens = np.zeros((B, n), np.int32)
 
     def one(b):
         rng = _rng(seed, _S_SSM, b)
-        llm = bf16_bits_to_f32(w["logits"][b]) if dt == "bf16" else w["logits"][b]
+        llm = to_f32(w["logits"][b], dt)
         par = np.maximum(w["parent"][b], 0)
         row = llm[par] + rng.standard_normal((n, V), dtype=np.float32) * np.float32(ssm_noise)
         row[0] = 0.0                                 # the root has no draft distribution
         ssm_st[b] = _store(row, dt)
-        rf = bf16_bits_to_f32(ssm_st[b]) if dt == "bf16" else ssm_st[b]
+        rf = to_f32(ssm_st[b], dt)
         e = np.exp((rf - rf.max(axis=1, keepdims=True)).astype(np.float64))
         cdf = np.cumsum(e, axis=1)
         u = rng.random(n) * cdf[:, -1]
@@ -457,7 +476,7 @@ def _plant(cfg: Config, parent, tokens, logits, rng) -> list:
     random draw reaches and tokens[c] = t.  What the method then accepts is left to
     the oracle and the kernels.
     """
-    big = 32.0 if cfg.dtype == "bf16" else 16.0
+    big = 32.0 if cfg.dtype == "bf16" else 16.0   # beyond any draw, exact in the stored type
     V = cfg.vocab
     bigv = _store(np.array([big], np.float32), cfg.dtype)[0]
     records = []
@@ -501,7 +520,7 @@ def _plant(cfg: Config, parent, tokens, logits, rng) -> list:
 def reference_bytes(w: dict) -> dict:
     """Algorithmic byte and flop counts of one pass over this workload."""
     cfg = w["cfg"]
-    es = 2 if cfg.dtype == "bf16" else 4
+    es = 2 if is16(cfg.dtype) else 4
     L = w["prefix_len"].astype(np.int64)
     n, Hq, Hkv, D, B = cfg.n, cfg.Hq, cfg.Hkv, cfg.D, cfg.B
     kv_prefix = int(L.sum()) * Hkv * D * 2 * es
