@@ -77,7 +77,29 @@ def to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
         return (np.asarray(a).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     if dtype == "f16":
         return np.asarray(a, dtype=np.uint16).view(np.float16).astype(np.float64)
+    if dtype == "fp8":
+        return fp8_e4m3_value(a)
     return np.asarray(a, dtype=np.float32).astype(np.float64)
+
+
+def fp8_e4m3_value(codes) -> np.ndarray:
+    """Values of OCP FP8 E4M3 codes (sign, 4 exponent bits with bias 7, 3 mantissa
+    bits; exponent 0 is subnormal; S.1111.111 is NaN; no infinities)."""
+    c = np.asarray(codes).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = (c & 7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * 2.0 ** (e - 7.0))
+    mag = np.where((e == 15) & ((c & 7) == 7), np.nan, mag)
+    return sign * mag
+
+
+def cache_values(w: dict, which: str, rows) -> np.ndarray:
+    """float64 values of cache rows: the stored element type, or fp8 codes times the
+    cache's scale when the cache is fp8."""
+    if w["cfg"].kv == "fp8":
+        return fp8_e4m3_value(rows) * float(w["k_scale" if which == "k" else "v_scale"])
+    return to_f64(rows, w["cfg"].dtype)
 
 
 # ----------------------------------------------------------------------------- topology
@@ -171,7 +193,7 @@ def tree_attention(w: dict, seqs=None, kv_heads=None, scale: float | None = None
         for g in kv_heads:
             Kp, Vp = gather_prefix(w["k_cache"], w["v_cache"], b, g, L, paged=cfg.paged,
                                    block_table=w.get("block_table"))
-            Kp, Vp = to_f64(Kp, dt), to_f64(Vp, dt)
+            Kp, Vp = cache_values(w, "k", Kp), cache_values(w, "v", Vp)
             Kt = to_f64(w["k_tree"][b, :, g, :], dt)            # [n][D]
             Vt = to_f64(w["v_tree"][b, :, g, :], dt)
             heads = range(g * G, (g + 1) * G)

@@ -540,3 +540,38 @@ def test_pins_catch_more_planted_oracle_mistakes(monkeypatch):
     monkeypatch.setattr(oracle, "accept_walk", highest_child)
     with pytest.raises(AssertionError):
         test_duplicate_siblings_lowest_node_wins()
+
+
+# ------------------------------------------------------------------ fp8 KV cache
+def test_fp8_e4m3_decoding_fixed_points():
+    """Values fixed by the OCP FP8 E4M3 format: 1.0, the largest normal (448),
+    the smallest normal (2^-6) and subnormal (2^-9), signed zero, NaN codes,
+    and strict monotonicity of the 126 positive finite codes."""
+    v = oracle.fp8_e4m3_value(np.array([0x38, 0x7E, 0x08, 0x01, 0x00, 0x80, 0xB8, 0x7F, 0xFF, 0x07, 0x40]))
+    assert list(v[:7]) == [1.0, 448.0, 2.0 ** -6, 2.0 ** -9, 0.0, 0.0, -1.0]
+    assert np.isnan(v[7]) and np.isnan(v[8])
+    assert v[9] == 7 * 2.0 ** -9 and v[10] == 2.0
+    pos = oracle.fp8_e4m3_value(np.arange(1, 127))
+    assert (np.diff(pos) > 0).all()
+    np.testing.assert_array_equal(oracle.fp8_e4m3_value(np.arange(128, 255)), -oracle.fp8_e4m3_value(np.arange(0, 127)))
+
+
+def test_fp8_cache_equals_bf16_cache_of_the_same_values():
+    """Every E4M3 value is exact in bf16: an fp8 cache at scale 1 and a bf16 cache
+    holding the decoded values give the same attention; a power-of-two scale
+    multiplies the keys and values exactly."""
+    cfg8 = small(4, n=9, L_lo=20, L_hi=70, kv="fp8")
+    w8 = W.make(cfg8, seed=3, kv_scale=1.0)
+    wb = dict(w8)
+    wb["cfg"] = W.config(4, B=cfg8.B, n=9, L_lo=20, L_hi=70, vocab=0)
+    for k in ("k_cache", "v_cache"):
+        vals = oracle.fp8_e4m3_value(w8[k])
+        wb[k] = W.f32_to_bf16_bits(vals.astype(np.float32))
+    O8, L8 = oracle.tree_attention(w8)
+    Ob, Lb = oracle.tree_attention(wb)
+    np.testing.assert_array_equal(O8, Ob)
+    w2 = dict(w8)
+    w2["k_scale"], w2["v_scale"] = np.float32(0.25), np.float32(0.25)
+    for k in ("k_cache", "v_cache"):
+        wb[k] = W.f32_to_bf16_bits((oracle.fp8_e4m3_value(w8[k]) * 0.25).astype(np.float32))
+    np.testing.assert_array_equal(oracle.tree_attention(w2)[0], oracle.tree_attention(wb)[0])

@@ -60,6 +60,7 @@ class Config:
     vocab: int          # 0 = no verification on this workload
     logit_sigma: float
     Lmax: int = 0       # contiguous cache capacity (0 = L_hi)
+    kv: str = ""        # "" : the cache has `dtype`; "fp8": OCP E4M3 codes times a per-tensor scale
 
     @property
     def G(self) -> int:
@@ -102,6 +103,25 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
 
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
     return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+FP8_NAN = np.uint8(0x7F)
+
+
+def _fp8_table():
+    """Non-negative finite E4M3 values (codes 0..126) in increasing order."""
+    codes = np.arange(127)
+    e, m = codes >> 3, codes & 7
+    return np.where(e == 0, m / 8.0 * 2.0 ** -6, (1 + m / 8.0) * 2.0 ** (e - 7.0))
+
+
+def fp8_encode(x: np.ndarray) -> np.ndarray:
+    """float -> nearest OCP E4M3 code (saturating at 448), as uint8."""
+    tab = _fp8_table()
+    y = np.abs(np.asarray(x, np.float64))
+    mid = (tab[1:] + tab[:-1]) / 2
+    code = np.searchsorted(mid, np.minimum(y, 448.0), side="left").astype(np.uint8)
+    return np.where(np.asarray(x) < 0, code | 0x80, code).astype(np.uint8)
 
 
 def is16(dtype: str) -> bool:
@@ -286,7 +306,7 @@ def children_lists(parent: np.ndarray) -> list[list[int]]:
 
 # ----------------------------------------------------------------------------- workload
 def make(cfg: Config, seed: int | None = None, *, variant: str = "plain", plant: bool = True,
-         poison: bool = True, with_logits: bool = True, room: int = 0) -> dict:
+         poison: bool = True, with_logits: bool = True, room: int = 0, kv_scale: float | None = None) -> dict:
     """Seeded inputs for one workload.
 
     variant:
@@ -299,6 +319,8 @@ def make(cfg: Config, seed: int | None = None, *, variant: str = "plain", plant:
     plant: planted accept paths, duplicate sibling tokens and logit ties (needs vocab).
     room: cache capacity kept free after each prefix, in tokens (NaN-filled), for
           committing accepted tokens; paged sequences get blocks for L_b + room tokens.
+    kv_scale: with an fp8 cache, the scale of both K and V (default: per tensor,
+          max |x| / 440).
     """
     seed = cfg.index if seed is None else seed
     dt = cfg.dtype
@@ -322,18 +344,26 @@ def make(cfg: Config, seed: int | None = None, *, variant: str = "plain", plant:
 
     # ---- prefix cache
     tot_valid = int(prefix_len.sum())
-    kvals = _normal(seed, _S_K, tot_valid * Hkv * D, 1.0, dt)
-    vvals = _normal(seed, _S_V, tot_valid * Hkv * D, 1.0, dt)
+    fp8 = cfg.kv == "fp8"
+    kvals = _normal(seed, _S_K, tot_valid * Hkv * D, 1.0, "f32" if fp8 else dt)
+    vvals = _normal(seed, _S_V, tot_valid * Hkv * D, 1.0, "f32" if fp8 else dt)
+    if fp8:   # per-tensor scales: the largest magnitude maps near the top code (or a given scale)
+        k_scale = kv_scale or max(float(np.abs(kvals).max()) / 440.0, 1e-30) if tot_valid else (kv_scale or 1.0)
+        v_scale = kv_scale or max(float(np.abs(vvals).max()) / 440.0, 1e-30) if tot_valid else (kv_scale or 1.0)
+        kvals = fp8_encode(kvals / k_scale)
+        vvals = fp8_encode(vvals / v_scale)
+        out.update(k_scale=np.float32(k_scale), v_scale=np.float32(v_scale))
     offs = np.concatenate([[0], np.cumsum(prefix_len.astype(np.int64))])
-    edt = np.uint16 if is16(dt) else np.float32
+    edt = np.uint8 if fp8 else (np.uint16 if is16(dt) else np.float32)
+    cnan = FP8_NAN if fp8 else _nan(dt)
     if cfg.paged:
         nblk = (prefix_len + room + PAGE - 1) // PAGE
         total_blocks = int(nblk.sum())
         max_blocks = (cfg.L_hi + room + PAGE - 1) // PAGE
         perm = _rng(seed, _S_PERM).permutation(total_blocks).astype(np.int32)
         bt = np.full((B, max_blocks), -1, np.int32)
-        k_cache = np.full((total_blocks, Hkv, PAGE, D), _nan(dt), edt)
-        v_cache = np.full((total_blocks, Hkv, PAGE, D), _nan(dt), edt)
+        k_cache = np.full((total_blocks, Hkv, PAGE, D), cnan, edt)
+        v_cache = np.full((total_blocks, Hkv, PAGE, D), cnan, edt)
         bo = 0
         for b in range(B):
             L = int(prefix_len[b])
@@ -354,8 +384,8 @@ def make(cfg: Config, seed: int | None = None, *, variant: str = "plain", plant:
         out.update(block_table=bt, max_blocks=max_blocks, num_blocks=total_blocks, Lmax=0)
     else:
         Lmax = max(cfg.capacity, (cfg.L_hi + room + PAGE - 1) // PAGE * PAGE)
-        k_cache = np.full((B, Hkv, Lmax, D), _nan(dt), edt)
-        v_cache = np.full((B, Hkv, Lmax, D), _nan(dt), edt)
+        k_cache = np.full((B, Hkv, Lmax, D), cnan, edt)
+        v_cache = np.full((B, Hkv, Lmax, D), cnan, edt)
         for b in range(B):
             L = int(prefix_len[b])
             kv = kvals[offs[b] * Hkv * D:offs[b + 1] * Hkv * D].reshape(L, Hkv, D)
@@ -365,10 +395,8 @@ def make(cfg: Config, seed: int | None = None, *, variant: str = "plain", plant:
         out.update(block_table=None, max_blocks=0, num_blocks=0, Lmax=Lmax)
     del kvals, vvals
     if not poison:
-        bad = np.isnan(to_f32(k_cache, dt))
-        k_cache[bad] = 0
-        bad = np.isnan(to_f32(v_cache, dt))
-        v_cache[bad] = 0
+        for c in (k_cache, v_cache):
+            c[(c & 0x7F) == 0x7F if fp8 else np.isnan(to_f32(c, dt))] = 0
 
     # ---- variants (input shaping only)
     if variant == "balanced":
@@ -396,7 +424,7 @@ def make(cfg: Config, seed: int | None = None, *, variant: str = "plain", plant:
             j = L - 1
             row = np.zeros(D, np.float32)
             row[0] = kappa
-            val = _store(row, dt)
+            val = fp8_encode(row / out["k_scale"]) if fp8 else _store(row, dt)
             if cfg.paged:
                 blk = out["block_table"][b, j // PAGE]
                 k_cache[blk, :, j % PAGE, :] = val
