@@ -100,6 +100,7 @@ def main():
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--dtype", choices=["bf16", "f16"], default=None,
                     help="element type of q/K/V/out/logits (default: the workload's)")
+    ap.add_argument("--kv", choices=["fp8"], default=None, help="store the prefix KV cache as fp8 (E4M3) codes")
     ap.add_argument("--copies", type=int, default=0, help="input copies to rotate (0 = auto)")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--eager", action="store_true", help="launch each step eagerly instead of replaying a HIP graph")
@@ -130,7 +131,10 @@ def main():
     from token_tree_verification_02_amd import runner
     from token_tree_verification_02_amd import workloads as W
 
-    cfg = W.config(args.config, **({"dtype": args.dtype} if args.dtype else {}))
+    over = {"dtype": args.dtype} if args.dtype else {}
+    if args.kv:
+        over["kv"] = args.kv
+    cfg = W.config(args.config, **over)
     t_gen = time.perf_counter()
     w = W.make(cfg, room=cfg.n)
     # stochastic verification and top-k expansion take bf16 or fp32 logits
@@ -214,10 +218,12 @@ def main():
     steps[0].verify(sh)
     torch.cuda.synchronize()
     committed = int(copies[0]["path_len"].sum().item()) if cfg.vocab else int(hl.sum())
-    t_commit = timed_graph(lambda i, h: steps[i].commit(cargs[i], h))
-    torch.cuda.synchronize()
-    if not (copies[0]["commit_status"] == 0).all().item():
-        raise RuntimeError("tree_commit_kv rejected a sequence of the benchmark batch")
+    t_commit = None
+    if cfg.kv != "fp8":  # committing into an fp8 cache is not supported
+        t_commit = timed_graph(lambda i, h: steps[i].commit(cargs[i], h))
+        torch.cuda.synchronize()
+        if not (copies[0]["commit_status"] == 0).all().item():
+            raise RuntimeError("tree_commit_kv rejected a sequence of the benchmark batch")
     mss_out = None
     if mss is not None:
         def mss_call(i, h):
@@ -318,17 +324,20 @@ def main():
         "metric": METRIC, "value": round(value, 1), "unit": "verified tree tokens/s", "n_gpus": 1,
         "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic (seeded, N(0,1) Q/K/V)",
-        "config": {"workload": cfg.name, "B": cfg.B, "n": cfg.n, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "D": cfg.D,
+        "config": {"workload": cfg.name + ("_fp8kv" if cfg.kv == "fp8" else ""), "B": cfg.B, "n": cfg.n,
+                   "Hq": cfg.Hq, "Hkv": cfg.Hkv, "D": cfg.D, "kv_cache": cfg.kv or cfg.dtype,
                    "prefix_len": [cfg.L_lo, cfg.L_hi], "paged": cfg.paged, "vocab": cfg.vocab,
                    "input_copies": R, "launch": "eager" if args.eager else "hip_graph"},
         "roofline": roofline,
         "attn_hbm_gbs": round(attn_gbs, 1), "mfma_util_pct": round(mfma_pct, 2),
         "kernel_us": {"tree_build": round(t_build * 1e6, 2), "tree_attention": round(t_attn * 1e6, 2),
-                      "tree_verify_greedy": round(t_ver * 1e6, 2), "tree_commit_kv": round(t_commit * 1e6, 2),
+                      "tree_verify_greedy": round(t_ver * 1e6, 2),
+                      "tree_commit_kv": round(t_commit * 1e6, 2) if t_commit else None,
                       "tree_verify_stochastic": mss_out["us"] if mss_out else None},
         "stochastic": mss_out,
         "construct": cons_out,
-        "commit": {"tokens": committed, "hbm_gbs": round(4 * committed * cfg.Hkv * cfg.D * es / t_commit / 1e9, 1)},
+        "commit": ({"tokens": committed, "hbm_gbs": round(4 * committed * cfg.Hkv * cfg.D * es / t_commit / 1e9, 1)}
+                   if t_commit else None),
         "verify_hbm_gbs": round(refb["verify_bytes"] / t_ver / 1e9, 1) if cfg.vocab and t_ver else None,
     }
     if not args.no_cpu_baseline:

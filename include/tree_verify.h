@@ -56,7 +56,7 @@ extern "C" {
 #define TV_NMAX 256     /* max tree nodes per sequence, root included          */
 #define TV_WMAX 4       /* max mask words per node = TV_NMAX / 64               */
 #define TV_PAGE 16      /* tokens per paged KV block                            */
-#define TV_VERSION 1
+#define TV_VERSION 2
 
 typedef enum {
   TV_OK = 0,
@@ -67,7 +67,7 @@ typedef enum {
   TV_EHIP = 5           /* a HIP runtime call failed; see tv_last_error()        */
 } tv_status;
 
-typedef enum { TV_F32 = 0, TV_BF16 = 1, TV_F16 = 2 } tv_dtype;
+typedef enum { TV_F32 = 0, TV_BF16 = 1, TV_F16 = 2, TV_FP8_E4M3 = 3 } tv_dtype;
 
 /* Static text for a status code; never NULL. */
 const char* tv_status_string(int status);
@@ -127,6 +127,14 @@ int tree_validate_host(int n, const int32_t* parent, const int32_t* depth);
  * `status` [B] (may be NULL) is given it reports TV_EINVAL for that sequence
  * (TV_OK otherwise).
  * Cache slots past L_b are never read (they may hold NaN).
+ *
+ * fp8 cache (kv_dtype == TV_FP8_E4M3): the prefix K/V are OCP FP8 E4M3 codes
+ * (1 byte, same layouts) with per-tensor scales; the tree K/V, q and out stay
+ * bf16.  Codes are converted to bf16 (exactly) in LDS before the matrix
+ * products; k_scale joins the score scale and v_scale multiplies the
+ * probabilities entering the PV product.  Supported for bf16
+ * with n * (Hq/Hkv) <= 128 query rows per KV head (else TV_EUNSUPPORTED); an
+ * fp8 cache halves the prefix bytes, which bound those workloads.
  * ------------------------------------------------------------------------- */
 typedef struct {
   int32_t B, n, Hq, Hkv, D;
@@ -137,6 +145,10 @@ typedef struct {
   int32_t Lmax;         /* contiguous: per-sequence capacity (tokens)         */
   int32_t max_blocks;   /* paged: block_table row length                      */
   int32_t num_blocks;   /* paged: physical blocks in the cache                */
+  int32_t kv_dtype;     /* element type of k_cache/v_cache: 0 = dtype, or
+                           TV_FP8_E4M3 (OCP FP8 codes, 1 byte; dtype TV_BF16)  */
+  float k_scale;        /* fp8 cache: a key's value is code * k_scale (> 0)   */
+  float v_scale;        /* fp8 cache: a value's value is code * v_scale (> 0) */
 } tv_attn_desc;
 
 /* Workspace bytes tree_attention needs for this descriptor (0 if none); the

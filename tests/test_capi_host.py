@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported(lib):
 def test_status_strings(lib):
     for code in range(6):
         assert lib.tv_status_string(code).decode()
-    assert lib.tv_version() == 1
+    assert lib.tv_version() == 2
 
 
 def test_host_validation_matches_oracle_on_all_small_trees():
@@ -199,3 +199,15 @@ def test_construction_argument_errors(lib):
 def test_f16_descriptor_plans_like_bf16():
     for kw in (dict(), dict(B=32, n=32, Hq=64, Hkv=8, paged=True, max_blocks=2048, num_blocks=41000)):
         assert tv.workspace_size(desc(dtype=tv.TV_F16, **kw)) == tv.workspace_size(desc(dtype=tv.TV_BF16, **kw))
+
+
+
+def test_fp8_cache_contract(lib):
+    fp8 = dict(kv_dtype=tv.TV_FP8_E4M3, k_scale=0.01, v_scale=0.02)
+    ok = desc(**fp8)                                                     # 21 rows per KV head
+    assert tv.workspace_size(ok) != SIZE_MAX
+    assert call_attn(lib, desc(B=32, n=32, Hq=64, Hkv=8, **fp8)) == tv.TV_EUNSUPPORTED   # 256 rows
+    assert call_attn(lib, desc(dtype=tv.TV_F16, **fp8)) == tv.TV_EUNSUPPORTED
+    assert call_attn(lib, desc(kv_dtype=tv.TV_FP8_E4M3, k_scale=0.0, v_scale=1.0)) == tv.TV_EINVAL
+    assert call_attn(lib, desc(kv_dtype=9)) == tv.TV_EUNSUPPORTED
+    assert call_commit(lib, desc(**fp8)) == tv.TV_EUNSUPPORTED

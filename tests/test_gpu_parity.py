@@ -91,6 +91,14 @@ SMALL = {
     "merge_f16_split": W.config(3, B=2, dtype="f16", L_lo=2900, L_hi=2900),
     "paged_f16": W.config(4, B=3, dtype="f16", L_lo=100, L_hi=3000),
     "d64_f16_chunks": W.config(2, B=1, D=64, dtype="f16", L_lo=9000, L_hi=9000, Lmax=9008, vocab=0),
+    # fp8 (E4M3) prefix cache, every few-row plan shape: rows 21, 64, 96, paged, chunked, D = 64
+    "llama_fp8": W.config(2, B=2, L_lo=1000, L_hi=1000, kv="fp8"),
+    "fp8_rows64_paged": W.config(4, B=3, Hq=16, Hkv=8, L_lo=100, L_hi=900, kv="fp8"),
+    "fp8_rows96": W.config(3, B=2, n=32, Hq=24, Hkv=8, tree="random", max_depth=6, L_lo=333, L_hi=700, vocab=0,
+                           kv="fp8"),
+    "fp8_rows32_paged": W.config(4, B=3, Hq=8, Hkv=8, L_lo=17, L_hi=600, kv="fp8"),
+    "fp8_chunks": W.config(2, B=1, L_lo=7000, L_hi=7000, Lmax=7008, vocab=0, kv="fp8"),
+    "fp8_d64": W.config(2, B=2, D=64, L_lo=500, L_hi=777, vocab=0, kv="fp8"),
 }
 
 

@@ -16,7 +16,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libtreeverify.so")
 
 TV_OK, TV_EINVAL, TV_ETOPOLOGY, TV_EUNSUPPORTED, TV_EWORKSPACE, TV_EHIP = range(6)
-TV_F32, TV_BF16, TV_F16 = 0, 1, 2
+TV_F32, TV_BF16, TV_F16, TV_FP8_E4M3 = 0, 1, 2, 3
 TV_NMAX, TV_PAGE, TV_MSS_VMAX, TV_TOPK_MAX, TV_MERGE_MMAX = 256, 16, 1 << 20, 16, 64
 
 _c_int, _c_float, _vp, _size_t = ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
@@ -25,7 +25,8 @@ _c_int, _c_float, _vp, _size_t = ctypes.c_int32, ctypes.c_float, ctypes.c_void_p
 class AttnDesc(ctypes.Structure):
     _fields_ = [("B", _c_int), ("n", _c_int), ("Hq", _c_int), ("Hkv", _c_int), ("D", _c_int),
                 ("dtype", _c_int), ("scale", _c_float), ("paged", _c_int), ("block_size", _c_int),
-                ("Lmax", _c_int), ("max_blocks", _c_int), ("num_blocks", _c_int)]
+                ("Lmax", _c_int), ("max_blocks", _c_int), ("num_blocks", _c_int),
+                ("kv_dtype", _c_int), ("k_scale", _c_float), ("v_scale", _c_float)]
 
 
 class TreeVerifyError(RuntimeError):
@@ -113,9 +114,10 @@ def validate_host(parent, depth) -> int:
     return load().tree_validate_host(len(p), p.ctypes.data, d.ctypes.data)
 
 
-def attn_desc(B, n, Hq, Hkv, D, dtype, *, paged=False, Lmax=0, max_blocks=0, num_blocks=0, scale=0.0):
+def attn_desc(B, n, Hq, Hkv, D, dtype, *, paged=False, Lmax=0, max_blocks=0, num_blocks=0, scale=0.0,
+              kv_dtype=0, k_scale=0.0, v_scale=0.0):
     return AttnDesc(B, n, Hq, Hkv, D, dtype, float(scale), int(paged), TV_PAGE if paged else 0,
-                    Lmax, max_blocks, num_blocks)
+                    Lmax, max_blocks, num_blocks, kv_dtype, float(k_scale), float(v_scale))
 
 
 def workspace_size(desc: AttnDesc) -> int:
@@ -140,18 +142,20 @@ def tree_build(parent, depth, prefix_len, *, mask=None, pos=None, status=None, s
 
 def tree_attention(q, k_cache, v_cache, prefix_len, k_tree, v_tree, mask, *, block_table=None,
                    num_blocks=0, scale=0.0, out=None, lse=None, status=None, workspace=None,
-                   want_lse=False, stream=None):
+                   want_lse=False, k_scale=0.0, v_scale=0.0, stream=None):
     """Tree attention.  q [B][n][Hq][D]; caches contiguous (k, v [B][Hkv][Lmax][D]) or
-    paged when block_table is given (k, v [blocks][Hkv][16][D]); k_tree, v_tree
-    [B][n][Hkv][D]; mask from tree_build."""
+    paged when block_table is given (k, v [blocks][Hkv][16][D]); uint8 caches hold
+    fp8 E4M3 codes with per-tensor k_scale / v_scale; k_tree, v_tree [B][n][Hkv][D];
+    mask from tree_build."""
     B, n, Hq, D = q.shape
     Hkv = k_tree.shape[2]
     paged = block_table is not None
+    fp8 = dict(kv_dtype=TV_FP8_E4M3, k_scale=k_scale, v_scale=v_scale) if k_cache.dtype == torch.uint8 else {}
     if paged:
         desc = attn_desc(B, n, Hq, Hkv, D, _dtype_code(q), paged=True, max_blocks=block_table.shape[1],
-                         num_blocks=num_blocks or k_cache.shape[0], scale=scale)
+                         num_blocks=num_blocks or k_cache.shape[0], scale=scale, **fp8)
     else:
-        desc = attn_desc(B, n, Hq, Hkv, D, _dtype_code(q), Lmax=k_cache.shape[2], scale=scale)
+        desc = attn_desc(B, n, Hq, Hkv, D, _dtype_code(q), Lmax=k_cache.shape[2], scale=scale, **fp8)
     out = torch.empty_like(q) if out is None else out
     if want_lse and lse is None:
         lse = torch.empty((B, n, Hq), dtype=torch.float32, device=q.device)

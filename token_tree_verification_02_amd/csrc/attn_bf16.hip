@@ -50,7 +50,7 @@ namespace {
 
 using namespace attn;
 
-template <int D, int RB, int KS, int TK, int S>
+template <int D, int RB, int KS, int TK, int S, bool FP8 = false>
 struct Cfg {
   static constexpr int NT = 64 * RB * KS;      // threads per workgroup
   static constexpr int ROWB = 2 * D;           // bytes per token row in LDS
@@ -67,8 +67,21 @@ struct Cfg {
   static constexpr int DB = D / 32;            // 32-row d blocks of O^T
   static constexpr int SD = D / 16;            // k-steps of the QK^T product
   static constexpr int MERGE = (KS > 1) ? (KS - 1) * RB * 64 * 66 * 4 : 0;
-  static constexpr int LDS = RING > MERGE ? RING : MERGE;
+  // fp8 cache: the ring stages fp8 tiles (1 byte per element) and one bf16 tile
+  // buffer per group (CUR) holds the converted tile the MFMAs read
+  static constexpr int GSTAGE8 = 2 * TK * D;
+  static constexpr int STAGE8 = KS * GSTAGE8;
+  static constexpr int LINES8 = GSTAGE8 / 1024;
+  static constexpr int HL8 = LINES8 / 2;
+  static constexpr int LPW8 = LINES8 / RB;
+  static constexpr int RPL8 = 1024 / D;  // token rows per fp8 line
+  static constexpr int GPR8 = D / 16;    // 16-byte granules per fp8 row
+  static constexpr int CUR = KS * GSTAGE;
+  static constexpr int USED = FP8 ? S * STAGE8 + CUR : RING;
+  static constexpr int LDS = USED > MERGE ? USED : MERGE;
+  static constexpr int WAITN = (S - 2) * (FP8 ? LPW8 : LPW);  // loads a wave may leave in flight
   static_assert(HL % RB == 0 && LPW * (S - 2) < 64, "pipeline shape");
+  static_assert(!FP8 || (HL8 % RB == 0 && LPW8 * (S - 2) < 64), "fp8 pipeline shape");
   static_assert(TK % 32 == 0 && TK <= 64 && 16 % RPL == 0, "tile");
 };
 
@@ -78,10 +91,10 @@ __device__ __forceinline__ uint32_t pick32(uint64_t w0, uint64_t w1, uint64_t w2
   return (half & 1) ? (uint32_t)(x >> 32) : (uint32_t)x;
 }
 
-template <bool F16, int D, int RB, int KS, int TK, int S>
+template <bool F16, bool FP8, int D, int RB, int KS, int TK, int S>
 __global__ __launch_bounds__(64 * RB * KS) void attn_bf16_kernel(AttnArgs a, int rsplit, int nchunks,
                                                                  int chunk_len, int cap) {
-  using C = Cfg<D, RB, KS, TK, S>;
+  using C = Cfg<D, RB, KS, TK, S, FP8>;
   using E = Elt<F16>;
   using V8 = typename E::V8;
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
@@ -160,7 +173,8 @@ __global__ __launch_bounds__(64 * RB * KS) void attn_bf16_kernel(AttnArgs a, int
 
   // ---- issue the DMA lines this wave owns for tile tt of its group into stage st
   auto issue = [=](int tt, int st) {
-    const uint32_t gbase = ring + st * C::STAGE + ks * C::GSTAGE;
+    // (fp8 cache: only tree tiles come here, into the group's bf16 buffer)
+    const uint32_t gbase = FP8 ? ring + S * C::STAGE8 + ks * C::GSTAGE : ring + st * C::STAGE + ks * C::GSTAGE;
     const char* zsrc = zero + lane * 16;
     if (tt >= T) {  // past the end: keep the vmcnt bookkeeping uniform with zero-page loads
 #pragma unroll
@@ -220,6 +234,81 @@ __global__ __launch_bounds__(64 * RB * KS) void attn_bf16_kernel(AttnArgs a, int
     }
   };
 
+  // ---- fp8 cache: prefix tiles go through an fp8 ring; each wave converts the
+  // lines it loaded into the group's bf16 tile buffer (codes, unscaled), at the
+  // positions the bf16 layout above gives each key row and granule
+  const uint32_t cur = ring + (FP8 ? S * C::STAGE8 : 0) + ks * C::GSTAGE;  // bf16 tile buffer of the group
+  auto issue8 = [=](int tt, int st) {
+    const uint32_t gbase = ring + st * C::STAGE8 + ks * C::GSTAGE8;
+    const char* zsrc = zero + lane * 16;
+    if (tt >= T_pre) {  // past the end, or a tree tile (loaded into the buffer when consumed)
+#pragma unroll
+      for (int q = 0; q < C::LPW8; ++q) dma16(zsrc, gbase + (q * RB + rb) * 1024);
+      return;
+    }
+    const int tstart = k0 + tt * TK;
+    const bool full = tstart + TK <= k1;
+    const int gran = lane % C::GPR8;
+    int id[4] = {-1, -1, -1, -1};
+    if (a.paged) {
+      const int b0 = tstart >> 4;
+      const AS4 int32_t* row = btc + (size_t)b * a.max_blocks;
+#pragma unroll
+      for (int i = 0; i < (TK + 15) / 16; ++i) id[i] = b0 + i < a.max_blocks ? row[b0 + i] : -1;
+    }
+#pragma unroll
+    for (int q = 0; q < C::LPW8; ++q) {
+      const int line = q * RB + rb;
+      const bool isv = line >= C::HL8;
+      const int r = (isv ? line - C::HL8 : line) * C::RPL8 + lane / C::GPR8;  // key row within the tile
+      const int j = tstart + r;
+      const char* src;
+      bool ok = full || j < k1;
+      if (a.paged) {
+        const int blk = id[r >> 4];
+        ok = ok && blk >= 0 && blk < a.num_blocks;
+        src = (isv ? vc : kc) + (((size_t)blk * Hkv + g) * TV_PAGE + (j & 15)) * D + gran * 16;
+      } else {
+        src = (isv ? vc : kc) + (rowbase + j) * D + gran * 16;
+      }
+      dma16(ok ? src : zsrc, gbase + line * 1024);
+    }
+  };
+  auto convert8 = [=](int st) {
+    const uint32_t gbase = ring + st * C::STAGE8 + ks * C::GSTAGE8;
+    const int gran = lane % C::GPR8;
+#pragma unroll
+    for (int q = 0; q < C::LPW8; ++q) {
+      const int line = q * RB + rb;
+      const bool isv = line >= C::HL8;
+      const int r = (isv ? line - C::HL8 : line) * C::RPL8 + lane / C::GPR8;
+      const u32x4 x = *(const u32x4 AS3*)((const char AS3*)(smem) + (gbase - ring) + line * 1024 + lane * 16);
+      u32x4 lo, hi;  // bf16 elements 0..7 and 8..15 of the 16 fp8 codes (exact: E4M3 fits bf16)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t src = x[w];
+        // scale 1: the instruction's scale operand acts as a power of two only
+        // (an E8M0 block scale), so the per-tensor scales are applied to the
+        // scores and probabilities instead
+        const auto p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(src, 1.0f, false);
+        const auto p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(src, 1.0f, true);
+        const uint32_t w0 = __builtin_bit_cast(uint32_t, p0), w1 = __builtin_bit_cast(uint32_t, p1);
+        if (w < 2) {
+          lo[2 * w] = w0;
+          lo[2 * w + 1] = w1;
+        } else {
+          hi[2 * (w - 2)] = w0;
+          hi[2 * (w - 2) + 1] = w1;
+        }
+      }
+      const int lrow = isv ? r : perm_row(r);  // K rows sit at perm_row(key)
+      const int sw = isv ? vswz<D>(lrow) : kswz<D>(lrow);
+      char AS3* rb0 = (char AS3*)(smem) + (cur - ring) + (isv ? C::REG : 0) + lrow * C::ROWB;
+      *(u32x4 AS3*)(rb0 + (((2 * gran) ^ sw) << 4)) = lo;
+      *(u32x4 AS3*)(rb0 + (((2 * gran + 1) ^ sw) << 4)) = hi;
+    }
+  };
+
   // ---- this lane's query column: operand registers and ancestor mask
   const int qrow = rs * 32 * RB + 32 * rb + col;
   const bool qvalid = qrow < rows;
@@ -269,26 +358,49 @@ __global__ __launch_bounds__(64 * RB * KS) void attn_bf16_kernel(AttnArgs a, int
   // so the two latencies overlap; the full wait (which the compiler can see)
   // then leaves no load of its own pending inside the loop
 #pragma unroll
-  for (int i = 0; i < S - 1; ++i) issue(i * KS + ks, i);
+  for (int i = 0; i < S - 1; ++i) {
+    if constexpr (FP8)
+      issue8(i * KS + ks, i);
+    else
+      issue(i * KS + ks, i);
+  }
   wait_vmcnt<0>();
 
   for (int it = 0; it < iters; ++it) {
-    wait_vmcnt<(S - 2) * C::LPW>();  // this wave's lines of iteration `it` have landed
+    wait_vmcnt<C::WAITN>();  // this wave's lines of iteration `it` have landed
     // With one wave per key-split group a wave only reads the ring region it
     // filled itself (its own vmcnt wait covers it, and its reads of the stage it
     // refills next were consumed last iteration), so it runs without barriers.
     if constexpr (RB > 1) lds_barrier();  // ... everyone's, and everyone left iteration it-1
-    issue((it + S - 1) * KS + ks, (it + S - 1) % S);
-
     const int tt = it * KS + ks;
+    if constexpr (FP8) {
+      issue8((it + S - 1) * KS + ks, (it + S - 1) % S);
+      if (tt < T) {
+        if (tt >= T_pre) {  // tree tile (bf16): straight into the buffer, waited here
+          issue(tt, 0);  // the tree branch of issue() takes the buffer as its stage base below
+          wait_vmcnt<0>();
+        } else {
+          convert8(it % S);
+        }
+      }
+      if constexpr (RB > 1) lds_barrier();  // the buffer holds the whole tile
+    } else {
+      issue((it + S - 1) * KS + ks, (it + S - 1) % S);
+    }
+
     if (tt < T) {
       const int st = it % S;
-      const char AS3* Kr = (const char AS3*)(smem) + st * C::STAGE + ks * C::GSTAGE;
+      const char AS3* Kr = (const char AS3*)(smem) + (FP8 ? cur - ring : st * C::STAGE + ks * C::GSTAGE);
       const char AS3* Vr = Kr + C::REG;
       const bool tree = tt >= T_pre;
       const int tstart = tree ? (tt - T_pre) * TK : k0 + tt * TK;
       const int lim = tree ? n - tstart : k1 - tstart;  // keys of this tile that exist
       const bool full = !tree && lim >= TK;
+      // fp8 prefix tiles hold unscaled codes: the key scale joins the score scale
+      // and the value scale multiplies the probabilities entering the PV product
+      // (the row sum keeps the plain probabilities)
+      const float slt = (FP8 && !tree) ? sl2 * a.k_scale : sl2;
+      const float vsc = (FP8 && !tree) ? a.v_scale : 1.f;
 
       // QK^T of the tile's key blocks as independent accumulator chains, stepped
       // together over the head dimension, so consecutive MFMAs never wait on each
@@ -342,7 +454,7 @@ __global__ __launch_bounds__(64 * RB * KS) void attn_bf16_kernel(AttnArgs a, int
             mx = fmaxf(mx, Scur[r]);
           }
         }
-        mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;  // scale > 0 commutes with max
+        mx = fmaxf(mx, __shfl_xor(mx, 32)) * slt;  // scale > 0 commutes with max
         if (__any(mx > m_run + kTau)) {
           const float m_new = fmaxf(m_run, mx);
           const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
@@ -357,9 +469,9 @@ __global__ __launch_bounds__(64 * RB * KS) void attn_bf16_kernel(AttnArgs a, int
         V8 pop[2];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(Scur[r], sl2, -msub));
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(Scur[r], slt, -msub));
           lsum += p;
-          pop[r >> 3][r & 7] = E::cvt(p);
+          pop[r >> 3][r & 7] = E::cvt(FP8 ? p * vsc : p);
         }
 #pragma unroll
         for (int half = 0; half < 2; ++half)
@@ -445,11 +557,17 @@ template <int D, int RB, int KS, int TK, int S>
 hipError_t launch_cfg(const AttnArgs& a, const AttnPlan& p, hipStream_t s) {
   const int grid = a.B * a.Hkv * p.nchunks * p.rsplit;
   if (grid == 0) return hipSuccess;
-  if (a.f16)
-    hipLaunchKernelGGL((attn_bf16_kernel<true, D, RB, KS, TK, S>), dim3(grid), dim3(64 * RB * KS), 0, s, a, p.rsplit,
+  if (a.kv_fp8) {
+    if constexpr (RB <= 4)
+      hipLaunchKernelGGL((attn_bf16_kernel<false, true, D, RB, KS, TK, S>), dim3(grid), dim3(64 * RB * KS), 0, s,
+                         a, p.rsplit, p.nchunks, p.chunk_len, p.cap);
+    else
+      return hipErrorInvalidConfiguration;  // the host never plans this
+  } else if (a.f16)
+    hipLaunchKernelGGL((attn_bf16_kernel<true, false, D, RB, KS, TK, S>), dim3(grid), dim3(64 * RB * KS), 0, s, a, p.rsplit,
                        p.nchunks, p.chunk_len, p.cap);
   else
-    hipLaunchKernelGGL((attn_bf16_kernel<false, D, RB, KS, TK, S>), dim3(grid), dim3(64 * RB * KS), 0, s, a,
+    hipLaunchKernelGGL((attn_bf16_kernel<false, false, D, RB, KS, TK, S>), dim3(grid), dim3(64 * RB * KS), 0, s, a,
                        p.rsplit, p.nchunks, p.chunk_len, p.cap);
   return hipGetLastError();
 }

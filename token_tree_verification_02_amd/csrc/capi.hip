@@ -52,6 +52,14 @@ int check_desc(const tv_attn_desc* d) {
     if (d->Lmax < 0 || d->Lmax % TV_PAGE) return fail(TV_EINVAL, "Lmax=%d must be >= 0 and a multiple of 16", d->Lmax);
   }
   if ((long long)d->Hq * d->n > (1LL << 24)) return fail(TV_EINVAL, "n*Hq too large");
+  if (d->kv_dtype != 0 && d->kv_dtype != d->dtype) {
+    if (d->kv_dtype != TV_FP8_E4M3) return fail(TV_EUNSUPPORTED, "cache dtype %d", d->kv_dtype);
+    if (d->dtype != TV_BF16) return fail(TV_EUNSUPPORTED, "an fp8 cache needs dtype TV_BF16");
+    if (!(d->k_scale > 0.f) || !(d->v_scale > 0.f) || isinf(d->k_scale) || isinf(d->v_scale))
+      return fail(TV_EINVAL, "fp8 cache scales must be finite and > 0");
+    if ((long long)d->n * (d->Hq / d->Hkv) > 128)
+      return fail(TV_EUNSUPPORTED, "an fp8 cache supports up to 128 query rows per KV head");
+  }
   return TV_OK;
 }
 
@@ -218,6 +226,9 @@ int tree_attention(const tv_attn_desc* desc, const void* q, const void* k_cache,
   a.max_blocks = desc->max_blocks;
   a.num_blocks = desc->num_blocks;
   a.f16 = desc->dtype == TV_F16;
+  a.kv_fp8 = desc->kv_dtype == TV_FP8_E4M3;
+  a.k_scale = desc->k_scale;
+  a.v_scale = desc->v_scale;
   const float scale = desc->scale > 0.f ? desc->scale : 1.f / sqrtf((float)desc->D);
   a.scale_log2 = scale * tv::kLog2e;
   a.ws_o = nullptr;
@@ -329,6 +340,7 @@ int tree_commit_kv(const tv_attn_desc* desc, void* k_cache, void* v_cache, const
                    const int32_t* path_len, int32_t* new_prefix_len, int32_t* status, void* stream) {
   int rc = check_desc(desc);
   if (rc != TV_OK) return rc;
+  if (desc->kv_dtype == TV_FP8_E4M3) return fail(TV_EUNSUPPORTED, "committing into an fp8 cache");
   if ((long long)desc->B * desc->n > 0x7fffffffLL) return fail(TV_EINVAL, "B*n too large");
   if (desc->B == 0) return TV_OK;
   if (!k_cache || !v_cache || !prefix_len || !k_tree || !v_tree || !path || !path_len || !new_prefix_len)

@@ -57,6 +57,8 @@ struct AttnArgs {
   int B, n, Hq, Hkv, G, D, W;
   int paged, Lmax, max_blocks, num_blocks;
   int f16;           // 16-bit element type: 0 bf16, 1 fp16
+  int kv_fp8;        // prefix cache holds OCP E4M3 codes; value = code * k_scale (v_scale)
+  float k_scale, v_scale;
   float scale_log2;  // softmax scale * log2(e)
 };
 

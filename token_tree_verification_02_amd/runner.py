@@ -33,8 +33,13 @@ def upload(w: dict, device="cuda") -> dict:
     d = dict(cfg=cfg, paged=cfg.paged, num_blocks=int(w.get("num_blocks", 0)))
     for k in ("parent", "depth", "prefix_len", "block_table", "tokens"):
         d[k] = _t(w.get(k), device)
-    for k in ("q", "k_cache", "v_cache", "k_tree", "v_tree", "logits"):
+    for k in ("q", "k_tree", "v_tree", "logits"):
         d[k] = _t(w.get(k), device, dtype=dt)
+    cdt = "u8" if cfg.kv == "fp8" else dt       # an fp8 cache holds 1-byte codes
+    for k in ("k_cache", "v_cache"):
+        d[k] = _t(w.get(k), device, dtype=cdt)
+    d["k_scale"] = float(w.get("k_scale", 0.0))
+    d["v_scale"] = float(w.get("v_scale", 0.0))
     B, n = cfg.B, cfg.n
     d["mask"] = torch.empty((B, n, (n + 63) // 64), dtype=torch.int64, device=device)
     d["pos"] = torch.empty((B, n), dtype=torch.int32, device=device)
@@ -58,10 +63,11 @@ def upload(w: dict, device="cuda") -> dict:
 def attn_desc_of(d):
     cfg = d["cfg"]
     code = dtype_code(cfg.dtype)
+    fp8 = dict(kv_dtype=_lib.TV_FP8_E4M3, k_scale=d["k_scale"], v_scale=d["v_scale"]) if cfg.kv == "fp8" else {}
     if d["paged"]:
         return _lib.attn_desc(cfg.B, cfg.n, cfg.Hq, cfg.Hkv, cfg.D, code, paged=True,
-                              max_blocks=d["block_table"].shape[1], num_blocks=d["num_blocks"])
-    return _lib.attn_desc(cfg.B, cfg.n, cfg.Hq, cfg.Hkv, cfg.D, code, Lmax=d["k_cache"].shape[2])
+                              max_blocks=d["block_table"].shape[1], num_blocks=d["num_blocks"], **fp8)
+    return _lib.attn_desc(cfg.B, cfg.n, cfg.Hq, cfg.Hkv, cfg.D, code, Lmax=d["k_cache"].shape[2], **fp8)
 
 
 def build(d, stream=None):
@@ -73,7 +79,8 @@ def attention(d, stream=None):
     return _lib.tree_attention(d["q"], d["k_cache"], d["v_cache"], d["prefix_len"], d["k_tree"], d["v_tree"],
                                d["mask"], block_table=d["block_table"], num_blocks=d["num_blocks"],
                                out=d["out"], lse=d["lse"], want_lse=True, status=d["attn_status"],
-                               workspace=d["workspace"], stream=stream)
+                               workspace=d["workspace"], k_scale=d["k_scale"], v_scale=d["v_scale"],
+                               stream=stream)
 
 
 def verify(d, stream=None):

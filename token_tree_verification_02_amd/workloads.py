@@ -551,7 +551,7 @@ def reference_bytes(w: dict) -> dict:
     es = 2 if is16(cfg.dtype) else 4
     L = w["prefix_len"].astype(np.int64)
     n, Hq, Hkv, D, B = cfg.n, cfg.Hq, cfg.Hkv, cfg.D, cfg.B
-    kv_prefix = int(L.sum()) * Hkv * D * 2 * es
+    kv_prefix = int(L.sum()) * Hkv * D * 2 * (1 if cfg.kv == "fp8" else es)
     kv_tree = B * n * Hkv * D * 2 * es
     q_o = 2 * B * n * Hq * D * es
     masks = B * n * ((n + 63) // 64) * 8
