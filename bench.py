@@ -168,7 +168,7 @@ def main():
                     plen=torch.empty(cfg.B, dtype=torch.int32, device="cuda"),
                     bonus=torch.empty(cfg.B, dtype=torch.int32, device="cuda"),
                     status=torch.empty(cfg.B, dtype=torch.int32, device="cuda"),
-                    ws=torch.empty(_lib.stochastic_workspace_size(cfg.B, cfg.vocab), dtype=torch.uint8,
+                    ws=torch.empty(_lib.stochastic_workspace_size(cfg.B, cfg.n, cfg.vocab), dtype=torch.uint8,
                                    device="cuda")) for _ in range(R)]
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
@@ -247,8 +247,14 @@ def main():
                 ch = [v for v in range(cfg.n) if par[v] == u]
                 rows += 1 + (ch.index(vis[j + 1]) + 1 if j + 1 < len(vis) else len(ch))
         es_l = 2 if W.is16(cfg.dtype) else 4
+        # the call's automatic mode: all row statistics first while all rows fit in 1 GiB
+        pre = 2.0 * cfg.B * cfg.n * cfg.vocab * es_l <= float(1 << 30)
+        if pre:   # every LLM row and every non-root SSM row, then the walk's residual and draw passes
+            rows_all = cfg.B * (2 * cfg.n - 1)
         mss_out = {"us": round(t_mss * 1e6, 2), "mean_path_len": round(float(plen_h.mean()), 3),
-                   "rows_read": rows, "hbm_gbs": round(rows * cfg.vocab * es_l / t_mss / 1e9, 1)}
+                   "mode": "all-row statistics" if pre else "visited rows",
+                   "rows_read": rows_all if pre else rows,
+                   "hbm_gbs": round((rows_all if pre else rows) * cfg.vocab * es_l / t_mss / 1e9, 1)}
     # tree construction: one expansion step (4 frontier nodes per sequence, k = 4,
     # on the SSM rows) and a merge of 8 drafts of 8 tokens per sequence
     cons_out = None

@@ -213,16 +213,23 @@ int tree_verify_greedy(int B, int n, int V, int logits_dtype, const void* logits
  *   status [B] int32 out (may be NULL): TV_OK, or TV_EINVAL for a sequence
  *     whose parent array is not topological with root 0 or whose draft token
  *     is outside [0, V); its path_len is then 0, path -1 and bonus -1.
- *   workspace: tree_verify_stochastic_workspace_size(B, V) bytes (fp32
- *     residual rows), 16-byte aligned; contents on entry do not matter.
+ *   mode: 0 = chosen from the sizes; 1 = each sequence's walk reads only the
+ *     rows it visits (the statistics of a visited node's rows are gathered
+ *     by the walk); 2 = a parallel pass first gathers the statistics of every
+ *     LLM and SSM row (reads all of them once), and the walk then reads rows
+ *     only for residuals and the final draw.  0 takes 2 while all rows
+ *     together are at most 1 GiB.  The results are the same in every mode.
+ *   workspace: tree_verify_stochastic_workspace_size(B, n, V) bytes (fp32
+ *     residual rows and row statistics), 16-byte aligned; contents on entry
+ *     do not matter.
  * Every logits row needs a finite maximum; NaN is out of contract.
  * Decisions are taken in fp32 (softmax with fp32 sums): a draw whose margin
  * to a decision boundary is below that rounding may differ from an exact
  * evaluation.  1 <= n <= TV_NMAX, 1 <= V <= TV_MSS_VMAX.
  * ------------------------------------------------------------------------- */
 #define TV_MSS_VMAX (1 << 20)
-size_t tree_verify_stochastic_workspace_size(int B, int V);
-int tree_verify_stochastic(int B, int n, int V, int logits_dtype, const void* logits,
+size_t tree_verify_stochastic_workspace_size(int B, int n, int V);
+int tree_verify_stochastic(int B, int n, int V, int logits_dtype, int mode, const void* logits,
                            const void* ssm_logits, const int32_t* tokens,
                            const int32_t* parent, const float* u_accept,
                            const float* u_sample, int32_t* path_out,

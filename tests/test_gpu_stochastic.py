@@ -57,12 +57,12 @@ def dev(a, bf16):
     return torch.from_numpy(a).cuda()
 
 
-def run_gpu(w):
+def run_gpu(w, mode=0):
     cfg = w["cfg"]
     bf = cfg.dtype == "bf16"
     out = _lib.tree_verify_stochastic(dev(w["logits"], bf), dev(w["ssm_logits"], bf), dev(w["tokens"], False),
                                       dev(w["parent"], False), dev(w["u_accept"], False),
-                                      dev(w["u_sample"], False))
+                                      dev(w["u_sample"], False), mode=mode)
     torch.cuda.synchronize()
     return [t.cpu().numpy() for t in out]
 
@@ -73,9 +73,9 @@ def valid_path(path, plen, parent):
         (path[plen:] == -1).all()
 
 
-def check(w, max_close_frac=0.1):
+def check(w, max_close_frac=0.1, mode=0):
     cfg = w["cfg"]
-    path, plen, bonus, status = run_gpu(w)
+    path, plen, bonus, status = run_gpu(w, mode)
     r_path, r_plen, r_bonus, r_status, dec = oracle.verify_stochastic(
         w["logits"], w["ssm_logits"], w["tokens"], w["parent"], w["u_accept"], w["u_sample"], cfg.dtype)
     np.testing.assert_array_equal(status, r_status)
@@ -93,7 +93,7 @@ def check(w, max_close_frac=0.1):
         assert plen[b] == r_plen[b], (b, plen[b], r_plen[b])
         np.testing.assert_array_equal(path[b], r_path[b], err_msg=f"sequence {b}")
         assert bonus[b] == r_bonus[b], (b, bonus[b], r_bonus[b])
-    log(f"  {cfg.name} V={cfg.vocab}: {exact} exact, {close} within rounding of a boundary; "
+    log(f"  {cfg.name} V={cfg.vocab} mode {mode}: {exact} exact, {close} within rounding of a boundary; "
         f"path lengths {list(plen[:8])}")
     assert close <= max(2, max_close_frac * cfg.B), close
     return plen
@@ -110,15 +110,19 @@ CASES = {
 }
 
 
+@pytest.mark.parametrize("mode", [1, 2])
 @pytest.mark.parametrize("name", list(CASES))
-def test_stochastic_parity(name):
+def test_stochastic_parity(name, mode):
+    """mode 1: the walk gathers the statistics of the rows it visits; mode 2: all
+    row statistics first, in parallel."""
     cfg, noise = CASES[name]
-    log(f"case stochastic {name}")
+    log(f"case stochastic {name} mode {mode}")
     w = W.make_stochastic(cfg, seed=17, ssm_noise=noise)
-    check(w)
+    check(w, mode=mode)
 
 
-def test_stochastic_invalid_sequences_reported():
+@pytest.mark.parametrize("mode", [1, 2])
+def test_stochastic_invalid_sequences_reported(mode):
     log("case stochastic invalid")
     cfg = W.config(2, B=4, L_lo=16, L_hi=16, vocab=500)
     w = W.make_stochastic(cfg, seed=3)
@@ -127,7 +131,7 @@ def test_stochastic_invalid_sequences_reported():
     w["tokens"][1, 5] = cfg.vocab                         # draft token outside the vocabulary
     w["tokens"][2, 3] = -2
     w["parent"][3, 4] = 9                                 # a parent after its child
-    check(w)
+    check(w, mode=mode)
 
 
 def test_gpu_emits_the_llm_distribution():
@@ -155,7 +159,7 @@ def test_gpu_emits_the_llm_distribution():
              tokens=tokens, parent=np.broadcast_to(parent, (B, n)).copy(),
              u_accept=(drng.integers(0, 1 << 24, (B, n)) / float(1 << 24)).astype(np.float32),
              u_sample=(drng.integers(0, 1 << 24, (B, n)) / float(1 << 24)).astype(np.float32))
-    path, plen, bonus, status = run_gpu(w)
+    path, plen, bonus, status = run_gpu(w)                 # 2 * 20000 * 6 * 6 values: precomputed statistics
     assert (status == 0).all()
     first = np.where(plen > 1, tokens[np.arange(B), np.maximum(path[:, 1], 0)], bonus)
     p1 = stats.chisquare(np.bincount(first, minlength=V), softmax(llm[0].astype(np.float64)) * B).pvalue

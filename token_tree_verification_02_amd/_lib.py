@@ -48,8 +48,8 @@ SIGNATURES = {
     "tree_attention": (_c_int, [ctypes.POINTER(AttnDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                 _vp, _vp, _size_t, _vp]),
     "tree_verify_greedy": (_c_int, [_c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
-    "tree_verify_stochastic_workspace_size": (_size_t, [_c_int, _c_int]),
-    "tree_verify_stochastic": (_c_int, [_c_int, _c_int, _c_int, _c_int] + [_vp] * 11 + [_size_t, _vp]),
+    "tree_verify_stochastic_workspace_size": (_size_t, [_c_int, _c_int, _c_int]),
+    "tree_verify_stochastic": (_c_int, [_c_int] * 5 + [_vp] * 11 + [_size_t, _vp]),
     "tree_expand_topk": (_c_int, [_c_int] * 6 + [_vp] * 9 + [_vp]),
     "tree_merge_drafts": (_c_int, [_c_int] * 4 + [_vp] * 9 + [_vp]),
     "tree_commit_kv": (_c_int, [ctypes.POINTER(AttnDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
@@ -187,14 +187,15 @@ def tree_verify_greedy(logits, tokens, parent, *, argmax=None, path=None, path_l
     return argmax, path, path_len, bonus
 
 
-def stochastic_workspace_size(B: int, V: int) -> int:
-    return int(load().tree_verify_stochastic_workspace_size(B, V))
+def stochastic_workspace_size(B: int, n: int, V: int) -> int:
+    return int(load().tree_verify_stochastic_workspace_size(B, n, V))
 
 
-def tree_verify_stochastic(logits, ssm_logits, tokens, parent, u_accept, u_sample, *, path=None, path_len=None,
-                           bonus=None, status=None, workspace=None, stream=None):
+def tree_verify_stochastic(logits, ssm_logits, tokens, parent, u_accept, u_sample, *, mode=0, path=None,
+                           path_len=None, bonus=None, status=None, workspace=None, stream=None):
     """Stochastic (multi-step speculative sampling) verification.  logits, ssm_logits
-    [B][n][V]; tokens, parent [B][n] int32; u_accept, u_sample [B][n] float32 uniforms.
+    [B][n][V]; tokens, parent [B][n] int32; u_accept, u_sample [B][n] float32 uniforms;
+    mode 0 auto, 1 walk reads only visited rows, 2 all row statistics first.
     Returns (path [B][n], path_len [B], bonus [B], status [B]) int32."""
     B, n, V = logits.shape
     dev = logits.device
@@ -202,11 +203,11 @@ def tree_verify_stochastic(logits, ssm_logits, tokens, parent, u_accept, u_sampl
     path_len = torch.empty((B,), dtype=torch.int32, device=dev) if path_len is None else path_len
     bonus = torch.empty((B,), dtype=torch.int32, device=dev) if bonus is None else bonus
     status = torch.empty((B,), dtype=torch.int32, device=dev) if status is None else status
-    need = stochastic_workspace_size(B, V)
+    need = stochastic_workspace_size(B, n, V)
     if workspace is None and need != (1 << 64) - 1:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    rc = load().tree_verify_stochastic(B, n, V, _dtype_code(logits), _ptr(logits), _ptr(ssm_logits), _ptr(tokens),
+    rc = load().tree_verify_stochastic(B, n, V, _dtype_code(logits), mode, _ptr(logits), _ptr(ssm_logits), _ptr(tokens),
                                        _ptr(parent), _ptr(u_accept), _ptr(u_sample), _ptr(path), _ptr(path_len),
                                        _ptr(bonus), _ptr(status), _ptr(workspace), wbytes, _stream(stream))
     _check(rc, "tree_verify_stochastic")

@@ -271,12 +271,12 @@ int tree_verify_greedy(int B, int n, int V, int logits_dtype, const void* logits
   return TV_OK;
 }
 
-size_t tree_verify_stochastic_workspace_size(int B, int V) {
-  if (B < 0 || V < 1 || V > TV_MSS_VMAX) return (size_t)-1;
-  return tv::mss_workspace_bytes(B, V);
+size_t tree_verify_stochastic_workspace_size(int B, int n, int V) {
+  if (B < 0 || n < 1 || n > TV_NMAX || V < 1 || V > TV_MSS_VMAX) return (size_t)-1;
+  return tv::mss_workspace_bytes(B, n, V);
 }
 
-int tree_verify_stochastic(int B, int n, int V, int logits_dtype, const void* logits, const void* ssm_logits,
+int tree_verify_stochastic(int B, int n, int V, int logits_dtype, int mode, const void* logits, const void* ssm_logits,
                            const int32_t* tokens, const int32_t* parent, const float* u_accept,
                            const float* u_sample, int32_t* path_out, int32_t* path_len, int32_t* bonus,
                            int32_t* status, void* workspace, size_t workspace_bytes, void* stream) {
@@ -285,15 +285,17 @@ int tree_verify_stochastic(int B, int n, int V, int logits_dtype, const void* lo
   if (V < 1 || V > TV_MSS_VMAX) return fail(TV_EINVAL, "V=%d outside [1, %d]", V, TV_MSS_VMAX);
   if (logits_dtype != TV_F32 && logits_dtype != TV_BF16)
     return fail(TV_EUNSUPPORTED, "logits dtype %d", logits_dtype);
+  if (mode < 0 || mode > 2) return fail(TV_EINVAL, "mode=%d outside [0, 2]", mode);
+  if ((long long)B * n * 2 > 0x7fffffffLL) return fail(TV_EINVAL, "B*n too large");
   if (B == 0) return TV_OK;
   if (!logits || !ssm_logits || !tokens || !parent || !u_accept || !u_sample || !path_out || !path_len || !bonus)
     return fail(TV_EINVAL, "null pointer argument");
-  const size_t need = tv::mss_workspace_bytes(B, V);
+  const size_t need = tv::mss_workspace_bytes(B, n, V);
   if (!workspace || workspace_bytes < need)
     return fail(TV_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
   if (((uintptr_t)logits | (uintptr_t)ssm_logits | (uintptr_t)workspace) & 15)
     return fail(TV_EINVAL, "logits, ssm_logits and workspace must be 16-byte aligned");
-  hipError_t e = tv::launch_mss(B, n, V, logits_dtype == TV_BF16, logits, ssm_logits, tokens, parent, u_accept,
+  hipError_t e = tv::launch_mss(B, n, V, logits_dtype == TV_BF16, mode, logits, ssm_logits, tokens, parent, u_accept,
                                 u_sample, (float*)workspace, path_out, path_len, bonus, status, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "tree_verify_stochastic launch");
   return TV_OK;

@@ -263,6 +263,58 @@ __device__ __forceinline__ void seg_store(Shared& S, int ch, const float (&v)[kE
   if ((threadIdx.x & 63) == 0) S.segd[ch * kWaves + (threadIdx.x >> 6)] = sd;
 }
 
+// Precomputed statistics of one row (the second mode: every LLM and SSM row's
+// statistics first, in a fully parallel kernel, so the walk needs no entry pass).
+struct StatRec {
+  float R;
+  float pad;
+  double S;
+};
+
+// One 256-thread workgroup per row: row r of the grid is (sequence, node, which)
+// with which 0 = the LLM row, 1 = the SSM row (node 0 has none).  Same exact
+// online statistics as the walk's own passes.
+template <bool BF16>
+__global__ __launch_bounds__(256) void row_stats_kernel(int n, int V, int vec, const void* __restrict__ logits,
+                                                        const void* __restrict__ ssm, StatRec* __restrict__ out) {
+  __shared__ float sR[4];
+  __shared__ double sS[4];
+  const int r = blockIdx.x, which = r & 1, node = (r >> 1) % n, b = (r >> 1) / n;
+  if (which == 1 && node == 0) return;
+  const int tid = threadIdx.x;
+  const size_t es = BF16 ? 2 : 4;
+  const char* row = (const char*)(which ? ssm : logits) + ((size_t)b * n + node) * V * es;
+  constexpr int kC = 256 * kEPT;  // elements per chunk of this kernel
+  const int nch = (V + kC - 1) / kC, nfull = vec ? V / kC : 0;
+  Stat st;
+  int c = 0;
+  constexpr int kG = BF16 ? 8 : 4;
+  for (; c + kG <= nfull; c += kG) {
+    Raw<BF16> q[kG];
+#pragma unroll
+    for (int u = 0; u < kG; ++u) q[u].load(row, (c + u) * kC + tid * kEPT);
+#pragma unroll
+    for (int u = 0; u < kG; ++u) {
+      float v[kEPT];
+      q[u].unpack(v);
+      stat_add8(st, v);
+    }
+  }
+  for (; c < nch; ++c) {
+    float v[kEPT];
+    load8<BF16>(row, c * kC + tid * kEPT, V, vec, v);
+    stat_add8(st, v);
+  }
+  const Stat w = wave_stat(st);
+  if ((tid & 63) == 0) sR[tid >> 6] = w.R, sS[tid >> 6] = w.S;
+  __syncthreads();
+  if (tid == 0) {
+    Stat t;
+    for (int k = 0; k < 4; ++k) stat_merge(t, sR[k], sS[k]);
+    out[r] = StatRec{t.R, 0.f, t.S};
+  }
+}
+
 template <bool BF16>
 __global__ __launch_bounds__(kThreads) void mss_kernel(int n, int V, int vec, const void* __restrict__ logits,
                                                        const void* __restrict__ ssm,
@@ -270,7 +322,8 @@ __global__ __launch_bounds__(kThreads) void mss_kernel(int n, int V, int vec, co
                                                        const int32_t* __restrict__ parent,
                                                        const float* __restrict__ u_acc,
                                                        const float* __restrict__ u_smp, float* __restrict__ ws,
-                                                       int Vpad, int32_t* __restrict__ path_out,
+                                                       int Vpad, const StatRec* __restrict__ pre,
+                                                       int32_t* __restrict__ path_out,
                                                        int32_t* __restrict__ plen_out, int32_t* __restrict__ bonus,
                                                        int32_t* __restrict__ status) {
   __shared__ Shared S;
@@ -327,11 +380,19 @@ __global__ __launch_bounds__(kThreads) void mss_kernel(int n, int V, int vec, co
     __syncthreads();  // S.child visible
     const char* lrow = lbase + (size_t)cur * V * es;
     const int c1 = k > 0 ? S.child[0] : -1;
-    const char* srow = c1 >= 0 ? sbase + (size_t)c1 * V * es : nullptr;
+    const char* srow = c1 >= 0 && !pre ? sbase + (size_t)c1 * V * es : nullptr;
 
-    // ---- node entry: one pass of statistics of the LLM row and the first child's SSM row
+    // ---- node entry: statistics of the LLM row and the first child's SSM row,
+    // precomputed or in one pass
     Stat sl, sq;
-    {
+    if (pre) {
+      const StatRec a = pre[((size_t)b * n + cur) * 2];
+      sl = Stat{a.R, a.S};
+      if (c1 >= 0) {
+        const StatRec q = pre[((size_t)b * n + c1) * 2 + 1];
+        sq = Stat{q.R, q.S};
+      }
+    } else {
       int c = 0;
       for (; c + kU <= nfull; c += kU) {
         Raw<BF16> a[kU], q[kU];
@@ -387,7 +448,7 @@ __global__ __launch_bounds__(kThreads) void mss_kernel(int n, int V, int vec, co
       // rejected: residual r = max(0, p - q_c) into the other workspace row, its
       // sum, and the next child's SSM maximum
       const int cn = i + 1 < k ? S.child[i + 1] : -1;
-      const char* nrow = cn >= 0 ? sbase + (size_t)cn * V * es : nullptr;
+      const char* nrow = cn >= 0 && !pre ? sbase + (size_t)cn * V * es : nullptr;
       const int xn = cn >= 0 ? S.tok[cn] : -1;
       const float* rin = rbase + (size_t)ib * Vpad;
       float* rout = rbase + (size_t)(ib ^ 1) * Vpad;
@@ -466,6 +527,10 @@ __global__ __launch_bounds__(kThreads) void mss_kernel(int n, int V, int vec, co
         T = tsum;
       } else {
         pnext = cn >= 0 ? (double)S.cap_prev[i & 1] : 0.0;
+      }
+      if (pre && cn >= 0) {
+        const StatRec q = pre[((size_t)b * n + cn) * 2 + 1];
+        sn = Stat{q.R, q.S};
       }
       sq = sn;
     }
@@ -631,23 +696,40 @@ __global__ __launch_bounds__(kThreads) void mss_kernel(int n, int V, int vec, co
 
 }  // namespace
 
-size_t mss_workspace_bytes(int B, int V) {
+size_t mss_workspace_bytes(int B, int n, int V) {
   const size_t vpad = (size_t)(V + kChunk - 1) / kChunk * kChunk;
-  return (size_t)B * 2 * vpad * sizeof(float);
+  return (size_t)B * 2 * vpad * sizeof(float) + (size_t)B * n * 2 * sizeof(StatRec);
 }
 
-hipError_t launch_mss(int B, int n, int V, int bf16, const void* logits, const void* ssm, const int32_t* tokens,
-                      const int32_t* parent, const float* u_acc, const float* u_smp, float* ws, int32_t* path,
-                      int32_t* plen, int32_t* bonus, int32_t* status, hipStream_t s) {
+int mss_precompute(int B, int n, int V, int bf16, int mode) {
+  if (mode != 0) return mode == 2;
+  // every row read once in parallel, against the walk's serial passes over the
+  // rows it visits: worth it while all rows together stay small
+  return (double)B * n * V * (bf16 ? 2 : 4) * 2 <= (double)(1u << 30);
+}
+
+hipError_t launch_mss(int B, int n, int V, int bf16, int mode, const void* logits, const void* ssm,
+                      const int32_t* tokens, const int32_t* parent, const float* u_acc, const float* u_smp,
+                      float* ws, int32_t* path, int32_t* plen, int32_t* bonus, int32_t* status, hipStream_t s) {
   if (B == 0) return hipSuccess;
   const int vpad = (V + kChunk - 1) / kChunk * kChunk;
   const int vec = ((size_t)V * (bf16 ? 2 : 4)) % 16 == 0;
+  StatRec* pre = nullptr;
+  if (mss_precompute(B, n, V, bf16, mode)) {
+    pre = (StatRec*)(ws + (size_t)B * 2 * vpad);
+    if (bf16)
+      hipLaunchKernelGGL(row_stats_kernel<true>, dim3(B * n * 2), dim3(256), 0, s, n, V, vec, logits, ssm, pre);
+    else
+      hipLaunchKernelGGL(row_stats_kernel<false>, dim3(B * n * 2), dim3(256), 0, s, n, V, vec, logits, ssm, pre);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (bf16)
     hipLaunchKernelGGL(mss_kernel<true>, dim3(B), dim3(kThreads), 0, s, n, V, vec, logits, ssm, tokens, parent,
-                       u_acc, u_smp, ws, vpad, path, plen, bonus, status);
+                       u_acc, u_smp, ws, vpad, pre, path, plen, bonus, status);
   else
     hipLaunchKernelGGL(mss_kernel<false>, dim3(B), dim3(kThreads), 0, s, n, V, vec, logits, ssm, tokens, parent,
-                       u_acc, u_smp, ws, vpad, path, plen, bonus, status);
+                       u_acc, u_smp, ws, vpad, pre, path, plen, bonus, status);
   return hipGetLastError();
 }
 

@@ -73,10 +73,10 @@ hipError_t launch_tree_build(int B, int n, const int32_t* parent, const int32_t*
 hipError_t launch_commit(const tv_attn_desc* d, void* kc, void* vc, const int32_t* bt, const int32_t* plen,
                          const void* kt, const void* vt, const int32_t* path, const int32_t* path_len,
                          int32_t* new_len, int32_t* status, hipStream_t s);
-size_t mss_workspace_bytes(int B, int V);
-hipError_t launch_mss(int B, int n, int V, int bf16, const void* logits, const void* ssm, const int32_t* tokens,
-                      const int32_t* parent, const float* u_acc, const float* u_smp, float* ws, int32_t* path,
-                      int32_t* plen, int32_t* bonus, int32_t* status, hipStream_t s);
+size_t mss_workspace_bytes(int B, int n, int V);
+hipError_t launch_mss(int B, int n, int V, int bf16, int mode, const void* logits, const void* ssm,
+                      const int32_t* tokens, const int32_t* parent, const float* u_acc, const float* u_smp,
+                      float* ws, int32_t* path, int32_t* plen, int32_t* bonus, int32_t* status, hipStream_t s);
 hipError_t launch_expand(int B, int F, int V, int k, int n_max, int bf16, const void* logits, const int32_t* frontier,
                          const int32_t* n_cur, int32_t* parent, int32_t* depth, int32_t* tokens, float* scores,
                          int32_t* n_out, int32_t* status, hipStream_t s);
