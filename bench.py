@@ -22,7 +22,8 @@ graph, so the figure is GPU time rather than the host's launch rate.
 
 Prints ONE JSON line.  `value` = B*n / (wall time per step).  `roofline` covers
 the dominant kernel (tree_attention) measured with HIP events on the launch
-stream; `traffic` is read from the committed rocprofv3 counter summary when it
+stream (the mean over K back-to-back launches; tree_attention_us_per_launch
+adds the p10 / median / p90 of single launches, one event between each); `traffic` is read from the committed rocprofv3 counter summary when it
 was taken on the current kernel source, else null.  `cpu_baseline` times the
 CPU oracle on the same workload.
 
@@ -212,8 +213,21 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) * 1e-3 / K
 
+    def timed_each(fn):
+        """Per-launch durations: an event between consecutive launches (p10, median, p90 in us)."""
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+        ev[0].record(stream)
+        for k in range(K):
+            fn(k % R, sh)
+            ev[k + 1].record(stream)
+        torch.cuda.synchronize()
+        d = np.array([ev[k].elapsed_time(ev[k + 1]) * 1e3 for k in range(K)])
+        return {"p10": round(float(np.percentile(d, 10)), 2), "median": round(float(np.median(d)), 2),
+                "p90": round(float(np.percentile(d, 90)), 2), "launches": K}
+
     t_build = timed_graph(lambda i, h: steps[i].build(h))
     t_attn = timed(lambda i, h: steps[i].attention(h))
+    attn_dist = timed_each(lambda i, h: steps[i].attention(h))
     t_ver = timed_graph(lambda i, h: steps[i].verify(h)) if cfg.vocab else 0.0
     steps[0].verify(sh)
     torch.cuda.synchronize()
@@ -336,6 +350,7 @@ def main():
                    "input_copies": R, "launch": "eager" if args.eager else "hip_graph"},
         "roofline": roofline,
         "attn_hbm_gbs": round(attn_gbs, 1), "mfma_util_pct": round(mfma_pct, 2),
+        "tree_attention_us_per_launch": attn_dist,
         "kernel_us": {"tree_build": round(t_build * 1e6, 2), "tree_attention": round(t_attn * 1e6, 2),
                       "tree_verify_greedy": round(t_ver * 1e6, 2),
                       "tree_commit_kv": round(t_commit * 1e6, 2) if t_commit else None,
