@@ -208,7 +208,9 @@ def test_fp8_cache_contract(lib):
     fp8 = dict(kv_dtype=tv.TV_FP8_E4M3, k_scale=0.01, v_scale=0.02)
     ok = desc(**fp8)                                                     # 21 rows per KV head
     assert tv.workspace_size(ok) != SIZE_MAX
-    assert call_attn(lib, desc(B=32, n=32, Hq=64, Hkv=8, **fp8)) == tv.TV_EUNSUPPORTED   # 256 rows
+    many = dict(B=32, n=32, Hq=64, Hkv=8)                                # 256 rows: the balanced schedule
+    assert tv.workspace_size(desc(**many, **fp8)) == tv.workspace_size(desc(**many))
+    assert call_attn(lib, desc(**many, **fp8)) == tv.TV_EWORKSPACE       # planned, refused before launch
     assert call_attn(lib, desc(dtype=tv.TV_F16, **fp8)) == tv.TV_EUNSUPPORTED
     assert call_attn(lib, desc(kv_dtype=tv.TV_FP8_E4M3, k_scale=0.0, v_scale=1.0)) == tv.TV_EINVAL
     assert call_attn(lib, desc(kv_dtype=9)) == tv.TV_EUNSUPPORTED

@@ -99,6 +99,14 @@ SMALL = {
     "fp8_rows32_paged": W.config(4, B=3, Hq=8, Hkv=8, L_lo=17, L_hi=600, kv="fp8"),
     "fp8_chunks": W.config(2, B=1, L_lo=7000, L_hi=7000, Lmax=7008, vocab=0, kv="fp8"),
     "fp8_d64": W.config(2, B=2, D=64, L_lo=500, L_hi=777, vocab=0, kv="fp8"),
+    # fp8 cache on the many-row (balanced schedule) kernel: split items, paged ragged, two mask
+    # words, four tree tiles, D = 64
+    "fp8_merge_split": W.config(3, B=2, L_lo=2900, L_hi=2900, vocab=0, kv="fp8"),
+    "fp8_paged_ragged": W.config(4, B=3, L_lo=100, L_hi=3000, kv="fp8"),
+    "fp8_wide_w2": W.config(5, B=3, L_lo=1, L_hi=2000, Lmax=2048, vocab=0, kv="fp8"),
+    "fp8_n256": W.config(3, B=2, n=256, Hq=8, Hkv=8, tree="random", max_depth=40, L_lo=50, L_hi=300, vocab=0,
+                         kv="fp8"),
+    "fp8_sk_d64": W.config(4, B=2, D=64, L_lo=40, L_hi=1500, vocab=0, kv="fp8"),
 }
 
 

@@ -57,8 +57,6 @@ int check_desc(const tv_attn_desc* d) {
     if (d->dtype != TV_BF16) return fail(TV_EUNSUPPORTED, "an fp8 cache needs dtype TV_BF16");
     if (!(d->k_scale > 0.f) || !(d->v_scale > 0.f) || isinf(d->k_scale) || isinf(d->v_scale))
       return fail(TV_EINVAL, "fp8 cache scales must be finite and > 0");
-    if ((long long)d->n * (d->Hq / d->Hkv) > 128)
-      return fail(TV_EUNSUPPORTED, "an fp8 cache supports up to 128 query rows per KV head");
   }
   return TV_OK;
 }
