@@ -234,6 +234,22 @@ def test_full_size_sampled(index):
         check_verify(w, d)
 
 
+@pytest.mark.slow
+def test_full_size_sampled_fp8_cache():
+    """The long-ragged paged workload at full size with an fp8 prefix cache (the
+    benchmark's --kv fp8 launch), checked on sampled (sequence, KV head) pairs."""
+    cfg = W.config(4, kv="fp8")
+    log(f"case full-size {cfg.name} fp8 cache: generating")
+    w = W.make(cfg)
+    log("  running")
+    d = run(w)
+    rng = np.random.default_rng(44)
+    seqs = sorted(set(rng.choice(cfg.B, size=3, replace=False).tolist()) | {int(np.argmax(w["prefix_len"]))})
+    heads = sorted(set(rng.choice(cfg.Hkv, size=2, replace=False).tolist()))
+    log(f"  oracle on sequences {seqs}, KV heads {heads}")
+    check_attention(w, d, seqs, heads)
+
+
 def test_graph_replay_matches_eager():
     """A HIP-graph replay of the step gives the eager outputs, on every replay,
     with eager work and synchronisations between replays."""
