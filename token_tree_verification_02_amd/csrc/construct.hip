@@ -8,13 +8,15 @@
 // sharing their first token's node).
 //
 // topk_kernel reads one SSM logits row per workgroup in two passes of 16-byte
-// vectors.  The first takes each thread's maximum; the k-th largest of those
-// 256 maxima bounds the row's k-th largest value from below.  The second pass
-// (mostly cache hits) keeps, per thread, its best 16 (value desc, index asc)
-// among the entries at or above that bound, which are few, so the insertion
-// code rarely runs and waves do not diverge on it.  k rounds of a workgroup
-// argmax over the threads' heads then pick the row's top k.  The children are written straight into the caller's tree
-// arrays after the existing nodes.
+// vectors.  The first takes each thread's maximum, then the maxima of 16 groups
+// of 16 threads: they are 16 entries of the row, so the k-th largest of them
+// (k <= 16) bounds the row's k-th largest value from below.  The second pass
+// (mostly cache hits) skips every vector whose maximum is below that bound and
+// keeps, per thread, its best 16 (value desc, index asc) among the entries at
+// or above it, which are few, so the insertion code rarely runs.  k rounds of a
+// workgroup argmax over the threads' heads then pick the row's top k, and the
+// children are written straight into the caller's tree arrays after the
+// existing nodes.
 //
 // merge_kernel builds the trie of one sequence's drafts without sequential
 // insertion: position d of draft m names the node of prefix drafts[m][0..d];
@@ -29,6 +31,13 @@ namespace tv {
 namespace {
 
 constexpr int kKeep = TV_TOPK_MAX;  // per-thread list length (>= k)
+
+// Workgroup barrier that orders LDS accesses only (no wait for global stores).
+__device__ __forceinline__ void lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 // (value desc, index asc): does (v2, i2) rank before (v1, i1)?
 __device__ __forceinline__ bool before(float v2, int i2, float v1, int i1) {
@@ -62,12 +71,13 @@ __global__ __launch_bounds__(256) void topk_kernel(int F, int V, int k, int n_ma
                                                    int32_t* __restrict__ depth, int32_t* __restrict__ tokens,
                                                    float* __restrict__ scores, int32_t* __restrict__ n_out,
                                                    int32_t* __restrict__ status) {
-  __shared__ float sv[4];
-  __shared__ int si[4];
+  __shared__ float sv[2][4];  // per round (double-buffered): each wave's best head
+  __shared__ int si[2][4];
   __shared__ unsigned long long sb[4];
-  __shared__ int s_win;
-  __shared__ float sv_all[256];
+  __shared__ float s_gmax[16];
   __shared__ float s_thr;
+  __shared__ float s_v[kKeep];  // the k winners, written out after the rounds
+  __shared__ int s_i[kKeep];
   const int b = blockIdx.x / F, f = blockIdx.x - b * F;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int nc = n_cur[b];
@@ -120,21 +130,26 @@ __global__ __launch_bounds__(256) void topk_kernel(int F, int V, int k, int n_ma
       fn(BF16 ? bf16_to_f32(((const uint16_t*)row)[i]) : ((const float*)row)[i], i);
   };
 
-  // ---- pass 1: each thread's maximum; the k-th largest of these 256 maxima is
-  // a lower bound on the row's k-th largest value (they are k real entries)
+  // ---- pass 1: each thread's maximum, then the maxima of 16 groups of 16
+  // threads; the k-th largest of those 16 entries bounds the row's k-th largest
+  // value from below
   float tmax = -INFINITY;
   sweep([&](float x, int) { tmax = fmaxf(tmax, x); });
-  sv_all[tid] = tmax;
-  __syncthreads();
-  {
-    int above = 0;  // maxima ranked before mine: larger, or equal from a lower thread
-    for (int t = 0; t < 256; ++t) {
-      const float o = sv_all[t];
-      above += o > tmax || (o == tmax && t < tid);
+#pragma unroll
+  for (int o = 8; o > 0; o >>= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, o));
+  if ((tid & 15) == 0) s_gmax[tid >> 4] = tmax;
+  lds_sync();
+  if (tid < 16) {
+    const float mine = s_gmax[tid];
+    int above = 0;  // group maxima ranked before mine: larger, or equal from a lower group
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const float o = s_gmax[t];
+      above += o > mine || (o == mine && t < tid);
     }
-    if (above == k - 1) s_thr = tmax;
+    if (above == k - 1) s_thr = mine;
   }
-  __syncthreads();
+  lds_sync();
   const float thr = s_thr;
 
   // ---- pass 2 (mostly cache hits): each thread's best 16 among entries >= thr
@@ -142,9 +157,33 @@ __global__ __launch_bounds__(256) void topk_kernel(int F, int V, int k, int n_ma
   int li[kKeep];
 #pragma unroll
   for (int s = 0; s < kKeep; ++s) lv[s] = -INFINITY, li[s] = INT_MAX;
-  sweep([&](float x, int i) {
+  for (int base = 0; base < nv; base += R * 256) {
+    uint4 w[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) w[r] = vp[min(base + r * 256 + tid, nv - 1)];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int vi = base + r * 256 + tid;
+      const uint32_t q[4] = {w[r].x, w[r].y, w[r].z, w[r].w};
+      float m;  // the vector's maximum: most vectors stop here
+      if (BF16)
+        m = fmaxf(fmaxf(fmaxf(bf16lo(q[0]), bf16hi(q[0])), fmaxf(bf16lo(q[1]), bf16hi(q[1]))),
+                  fmaxf(fmaxf(bf16lo(q[2]), bf16hi(q[2])), fmaxf(bf16lo(q[3]), bf16hi(q[3]))));
+      else
+        m = fmaxf(fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1])), fmaxf(__uint_as_float(q[2]), __uint_as_float(q[3])));
+      if (vi < nv && m >= thr) {
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) {
+          const float x = BF16 ? ((e & 1) ? bf16hi(q[e >> 1]) : bf16lo(q[e >> 1])) : __uint_as_float(q[e]);
+          if (x >= thr) keep_insert(lv, li, x, vi * EPV + e);
+        }
+      }
+    }
+  }
+  for (int i = nv * EPV + tid; i < V; i += 256) {  // unaligned rows and the tail
+    const float x = BF16 ? bf16_to_f32(((const uint16_t*)row)[i]) : ((const float*)row)[i];
     if (x >= thr) keep_insert(lv, li, x, i);
-  });
+  }
 
   // ---- k rounds: the best head among all threads; its owner drops it
   const int dp = depth[(size_t)b * n_max + p];
@@ -158,26 +197,27 @@ __global__ __launch_bounds__(256) void topk_kernel(int F, int V, int k, int n_ma
       const int oi = __shfl_xor(bi, o);
       if (before(ov, oi, bv, bi)) bv = ov, bi = oi;
     }
-    if (lane == 0) sv[wv] = bv, si[wv] = bi;
-    __syncthreads();
-    if (tid == 0) {
-      float v = sv[0];
-      int i = si[0];
-      for (int w = 1; w < 4; ++w)
-        if (before(sv[w], si[w], v, i)) v = sv[w], i = si[w];
-      const int u = u0 + j;
-      parent[(size_t)b * n_max + u] = p;
-      depth[(size_t)b * n_max + u] = dp + 1;
-      tokens[(size_t)b * n_max + u] = i;
-      if (scores) scores[(size_t)b * n_max + u] = v;
-      s_win = i;
-    }
-    __syncthreads();
-    if (li[0] == s_win) {  // indices are unique, so exactly one thread owns the winner
+    if (lane == 0) sv[j & 1][wv] = bv, si[j & 1][wv] = bi;
+    lds_sync();  // (the buffers alternate, so the next round's writes need no second barrier)
+    float v = sv[j & 1][0];  // every thread takes the workgroup's winner itself
+    int i = si[j & 1][0];
+#pragma unroll
+    for (int w = 1; w < 4; ++w)
+      if (before(sv[j & 1][w], si[j & 1][w], v, i)) v = sv[j & 1][w], i = si[j & 1][w];
+    if (tid == 0) s_v[j] = v, s_i[j] = i;
+    if (li[0] == i) {  // indices are unique, so exactly one thread owns the winner
 #pragma unroll
       for (int s = 0; s < kKeep - 1; ++s) lv[s] = lv[s + 1], li[s] = li[s + 1];
       lv[kKeep - 1] = -INFINITY, li[kKeep - 1] = INT_MAX;
     }
+  }
+  lds_sync();
+  if (tid < k) {
+    const int u = u0 + tid;
+    parent[(size_t)b * n_max + u] = p;
+    depth[(size_t)b * n_max + u] = dp + 1;
+    tokens[(size_t)b * n_max + u] = s_i[tid];
+    if (scores) scores[(size_t)b * n_max + u] = s_v[tid];
   }
 }
 
