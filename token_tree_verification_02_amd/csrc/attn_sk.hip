@@ -20,11 +20,12 @@
 // compute units; the plan is computed on the device from the prefix lengths by
 // a one-workgroup scheduling kernel, since the host does not know them.
 //
-// Inside a workgroup: 4 waves (one per SIMD), each owning 64 query rows as two
-// 32-row MFMA column blocks, so every K or V operand read from LDS feeds two
-// v_mfma_f32_32x32x16_bf16.  The KV tiles stream HBM -> LDS through an S-stage
-// ring with global_load_lds_dwordx4 and hand-placed vmcnt waits (one LDS-only
-// barrier per tile).  Full prefix tiles and masked tiles (the ragged last
+// Inside a workgroup: 8 waves (two per SIMD), each owning one 32-row MFMA
+// column block of query rows, so a workgroup covers 256 rows of an item and
+// reads each of its KV tiles from HBM once for all of them; every K or V operand
+// read from LDS feeds one v_mfma_f32_32x32x16_bf16.  The KV tiles stream HBM ->
+// LDS through an S-stage ring with global_load_lds_dwordx4 and hand-placed
+// vmcnt waits (one LDS-only barrier per tile).  Full prefix tiles and masked tiles (the ragged last
 // prefix tile, the tree tiles) run separate code, so the common case carries no
 // per-score selects.  Per score the softmax costs one FMA, one exp2, half a
 // max3, half a bf16 pack and half a dot2: the row sums are taken from the
