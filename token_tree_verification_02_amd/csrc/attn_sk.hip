@@ -17,8 +17,9 @@
 // partial (running max, sum, O) into a slot of its workgroup, and a merge pass
 // combines the pieces of every item split that way.  Items that a range covers
 // whole are written directly.  Ragged prefix lengths therefore cost no idle
-// compute units; the plan is computed on the device from the prefix lengths by
-// a one-workgroup scheduling kernel, since the host does not know them.
+// compute units.  The host does not know the prefix lengths, so every
+// workgroup derives the tile list from them on the device (two workgroup scans
+// over the sequences) before it starts its range.
 //
 // Inside a workgroup: 8 waves (two per SIMD), each owning one 32-row MFMA
 // column block of query rows, so a workgroup covers 256 rows of an item and
@@ -48,86 +49,14 @@ constexpr int kSkQB = 1;  // 32-row query blocks per wave (256 rows per workgrou
 __device__ __attribute__((aligned(4096))) uint4 sk_zero_page[256];
 
 
-// Scheduling record in the workspace (int32):
+// Scheduling record in the workspace (int32), written by one workgroup of the
+// attention kernel for the merge pass:
 //   [0] total tiles T, [1] tiles per virtual workgroup, [2] NV, [3] unused,
-//   [4 .. 4+B]   exclusive prefix sum of tiles over sequences (B+1 entries),
-//   [cur .. ]    start cursor of every virtual workgroup: (b, g, tile in item, 0).
-__host__ __device__ inline int sk_cursor_offset(int B) { return 4 + ((B + 1 + 3) & ~3); }
-
+//   [4 .. 4+B]   exclusive prefix sum of tiles over sequences (B+1 entries).
 __device__ __forceinline__ int clamp_len(int L, int cap) { return L < 0 ? 0 : (L > cap ? cap : L); }
 
-// One workgroup of 1024 threads.  Two passes over the prefix lengths (the
-// second knows the per-range size) so nothing written here is read back here.
-__global__ __launch_bounds__(1024) void sk_sched_kernel(const int32_t* __restrict__ plen, int B, int n, int cap,
-                                                        int Hkv, int NV, int32_t* __restrict__ sched) {
-  __shared__ int wsum[16];
-  __shared__ int carry;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int ttree = (n + kTK - 1) / kTK;
-  int32_t* cum = sched + 4;
-  int32_t* curs = sched + sk_cursor_offset(B);
-  int per = 1, T = 0;
-  for (int pass = 0; pass < 2; ++pass) {
-    if (tid == 0) carry = 0;
-    __syncthreads();
-    for (int base = 0; base < B; base += 1024) {
-      const int b = base + tid;
-      int tb = 0, L = 0;
-      if (b < B) {
-        L = clamp_len(plen[b], cap);
-        tb = (L + kTK - 1) / kTK + ttree;
-      }
-      const int t = tb * Hkv;
-      int x = t;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(x, o);
-        if (lane >= o) x += y;
-      }
-      if (lane == 63) wsum[wv] = x;
-      __syncthreads();
-      int off = carry;
-      for (int w = 0; w < wv; ++w) off += wsum[w];
-      const int ex = off + x - t;  // tiles before sequence b
-      if (pass == 1 && b < B) {
-        cum[b] = ex;
-        // every range whose first tile lies in sequence b starts its cursor here
-        const int vf = (ex + per - 1) / per;
-        const int vl = (ex + t - 1) / per;
-        for (int v = vf; v <= vl && v < NV; ++v) {
-          const int r = (int)((long long)v * per - ex);
-          curs[4 * v] = b;
-          curs[4 * v + 1] = r / tb;
-          curs[4 * v + 2] = r % tb;
-          curs[4 * v + 3] = 0;
-        }
-      }
-      __syncthreads();
-      if (tid == 1023) carry = off + x;
-      __syncthreads();
-    }
-    T = carry;
-    per = T > 0 ? (T + NV - 1) / NV : 1;
-    __syncthreads();
-  }
-  if (tid == 0) {
-    cum[B] = T;
-    sched[0] = T;
-    sched[1] = per;
-    sched[2] = NV;
-    sched[3] = 0;
-  }
-  for (int v = tid; v < NV; v += 1024)
-    if ((long long)v * per >= T) {
-      curs[4 * v] = B;
-      curs[4 * v + 1] = 0;
-      curs[4 * v + 2] = 0;
-      curs[4 * v + 3] = 0;
-    }
-}
-
 struct SkArgs {
-  const int32_t* sched;
+  int32_t* sched;
   float* po;   // [2*NV][rsplit][RW][D] partial O (unnormalised)
   float* pml;  // [2*NV][rsplit][RW][2]  (max in the log2 domain, sum)
   int rsplit, NV, cap;
@@ -150,6 +79,82 @@ __device__ __forceinline__ void cursor_next(Cursor& c, const AS4 int32_t* plen, 
   if (++c.g < Hkv) return;
   c.g = 0;
   if (++c.b < B) cursor_seq(c, plen, cap, ttree);
+}
+
+// The tile list, derived from the prefix lengths by every workgroup with the
+// same integer arithmetic (the host does not know the lengths): T tiles in all,
+// `per` tiles per range, and the cursor of tile r0 = v * per, the first of range
+// v.  A workgroup passing rec != nullptr also writes the scheduling record.
+// NT threads, all of which call this; returns false (uniformly) for an empty range.
+template <int NT>
+__device__ __forceinline__ bool sk_plan(const int32_t* __restrict__ plen, int B, int cap, int ttree, int Hkv, int NV,
+                                        int v, int32_t* rec, int& T_out, int& per_out, Cursor& c) {
+  __shared__ int part[NT / 64];
+  __shared__ int hit[3];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  auto tiles = [&](int b) { return b < B ? ((clamp_len(plen[b], cap) + kTK - 1) / kTK + ttree) * Hkv : 0; };
+  // pass 1: the total
+  int T = 0;
+  for (int base = 0; base < B; base += NT) {
+    int x = tiles(base + tid);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+    if (lane == 0) part[wv] = x;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) T += part[w];
+    __syncthreads();
+  }
+  const int per = (T + NV - 1) / NV;
+  const long long r0 = (long long)v * per;
+  T_out = T;
+  per_out = per;
+  if (rec != nullptr && tid == 0) {
+    rec[0] = T;
+    rec[1] = per;
+    rec[2] = NV;
+    rec[3] = 0;
+    rec[4 + B] = T;
+  }
+  if (r0 >= T) return false;
+  // pass 2: exclusive prefix sum over the sequences; the one holding tile r0
+  // gives the cursor (the recording workgroup goes through all of them)
+  int carry = 0;
+  for (int base = 0; base < B; base += NT) {
+    const int b = base + tid;
+    const int t = tiles(b);
+    int x = t;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(x, o);
+      if (lane >= o) x += y;
+    }
+    if (lane == 63) part[wv] = x;
+    __syncthreads();
+    int off = carry, tot = 0;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) {
+      off += w < wv ? part[w] : 0;
+      tot += part[w];
+    }
+    const int ex = off + x - t;  // tiles before sequence b
+    if (b < B) {
+      if (rec != nullptr) rec[4 + b] = ex;
+      if (ex <= r0 && r0 < ex + t) {
+        const int tb = t / Hkv, r = (int)(r0 - ex);
+        hit[0] = b;
+        hit[1] = r / tb;
+        hit[2] = r % tb;
+      }
+    }
+    carry += tot;
+    __syncthreads();
+    if (rec == nullptr && carry > r0) break;  // uniform: every thread holds the same carry
+  }
+  c.b = hit[0];
+  c.g = hit[1];
+  c.off = hit[2];
+  return true;
 }
 
 // 64-bit word `w` (< 4) of a node's mask, from registers.
@@ -356,18 +361,13 @@ __global__ __launch_bounds__(64 * RB) void attn_sk_kernel(AttnArgs a, SkArgs k) 
   const int lid = xcd * perx + min(xcd, rem) + (wg >> 3);
   const int rs = lid % k.rsplit, v = lid / k.rsplit;
 
-  const AS4 int32_t* sc = (const AS4 int32_t*)k.sched;
   const AS4 int32_t* plen = (const AS4 int32_t*)a.plen;
-  const int T = sc[0], per = sc[1];
-  const long long r0l = (long long)v * per;
-  if (r0l >= T) return;  // uniform per workgroup
-  const int r0 = (int)r0l;
-  const int ntiles = min(T - r0, per);
-  const AS4 int32_t* cp = sc + sk_cursor_offset(B) + 4 * v;
+  int T, per;
   Cursor ic;
-  ic.b = cp[0];
-  ic.g = cp[1];
-  ic.off = cp[2];
+  if (!sk_plan<64 * RB>(a.plen, B, k.cap, ttree, Hkv, k.NV, v, lid == 0 ? k.sched : nullptr, T, per, ic))
+    return;  // empty range (uniform per workgroup)
+  const int r0 = v * per;
+  const int ntiles = min(T - r0, per);
   cursor_seq(ic, plen, k.cap, ttree);
   Cursor cc = ic;
 
@@ -806,26 +806,20 @@ __global__ __launch_bounds__(256) void sk_merge_kernel(AttnArgs a, SkArgs k, int
 
 }  // namespace
 
-size_t sk_sched_bytes(int B, int NV) {
-  return (((size_t)sk_cursor_offset(B) + 4 * (size_t)NV) * sizeof(int32_t) + 255) & ~(size_t)255;
-}
+size_t sk_sched_bytes(int B) { return (((size_t)B + 5) * sizeof(int32_t) + 255) & ~(size_t)255; }
 
 hipError_t launch_attn_sk(const AttnArgs& a, const AttnPlan& p, void* ws, hipStream_t s) {
   if (a.B == 0) return hipSuccess;
   const int NV = p.sk_nv, rsplit = p.rsplit, RW = 256;
   SkArgs k;
-  k.sched = (const int32_t*)ws;
-  const size_t sb = sk_sched_bytes(a.B, NV);
+  k.sched = (int32_t*)ws;
+  const size_t sb = sk_sched_bytes(a.B);
   const size_t slots = (size_t)2 * NV * rsplit * RW;
   k.po = (float*)((char*)ws + sb);
   k.pml = (float*)((char*)ws + sb + ((slots * a.D * sizeof(float) + 255) & ~(size_t)255));
   k.rsplit = rsplit;
   k.NV = NV;
   k.cap = p.cap;
-  hipLaunchKernelGGL(sk_sched_kernel, dim3(1), dim3(1024), 0, s, a.plen, a.B, a.n, p.cap, a.Hkv, NV,
-                     (int32_t*)ws);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   const dim3 grid(NV * rsplit), block(512 / kSkQB);
   constexpr int RB = 8 / kSkQB;
   // fp8 cache: a 6-stage fp8 ring plus the bf16 tile buffer (128 KB at D = 128)
@@ -841,7 +835,7 @@ hipError_t launch_attn_sk(const AttnArgs& a, const AttnPlan& p, void* ws, hipStr
     hipLaunchKernelGGL((attn_sk_kernel<true, false, 128, kSkQB, RB, 4>), grid, block, 0, s, a, k);
   else
     hipLaunchKernelGGL((attn_sk_kernel<false, false, 128, kSkQB, RB, 4>), grid, block, 0, s, a, k);
-  e = hipGetLastError();
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int chunks = RW / 64;
   if (a.f16)

@@ -97,7 +97,7 @@ int plan_attention(const tv_attn_desc* d, AttnPlan* p, int cus) {
       p->rsplit = (int)rs;
       p->sk_nv = (int)(rs >= cus ? 1 : cus / rs);
       const size_t slots = (size_t)2 * p->sk_nv * p->rsplit * 256;
-      p->ws_bytes = tv::sk_sched_bytes(d->B, p->sk_nv) + ((slots * d->D * sizeof(float) + 255) & ~(size_t)255) +
+      p->ws_bytes = tv::sk_sched_bytes(d->B) + ((slots * d->D * sizeof(float) + 255) & ~(size_t)255) +
                     ((slots * 2 * sizeof(float) + 255) & ~(size_t)255);
       return TV_OK;
     }

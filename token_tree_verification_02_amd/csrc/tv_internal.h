@@ -64,7 +64,7 @@ struct AttnArgs {
 
 hipError_t launch_attn_bf16(const AttnArgs& a, const AttnPlan& p, hipStream_t s);
 hipError_t launch_attn_f32(const AttnArgs& a, const AttnPlan& p, hipStream_t s);
-size_t sk_sched_bytes(int B, int NV);
+size_t sk_sched_bytes(int B);
 hipError_t launch_attn_sk(const AttnArgs& a, const AttnPlan& p, void* ws, hipStream_t s);
 hipError_t launch_merge(const AttnArgs& a, const AttnPlan& p, int out_dtype, hipStream_t s);
 hipError_t launch_tree_build(int B, int n, const int32_t* parent, const int32_t* depth,
