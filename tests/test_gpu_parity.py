@@ -107,6 +107,11 @@ SMALL = {
     "fp8_n256": W.config(3, B=2, n=256, Hq=8, Hkv=8, tree="random", max_depth=40, L_lo=50, L_hi=300, vocab=0,
                          kv="fp8"),
     "fp8_sk_d64": W.config(4, B=2, D=64, L_lo=40, L_hi=1500, vocab=0, kv="fp8"),
+    # many-row kernel over more sequences than one 512-thread scan covers: the tile schedule
+    # each workgroup derives takes several passes; short and empty prefixes split most items
+    "sk_600_seqs": W.config(4, B=600, n=17, Hq=8, Hkv=1, L_lo=0, L_hi=90, vocab=0),
+    "sk_1100_seqs_contig": W.config(3, B=1100, n=20, Hq=8, Hkv=1, tree="random", max_depth=5, L_lo=0, L_hi=70,
+                                    Lmax=80, vocab=0),
 }
 
 
