@@ -333,7 +333,10 @@ def main():
     attn_gbs = refb["attn_bytes"] / t_attn / 1e9
     peak_tf = BF16_PEAK_TFLOPS if W.is16(cfg.dtype) else FP32_PEAK_TFLOPS  # fp16 dense MFMA peak = bf16's
     mfma_pct = refb["attn_flops"] / t_attn / 1e12 / peak_tf * 100
-    traffic = load_traffic(cfg.name)
+    # the workload as measured: element type and cache format are part of its name, so a
+    # counter summary is only used for the variant it was taken on
+    wname = cfg.name + ("_f16" if cfg.dtype == "f16" else "") + ("_fp8kv" if cfg.kv == "fp8" else "")
+    traffic = load_traffic(wname)
     # the binding resource is the one whose peak takes longer for the algorithmic work:
     # HBM bytes at 8 TB/s, or the products at the dense matrix peak (fp32: the vector ALUs)
     t_hbm = refb["attn_bytes"] / (HBM_PEAK_GBS * 1e9)
@@ -353,7 +356,7 @@ def main():
         "metric": METRIC, "value": round(value, 1), "unit": "verified tree tokens/s", "n_gpus": 1,
         "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic (seeded, N(0,1) Q/K/V)",
-        "config": {"workload": cfg.name + ("_fp8kv" if cfg.kv == "fp8" else ""), "B": cfg.B, "n": cfg.n,
+        "config": {"workload": wname, "B": cfg.B, "n": cfg.n,
                    "Hq": cfg.Hq, "Hkv": cfg.Hkv, "D": cfg.D, "kv_cache": cfg.kv or cfg.dtype,
                    "prefix_len": [cfg.L_lo, cfg.L_hi], "paged": cfg.paged, "vocab": cfg.vocab,
                    "input_copies": R, "launch": "eager" if args.eager else "hip_graph"},

@@ -129,7 +129,15 @@ __global__ __launch_bounds__(64 * RB * KS) void attn_bf16_kernel(AttnArgs a, int
         bad |= (id < 0 || id >= a.num_blocks);
       }
     }
-    bad = __syncthreads_or(bad);
+    // workgroup OR through the first LDS word (the ring is not in use yet), so
+    // the kernel needs no LDS beyond its ring
+    int AS3* flag = (int AS3*)smem;
+    if (tid == 0) *flag = 0;
+    __syncthreads();
+    if (bad) *flag = 1;
+    __syncthreads();
+    bad = *flag;
+    __syncthreads();  // read by every thread before the ring is written
     if (tid == 0) a.status[b] = bad ? TV_EINVAL : TV_OK;
   }
 
@@ -576,7 +584,7 @@ hipError_t launch_cfg(const AttnArgs& a, const AttnPlan& p, hipStream_t s) {
 
 template <int D>
 hipError_t launch_d(const AttnArgs& a, const AttnPlan& p, hipStream_t s) {
-  if (p.rb == 1) return launch_cfg<D, 1, 3, 32, 3, 3, 4>(a, p, s);
+  if (p.rb == 1) return launch_cfg<D, 1, 5, 32, 2, 5, 2>(a, p, s);
   if (p.rb == 2) return launch_cfg<D, 2, 2, 32, 4, 2, 6>(a, p, s);
   if (p.rb == 4) return launch_cfg<D, 4, 1, 64, 4, 1, 6>(a, p, s);
   return launch_cfg<D, 8, 1, 64, 4, 1, 4>(a, p, s);

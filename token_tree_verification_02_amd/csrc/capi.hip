@@ -82,7 +82,7 @@ int plan_attention(const tv_attn_desc* d, AttnPlan* p, int cus) {
   }
   const int qb = (p->rows + 31) / 32;
   if (qb <= 1) {
-    p->rb = 1, p->ks = 3, p->tk = 32;
+    p->rb = 1, p->ks = 5, p->tk = 32;
   } else if (qb <= 2) {
     p->rb = 2, p->ks = 2, p->tk = 32;
   } else if (qb <= 4) {
