@@ -107,6 +107,15 @@ SMALL = {
     "fp8_n256": W.config(3, B=2, n=256, Hq=8, Hkv=8, tree="random", max_depth=40, L_lo=50, L_hi=300, vocab=0,
                          kv="fp8"),
     "fp8_sk_d64": W.config(4, B=2, D=64, L_lo=40, L_hi=1500, vocab=0, kv="fp8"),
+    # bf16 / fp16 few-row plans for 33-64 rows (8 waves: 2 row waves x 4 key-split groups) and
+    # 65-128 rows (8 waves: 4 row waves x 2 key-split groups): paged, chunked, D = 64, fp16
+    "rows64_paged": W.config(4, B=3, Hq=16, Hkv=8, L_lo=100, L_hi=900),
+    "rows64_d64_chunks": W.config(4, B=1, Hq=16, Hkv=8, D=64, L_lo=5000, L_hi=5000, vocab=0),
+    "rows64_f16": W.config(4, B=2, Hq=16, Hkv=8, dtype="f16", L_lo=100, L_hi=1200, vocab=0),
+    "rows96": W.config(3, B=2, n=32, Hq=24, Hkv=8, tree="random", max_depth=6, L_lo=333, L_hi=700, vocab=0),
+    "rows128_d64_chunks": W.config(3, B=1, n=16, tree="random", max_depth=4, D=64, L_lo=6000, L_hi=6000,
+                                   Lmax=6000, vocab=0),
+    "rows128_f16_paged": W.config(4, B=2, n=16, dtype="f16", L_lo=50, L_hi=2000, vocab=0),
     # many-row kernel over more sequences than one 512-thread scan covers: the tile schedule
     # each workgroup derives takes several passes; short and empty prefixes split most items
     "sk_600_seqs": W.config(4, B=600, n=17, Hq=8, Hkv=1, L_lo=0, L_hi=90, vocab=0),

@@ -561,15 +561,15 @@ __global__ __launch_bounds__(64 * RB * KS) void attn_bf16_kernel(AttnArgs a, int
   }
 }
 
-// KS8, S8: key-split groups and ring depth of the fp8 variant; its stages are
-// half the size, so the same LDS holds more groups (waves) or more tiles
-template <int D, int RB, int KS, int TK, int S, int KS8, int S8>
+// KS8, S8, TK8: key-split groups, ring depth and tile keys of the fp8 variant; its
+// stages are half the size, so the same LDS holds more groups (waves) or more tiles
+template <int D, int RB, int KS, int TK, int S, int KS8, int S8, int TK8 = TK>
 hipError_t launch_cfg(const AttnArgs& a, const AttnPlan& p, hipStream_t s) {
   const int grid = a.B * a.Hkv * p.nchunks * p.rsplit;
   if (grid == 0) return hipSuccess;
   if (a.kv_fp8) {
     if constexpr (RB <= 4)
-      hipLaunchKernelGGL((attn_bf16_kernel<false, true, D, RB, KS8, TK, S8>), dim3(grid), dim3(64 * RB * KS8), 0,
+      hipLaunchKernelGGL((attn_bf16_kernel<false, true, D, RB, KS8, TK8, S8>), dim3(grid), dim3(64 * RB * KS8), 0,
                          s, a, p.rsplit, p.nchunks, p.chunk_len, p.cap);
     else
       return hipErrorInvalidConfiguration;  // the host never plans this
@@ -585,8 +585,8 @@ hipError_t launch_cfg(const AttnArgs& a, const AttnPlan& p, hipStream_t s) {
 template <int D>
 hipError_t launch_d(const AttnArgs& a, const AttnPlan& p, hipStream_t s) {
   if (p.rb == 1) return launch_cfg<D, 1, 5, 32, 2, 5, 2>(a, p, s);
-  if (p.rb == 2) return launch_cfg<D, 2, 2, 32, 4, 2, 6>(a, p, s);
-  if (p.rb == 4) return launch_cfg<D, 4, 1, 64, 4, 1, 6>(a, p, s);
+  if (p.rb == 2) return launch_cfg<D, 2, 4, 32, 2, 2, 6>(a, p, s);
+  if (p.rb == 4) return launch_cfg<D, 4, 2, 32, 4, 1, 6, 64>(a, p, s);
   return launch_cfg<D, 8, 1, 64, 4, 1, 4>(a, p, s);
 }
 

@@ -84,9 +84,9 @@ int plan_attention(const tv_attn_desc* d, AttnPlan* p, int cus) {
   if (qb <= 1) {
     p->rb = 1, p->ks = 5, p->tk = 32;
   } else if (qb <= 2) {
-    p->rb = 2, p->ks = 2, p->tk = 32;
+    p->rb = 2, p->ks = 4, p->tk = 32;
   } else if (qb <= 4) {
-    p->rb = 4, p->ks = 1, p->tk = 64;
+    p->rb = 4, p->ks = 2, p->tk = 32;
   } else {
     // many rows per KV head: 256-row workgroups on a balanced schedule of
     // 64-key tiles (the tile count must fit in int32)
