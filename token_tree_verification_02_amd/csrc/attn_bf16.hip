@@ -585,8 +585,8 @@ hipError_t launch_cfg(const AttnArgs& a, const AttnPlan& p, hipStream_t s) {
 template <int D>
 hipError_t launch_d(const AttnArgs& a, const AttnPlan& p, hipStream_t s) {
   if (p.rb == 1) return launch_cfg<D, 1, 5, 32, 2, 5, 2>(a, p, s);
-  if (p.rb == 2) return launch_cfg<D, 2, 4, 32, 2, 2, 6>(a, p, s);
-  if (p.rb == 4) return launch_cfg<D, 4, 2, 32, 4, 1, 6, 64>(a, p, s);
+  if (p.rb == 2) return launch_cfg<D, 2, 4, 32, 2, 4, 3>(a, p, s);
+  if (p.rb == 4) return launch_cfg<D, 4, 2, 32, 4, 2, 3, 64>(a, p, s);
   return launch_cfg<D, 8, 1, 64, 4, 1, 4>(a, p, s);
 }
 
