@@ -116,6 +116,8 @@ SMALL = {
     "rows128_d64_chunks": W.config(3, B=1, n=16, tree="random", max_depth=4, D=64, L_lo=6000, L_hi=6000,
                                    Lmax=6000, vocab=0),
     "rows128_f16_paged": W.config(4, B=2, n=16, dtype="f16", L_lo=50, L_hi=2000, vocab=0),
+    "fp8_rows128_d64": W.config(4, B=2, n=16, D=64, L_lo=50, L_hi=1500, vocab=0, kv="fp8"),
+    "fp8_rows64_d64_chunks": W.config(4, B=1, Hq=16, Hkv=8, D=64, L_lo=5000, L_hi=5000, vocab=0, kv="fp8"),
     # many-row kernel over more sequences than one 512-thread scan covers: the tile schedule
     # each workgroup derives takes several passes; short and empty prefixes split most items
     "sk_600_seqs": W.config(4, B=600, n=17, Hq=8, Hkv=1, L_lo=0, L_hi=90, vocab=0),
