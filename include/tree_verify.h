@@ -133,9 +133,9 @@ int tree_validate_host(int n, const int32_t* parent, const int32_t* depth);
  * bf16.  Codes are converted to bf16 (exactly) in LDS before the matrix
  * products; k_scale joins the score scale and v_scale multiplies the
  * probabilities entering the PV product (the softmax normaliser sums the
- * unscaled probabilities).  Supported with dtype TV_BF16 (else
- * TV_EUNSUPPORTED), for any number of query rows per KV head; an fp8 cache
- * halves the prefix bytes.
+ * unscaled probabilities).  Supported with dtype TV_BF16 and at most 128
+ * query rows per KV head (n * Hq / Hkv <= 128); otherwise TV_EUNSUPPORTED.
+ * An fp8 cache halves the prefix bytes.
  * ------------------------------------------------------------------------- */
 typedef struct {
   int32_t B, n, Hq, Hkv, D;

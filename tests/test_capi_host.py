@@ -209,8 +209,10 @@ def test_fp8_cache_contract(lib):
     ok = desc(**fp8)                                                     # 21 rows per KV head
     assert tv.workspace_size(ok) != SIZE_MAX
     many = dict(B=32, n=32, Hq=64, Hkv=8)                                # 256 rows: the balanced schedule
-    assert tv.workspace_size(desc(**many, **fp8)) == tv.workspace_size(desc(**many))
-    assert call_attn(lib, desc(**many, **fp8)) == tv.TV_EWORKSPACE       # planned, refused before launch
+    assert tv.workspace_size(desc(**many)) != SIZE_MAX
+    assert tv.workspace_size(desc(**many, **fp8)) == SIZE_MAX            # fp8 is limited to 128 rows per KV head
+    assert call_attn(lib, desc(**many, **fp8)) == tv.TV_EUNSUPPORTED
+    assert tv.workspace_size(desc(B=32, n=16, Hq=64, Hkv=8, **fp8)) != SIZE_MAX   # 128 rows
     assert call_attn(lib, desc(dtype=tv.TV_F16, **fp8)) == tv.TV_EUNSUPPORTED
     assert call_attn(lib, desc(kv_dtype=tv.TV_FP8_E4M3, k_scale=0.0, v_scale=1.0)) == tv.TV_EINVAL
     assert call_attn(lib, desc(kv_dtype=9)) == tv.TV_EUNSUPPORTED

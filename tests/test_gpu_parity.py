@@ -79,6 +79,14 @@ def check_verify(w, d):
     log(f"  verify: path lengths {list(plen[:8])}")
 
 
+# An fp8 cache with more than 128 query rows per KV head (the many-row kernel) is switched off:
+# the library refuses it.  A long back-to-back run of that variant once stopped making progress
+# with the GPU idle; no cause was found in the code, so its cases stay skipped, not deleted.
+FP8_MANY_ROWS = {"fp8_merge_split", "fp8_paged_ragged", "fp8_wide_w2", "fp8_n256", "fp8_sk_d64"}
+FP8_MANY_ROWS_REASON = ("an fp8 cache with more than 128 query rows per KV head is switched off (the library "
+                        "refuses it): a long back-to-back run of that variant once stopped making progress, "
+                        "cause not found")
+
 # ----------------------------------------------------------------------------- small shapes
 SMALL = {
     "tiny_fp32": W.config(1),
@@ -100,7 +108,7 @@ SMALL = {
     "fp8_chunks": W.config(2, B=1, L_lo=7000, L_hi=7000, Lmax=7008, vocab=0, kv="fp8"),
     "fp8_d64": W.config(2, B=2, D=64, L_lo=500, L_hi=777, vocab=0, kv="fp8"),
     # fp8 cache on the many-row (balanced schedule) kernel: split items, paged ragged, two mask
-    # words, four tree tiles, D = 64
+    # words, four tree tiles, D = 64 (skipped: the library refuses this variant, see FP8_MANY_ROWS)
     "fp8_merge_split": W.config(3, B=2, L_lo=2900, L_hi=2900, vocab=0, kv="fp8"),
     "fp8_paged_ragged": W.config(4, B=3, L_lo=100, L_hi=3000, kv="fp8"),
     "fp8_wide_w2": W.config(5, B=3, L_lo=1, L_hi=2000, Lmax=2048, vocab=0, kv="fp8"),
@@ -129,6 +137,8 @@ SMALL = {
 @pytest.mark.parametrize("name", list(SMALL))
 @pytest.mark.parametrize("variant", ["plain", "balanced", "needle"])
 def test_small_parity(name, variant):
+    if name in FP8_MANY_ROWS:
+        pytest.skip(FP8_MANY_ROWS_REASON)
     cfg = SMALL[name]
     if cfg.dtype == "f32" and variant != "plain":
         pytest.skip("variants target the bf16 tolerance")
@@ -251,6 +261,7 @@ def test_full_size_sampled(index):
 
 
 @pytest.mark.slow
+@pytest.mark.skip(reason=FP8_MANY_ROWS_REASON)
 def test_full_size_sampled_fp8_cache():
     """The long-ragged paged workload at full size with an fp8 prefix cache (the
     benchmark's --kv fp8 launch), checked on sampled (sequence, KV head) pairs."""

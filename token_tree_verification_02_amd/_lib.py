@@ -124,6 +124,14 @@ def workspace_size(desc: AttnDesc) -> int:
     return int(load().tree_attention_workspace_size(ctypes.byref(desc)))
 
 
+def checked_workspace_size(desc: AttnDesc) -> int:
+    """workspace_size, raising the library's own error for a descriptor it refuses."""
+    ws = workspace_size(desc)
+    if ws == (1 << 64) - 1:
+        _check(load().tree_attention(ctypes.byref(desc), *([None] * 12), 0, None), "tree_attention")
+    return ws
+
+
 # ----------------------------------------------------------------------------- the library calls
 def tree_build(parent, depth, prefix_len, *, mask=None, pos=None, status=None, stream=None):
     """parent, depth [B][n] int32, prefix_len [B] int32 -> (mask [B][n][W] int64 view of
@@ -159,9 +167,7 @@ def tree_attention(q, k_cache, v_cache, prefix_len, k_tree, v_tree, mask, *, blo
     out = torch.empty_like(q) if out is None else out
     if want_lse and lse is None:
         lse = torch.empty((B, n, Hq), dtype=torch.float32, device=q.device)
-    ws = workspace_size(desc)
-    if ws == (1 << 64) - 1:
-        _check(load().tree_attention(ctypes.byref(desc), *([None] * 12), 0, None), "tree_attention")
+    ws = checked_workspace_size(desc)
     if workspace is None and ws > 0:
         workspace = torch.empty(ws, dtype=torch.uint8, device=q.device)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()

@@ -57,6 +57,11 @@ int check_desc(const tv_attn_desc* d) {
     if (d->dtype != TV_BF16) return fail(TV_EUNSUPPORTED, "an fp8 cache needs dtype TV_BF16");
     if (!(d->k_scale > 0.f) || !(d->v_scale > 0.f) || isinf(d->k_scale) || isinf(d->v_scale))
       return fail(TV_EINVAL, "fp8 cache scales must be finite and > 0");
+    // the many-row (balanced schedule) plan is not offered with an fp8 cache: a long run of
+    // back-to-back calls of that variant once stopped making progress, with no cause found
+    if ((long long)d->n * (d->Hq / d->Hkv) > 128)
+      return fail(TV_EUNSUPPORTED, "an fp8 cache supports at most 128 query rows per KV head (n * Hq / Hkv = %d)",
+                  d->n * (d->Hq / d->Hkv));
   }
   return TV_OK;
 }

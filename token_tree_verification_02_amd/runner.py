@@ -50,7 +50,7 @@ def upload(w: dict, device="cuda") -> dict:
     d["new_len"] = torch.empty((B,), dtype=torch.int32, device=device)
     d["commit_status"] = torch.empty((B,), dtype=torch.int32, device=device)
     desc = attn_desc_of(d)
-    ws = _lib.workspace_size(desc)
+    ws = _lib.checked_workspace_size(desc)
     d["workspace"] = torch.empty(max(ws, 1), dtype=torch.uint8, device=device) if ws else None
     if cfg.vocab and d.get("logits") is not None:
         d["argmax"] = torch.empty((B, n), dtype=torch.int32, device=device)
