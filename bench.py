@@ -1,9 +1,12 @@
 """Benchmark: verified tree tokens/s of one speculative-decoding verification step.
 
 A step is the whole hot path over one batch: tree_build -> tree_attention ->
-tree_verify_greedy, on one GPU, inputs resident in HBM.  Default workload: the
-Llama-7B-shaped layer (batch 8, 32 MHA heads, head dim 128, bf16, 1024-token
-prefix, expansion tree <1,1,3,1,1,1,1,1> = 21 nodes, vocab 32000).
+tree_verify_greedy, on one GPU, inputs resident in HBM.  Default workload: long
+ragged prefixes on a paged cache (batch 32, 64 query / 8 KV heads, head dim 128,
+bf16, prefix lengths uniform in 8192..32768 tokens in 16-token blocks behind a
+shuffled block table, 32-node random trees of depth <= 6, no vocabulary), the
+largest single-GPU attention workload and the one the HBM-roofline goal is set
+on.  Without a vocabulary the step is tree_build -> tree_attention.
 
 Each timed step uses the next of R input copies (R chosen so the copies exceed
 twice the 256 MB last-level cache), the way consecutive layers each bring their
@@ -27,7 +30,7 @@ adds the p10 / median / p90 of single launches, one event between each); `traffi
 was taken on the current kernel source, else null.  `cpu_baseline` times the
 CPU oracle on the same workload.
 
-    python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--config 2]
+    python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--config 4]
 """
 from __future__ import annotations
 
@@ -50,10 +53,14 @@ MALL_BYTES = 256 << 20
 
 
 def kernel_source_hash() -> str:
+    """Hash of everything that decides what tree_attention launches: the attention
+    kernels, the host plan and dispatch (capi.hip), and the compiler flags."""
+    from token_tree_verification_02_amd import build as _build
     h = hashlib.sha256()
-    for f in ("attn_bf16.hip", "attn_sk.hip", "attn_bf16_common.h", "attn_f32.hip", "tv_internal.h"):
+    for f in ("attn_bf16.hip", "attn_sk.hip", "attn_bf16_common.h", "attn_f32.hip", "tv_internal.h", "capi.hip"):
         with open(os.path.join(ROOT, "token_tree_verification_02_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
+    h.update(" ".join(_build.FLAGS[1:]).replace(_build.ROOT, "").encode())
     return h.hexdigest()[:16]
 
 
@@ -98,7 +105,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--config", type=int, default=4)
     ap.add_argument("--dtype", choices=["bf16", "f16"], default=None,
                     help="element type of q/K/V/out/logits (default: the workload's)")
     ap.add_argument("--kv", choices=["fp8"], default=None, help="store the prefix KV cache as fp8 (E4M3) codes")

@@ -33,8 +33,8 @@
  *   - `stream` is a hipStream_t (NULL = the null stream).  Calls return after
  *     host-side validation and kernel enqueue; results are ready when the
  *     stream reaches them.
- *   - Return value: TV_OK, or a tv_status code for an error found on the host
- *     (nothing is enqueued then).  tv_last_error() gives a thread-local
+ *   - Return value: an int holding a tv_status value: TV_OK, or the code of an
+ *     error found on the host (nothing is enqueued then).  tv_last_error() gives a thread-local
  *     message for the last failing call.
  *   - Tree nodes are in a topological order: node 0 is the single root,
  *     parent[u] < u for u >= 1 (BFS and DFS orders both qualify).
@@ -99,6 +99,13 @@ int tree_validate_host(int n, const int32_t* parent, const int32_t* depth);
 
 /* ---------------------------------------------------------------------------
  * tree_attention: O = tree attention of every node over prefix + S_u.
+ *
+ * Defined by the SpecInfer explainer, token-tree structure section: the
+ * attention equation over the ancestor set S_u (the root path of u, u
+ * included) under the topology-aware mask; the cached prefix joins the same
+ * softmax because the mask is kept consistent with KV-cache reuse (its list of
+ * contributions).  Its implementation-points section (kernel fusion) fixes the
+ * precomputed mask taken here as anc_mask.
  *
  * For node u of sequence b and query head h (KV head g = h / (Hq/Hkv)):
  *   O[b][u][h] = sum_j p_j V_j / sum_j p_j,  p_j = exp(s_j - max s),

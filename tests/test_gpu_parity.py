@@ -209,6 +209,31 @@ def test_verify_ties_and_signed_zero():
     assert d["argmax"][0, 0].item() == 5 and d["argmax"][1, 0].item() == 0 and d["argmax"][2, 3].item() == 260
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_verify_nan_rows_stay_in_vocab(dtype):
+    """NaN logits are outside the contract, but the argmax, path and bonus token
+    must still be indices a caller can use to address a table: in [0, V)."""
+    log(f"case verify NaN rows {dtype}")
+    V = 1000
+    cfg = W.config(2, B=3, vocab=V, dtype=dtype, L_lo=16, L_hi=16)
+    w = W.make(cfg, seed=11)
+    lg = (W.bf16_bits_to_f32(w["logits"]) if dtype == "bf16" else w["logits"]).copy()
+    lg[0, :, :] = np.nan                                  # whole rows of NaN
+    lg[1, :, V - 8:] = np.nan                             # the last 16-byte vector of every row
+    lg[2, :, 0:8] = np.nan                                # a thread's first vector
+    w["logits"] = W.f32_to_bf16_bits(lg) if dtype == "bf16" else lg.astype(np.float32)
+    d = runner.upload(w)
+    runner.build(d)
+    runner.verify(d)
+    torch.cuda.synchronize()
+    am = d["argmax"].cpu().numpy()
+    assert ((am >= 0) & (am < V)).all(), am.min()
+    bonus = d["bonus"].cpu().numpy()
+    assert ((bonus >= 0) & (bonus < V)).all()
+    plen = d["path_len"].cpu().numpy()
+    assert ((plen >= 1) & (plen <= cfg.n)).all()
+
+
 def test_invalid_inputs_are_reported_not_read():
     log("case invalid inputs")
     cfg = W.config(4, B=3, L_lo=40, L_hi=300, vocab=0)

@@ -67,19 +67,39 @@ __device__ __forceinline__ int vswz(int row) {  // 4 consecutive rows x 4 granul
 // HBM -> LDS copy of 16 bytes per lane; lane l lands at lds_line + 16*l.  Issued
 // through asm so the compiler does not add its own (full) waits around it; the
 // kernel waits with explicit vmcnt counts instead.
+//
+// The LDS address comes from M0.  Two rules of the GFX9 family apply, and the
+// compiler cannot apply them inside asm:
+//  - an LDS DMA that reads M0 in the cycle after a scalar write of M0 may see the
+//    old value, so one wait state (s_nop 0) separates them, as the compiler's own
+//    hazard pass does when it emits this pair;
+//  - M0 is a register the compiler reserves, so the asm restores the value it
+//    found instead of declaring it clobbered.
 __device__ __forceinline__ void dma16(const void* gaddr, uint32_t lds_line) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gaddr),
-               "s"(__builtin_amdgcn_readfirstlane(lds_line))
-               : "m0");
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(gaddr), "s"(__builtin_amdgcn_readfirstlane(lds_line)));
 }
 // Same with a wave-uniform 64-bit base and a per-lane 32-bit byte offset.
 __device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, uint32_t lds_line) {
   const uint64_t b = (uint64_t)sbase;
   const uint64_t ub = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
                       (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(ub),
-               "s"(__builtin_amdgcn_readfirstlane(lds_line))
-               : "m0");
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(ub), "s"(__builtin_amdgcn_readfirstlane(lds_line)));
 }
 
 template <int N>

@@ -187,23 +187,17 @@ __device__ __forceinline__ float sk_colmax(const f32x16& s) {
 
 // Probabilities of 16 scores against the running max (log2 domain), rounded to
 // the 16-bit type (the PV operand); their sum is added to l with a 16-bit dot
-// product.  SC (fp8 cache tiles): the probabilities are multiplied by vsc, the
-// value scale, before rounding, so l sums vsc * p (the caller divides it out).
-template <class E, bool SC>
-__device__ __forceinline__ void sk_probs(const f32x16& s, typename E::V8 (&P)[2], float& l, float sl2, float msub,
-                                         float vsc) {
+// product.
+template <class E>
+__device__ __forceinline__ void sk_probs(const f32x16& s, typename E::V8 (&P)[2], float& l, float sl2, float msub) {
   const typename E::V2 ones = {E::cvt(1.0f), E::cvt(1.0f)};
 #pragma unroll
   for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
       typename E::V2 pr;
-      float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * h2 + e], sl2, -msub));
-      float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * h2 + e + 1], sl2, -msub));
-      if constexpr (SC) {
-        p0 *= vsc;
-        p1 *= vsc;
-      }
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * h2 + e], sl2, -msub));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * h2 + e + 1], sl2, -msub));
       pr[0] = E::cvt(p0);
       pr[1] = E::cvt(p1);
       l = E::dot2(pr, ones, l);
@@ -215,12 +209,10 @@ __device__ __forceinline__ void sk_probs(const f32x16& s, typename E::V8 (&P)[2]
 // Running-max update for one query block (log2 domain): the accumulators are
 // rescaled only when the block max exceeds the running max by more than kTau.
 template <int D>
-__device__ __forceinline__ void sk_rescale(f32x16 (&Oq)[D / 32], float& m_run, float& lsum, float& ltree,
-                                           float mx) {
+__device__ __forceinline__ void sk_rescale(f32x16 (&Oq)[D / 32], float& m_run, float& lsum, float mx) {
   const float m_new = fmaxf(m_run, mx);
   const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
   lsum *= alpha;
-  ltree *= alpha;
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
@@ -286,15 +278,13 @@ __device__ __forceinline__ void sk_qk(const char AS3* Kr, int kb, const typename
 // the VALU (in-flight MFMAs overlap later independent instructions, across the
 // rescale branch too); then per block QK -> max -> (rare) rescale -> softmax
 // -> PV, and the other wave on the SIMD fills the gaps.
-// slt: the tile's score scale (log2 domain).  FP8 (fp8 cache): prefix tiles
-// scale their probabilities by vsc into lsum; tree tiles (bf16) sum into ltree.
-template <class E, int D, int QB, bool MASKED, bool FP8>
+// slt: the score scale (log2 domain).
+template <class E, int D, int QB, bool MASKED>
 __device__ __forceinline__ void sk_tile(const char AS3* Kr, const char AS3* Vr,
                                         const typename E::V8 (&qop)[QB][D / 16],
                                         f32x16 (&O)[QB][D / 32], float (&m_run)[QB], float (&lsum)[QB],
-                                        float (&ltree)[QB], const uint32_t (&kofs)[D / 16],
-                                        const uint32_t (&vofs)[D / 32], float slt, float vsc, int lim, bool tree,
-                                        const uint64_t (&bits)[QB], int hh) {
+                                        const uint32_t (&kofs)[D / 16], const uint32_t (&vofs)[D / 32], float slt,
+                                        int lim, bool tree, const uint64_t (&bits)[QB], int hh) {
   static_assert(QB == 1, "one query block per wave");
   f32x16 Sa[2][1];
   sk_qk<E, D, 1>(Kr, 0, qop, kofs, Sa[0]);
@@ -303,27 +293,15 @@ __device__ __forceinline__ void sk_tile(const char AS3* Kr, const char AS3* Vr,
   for (int kb = 0; kb < 2; ++kb) {
     if constexpr (MASKED) sk_mask(Sa[kb][0], kb, lim, tree, bits[0], hh);
     const float mx = sk_colmax(Sa[kb][0]) * slt;  // scale > 0 commutes with max
-    if (__builtin_expect(__any(mx > m_run[0] + kTau), 0)) sk_rescale<D>(O[0], m_run[0], lsum[0], ltree[0], mx);
+    if (__builtin_expect(__any(mx > m_run[0] + kTau), 0)) sk_rescale<D>(O[0], m_run[0], lsum[0], mx);
     typename E::V8 P[1][2];
     const float msub = (m_run[0] == -INFINITY) ? 0.f : m_run[0];
-    if constexpr (FP8) {
-      if (MASKED && tree)
-        sk_probs<E, false>(Sa[kb][0], P[0], ltree[0], slt, msub, 1.f);
-      else
-        sk_probs<E, true>(Sa[kb][0], P[0], lsum[0], slt, msub, vsc);
-    } else {
-      sk_probs<E, false>(Sa[kb][0], P[0], lsum[0], slt, msub, 1.f);
-    }
+    sk_probs<E>(Sa[kb][0], P[0], lsum[0], slt, msub);
     sk_pv<E, D, 1>(Vr, kb, P, O, vofs);
   }
 }
 
-// FP8: the prefix cache holds fp8 E4M3 codes.  Their tiles stream through an
-// S-stage fp8 ring; before a tile is used each wave converts the lines it
-// loaded to bf16 (exact) into one bf16 tile buffer, at the positions of the
-// bf16 layout, so the operand reads are unchanged.  Tree tiles (bf16) load
-// straight into that buffer when they are used.
-template <bool F16, bool FP8, int D, int QB, int RB, int S>
+template <bool F16, int D, int QB, int RB, int S>
 __global__ __launch_bounds__(64 * RB) void attn_sk_kernel(AttnArgs a, SkArgs k) {
   using E = Elt<F16>;
   constexpr int RW = 32 * QB * RB;          // query rows per workgroup
@@ -336,17 +314,9 @@ __global__ __launch_bounds__(64 * RB) void attn_sk_kernel(AttnArgs a, SkArgs k) 
   constexpr int RPL = 1024 / ROWB;          // token rows per line
   constexpr int GPR = D / 8;                // 16-byte granules per row
   constexpr int SD = D / 16, DB = D / 32;
-  constexpr int STAGE8 = 2 * kTK * D;       // fp8 tile: K and V, one byte per element
-  constexpr int LINES8 = STAGE8 / 1024;
-  constexpr int HL8 = LINES8 / 2;
-  constexpr int LPW8 = LINES8 / RB;
-  constexpr int RPL8 = 1024 / D;            // fp8 token rows per line
-  constexpr int GPR8 = D / 16;              // 16-byte granules per fp8 row
-  constexpr int BUF = FP8 ? S * STAGE8 : 0;  // fp8 cache: offset of the bf16 tile buffer
-  constexpr int WAITN = (S - 2) * (FP8 ? LPW8 : LPW);  // loads a wave may leave in flight
+  constexpr int WAITN = (S - 2) * LPW;      // loads a wave may leave in flight
   static_assert(HL % RB == 0 && LPW * (S - 2) < 64, "pipeline shape");
-  static_assert(!FP8 || (LINES8 % RB == 0 && WAITN < 64 && !F16), "fp8 pipeline shape");
-  __shared__ __attribute__((aligned(1024))) char smem[FP8 ? S * STAGE8 + STAGE : S * STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem[S * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int rb = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -379,7 +349,6 @@ __global__ __launch_bounds__(64 * RB) void attn_sk_kernel(AttnArgs a, SkArgs k) 
   const char* zsrc = zero + lane * 16;
   const uint32_t ring = (uint32_t)(uintptr_t)(AS3 void*)smem;
   const AS4 int32_t* btc = (const AS4 int32_t*)a.bt;
-  const int paged = a.paged, max_blocks = a.max_blocks, num_blocks = a.num_blocks, Lmax = a.Lmax;
 
   // per-lane DMA geometry: line q*RB + rb of the tile belongs to this wave; the
   // lane's token row within the tile and its source granule (swizzled) follow
@@ -467,87 +436,6 @@ __global__ __launch_bounds__(64 * RB) void attn_sk_kernel(AttnArgs a, SkArgs k) 
     }
   };
 
-  // fp8 cache: DMA of this wave's lines of the fp8 prefix tile at cursor c into
-  // fp8 stage st (!live, or a tree tile: zeros in their place, so every wave
-  // issues the same number of loads per tile)
-  auto issue8 = [=](const Cursor& c, bool live, int st) {
-    const uint32_t gbase = ring + st * STAGE8;
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
-    if (!live || c.off >= c.tpre) {
-#pragma unroll
-      for (int q = 0; q < LPW8; ++q) dma16(zero + ln * 16, gbase + (q * RB + rb) * 1024);
-      return;
-    }
-    const int b = c.b, g = c.g;
-    const int tstart = c.off * kTK;
-    const int gran = ln % GPR8;
-    int id0 = -1, id1 = -1, id2 = -1, id3 = -1;
-    if (paged) {
-      const int b0 = tstart >> 4;
-      const AS4 int32_t* row = btc + (size_t)b * max_blocks;
-      id0 = b0 < max_blocks ? row[b0] : -1;
-      id1 = b0 + 1 < max_blocks ? row[b0 + 1] : -1;
-      id2 = b0 + 2 < max_blocks ? row[b0 + 2] : -1;
-      id3 = b0 + 3 < max_blocks ? row[b0 + 3] : -1;
-    }
-#pragma unroll
-    for (int q = 0; q < LPW8; ++q) {
-      const int line = q * RB + rb;
-      const bool isv = line >= HL8;
-      const int l0 = (isv ? line - HL8 : line) * RPL8;  // first key row of the line (a line is within one block)
-      const int r = l0 + ln / GPR8;                      // the lane's key row within the tile
-      const int j = tstart + r;
-      bool ok = j < c.L;
-      const char* src;
-      if (paged) {
-        const int kq = l0 >> 4;
-        const int blk = kq == 0 ? id0 : (kq == 1 ? id1 : (kq == 2 ? id2 : id3));
-        ok = ok && blk >= 0 && blk < num_blocks;
-        src = (isv ? vc : kc) + (((size_t)blk * Hkv + g) * TV_PAGE + (j & 15)) * D + gran * 16;
-      } else {
-        src = (isv ? vc : kc) + (((size_t)b * Hkv + g) * Lmax + j) * D + gran * 16;
-      }
-      dma16(ok ? src : zero + ln * 16, gbase + line * 1024);
-    }
-  };
-  // fp8 cache: this wave's lines of fp8 stage st, converted to bf16 into the
-  // tile buffer at the bf16 layout's positions of each key row and granule
-  auto convert8 = [=](int st) {
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
-    const int gran = ln % GPR8;
-#pragma unroll
-    for (int q = 0; q < LPW8; ++q) {
-      const int line = q * RB + rb;
-      const bool isv = line >= HL8;
-      const int r = (isv ? line - HL8 : line) * RPL8 + ln / GPR8;
-      const u32x4 x = *(const u32x4 AS3*)((const char AS3*)smem + st * STAGE8 + line * 1024 + ln * 16);
-      u32x4 lo, hi;  // bf16 elements 0..7 and 8..15 of the 16 fp8 codes (exact: E4M3 fits bf16)
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        // scale 1: the instruction's scale operand acts as a power of two only
-        // (an E8M0 block scale), so the per-tensor scales are applied to the
-        // scores and probabilities instead
-        const auto p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[w], 1.0f, false);
-        const auto p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[w], 1.0f, true);
-        const uint32_t w0 = __builtin_bit_cast(uint32_t, p0), w1 = __builtin_bit_cast(uint32_t, p1);
-        if (w < 2) {
-          lo[2 * w] = w0;
-          lo[2 * w + 1] = w1;
-        } else {
-          hi[2 * (w - 2)] = w0;
-          hi[2 * (w - 2) + 1] = w1;
-        }
-      }
-      const int lrow = isv ? r : perm_row(r);  // K rows sit at perm_row(key)
-      const int sw = isv ? vswz<D>(lrow) : kswz<D>(lrow);
-      char AS3* r0 = (char AS3*)smem + BUF + (isv ? REG : 0) + lrow * ROWB;
-      *(u32x4 AS3*)(r0 + (((2 * gran) ^ sw) << 4)) = lo;
-      *(u32x4 AS3*)(r0 + (((2 * gran + 1) ^ sw) << 4)) = hi;
-    }
-  };
-
   // per-lane LDS read offsets
   uint32_t kofs[SD], vofs[DB];
 #pragma unroll
@@ -569,10 +457,7 @@ __global__ __launch_bounds__(64 * RB) void attn_sk_kernel(AttnArgs a, SkArgs k) 
 #pragma unroll
   for (int i = 0; i < S - 1; ++i) {
     const bool live = i < ntiles;
-    if constexpr (FP8)
-      issue8(ic, live, i);
-    else
-      issue(ic, live, ring + i * STAGE);
+    issue(ic, live, ring + i * STAGE);
     if (live) cursor_next(ic, plen, B, Hkv, k.cap, ttree);
   }
 
@@ -605,12 +490,11 @@ __global__ __launch_bounds__(64 * RB) void attn_sk_kernel(AttnArgs a, SkArgs k) 
     }
     wait_vmcnt<0>();  // queries and masks are in registers (drains the ring once per segment)
     f32x16 O[QB][DB];
-    float m_run[QB], lsum[QB], ltree[QB];
+    float m_run[QB], lsum[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       m_run[qb] = -INFINITY;
       lsum[qb] = 0.f;
-      ltree[qb] = 0.f;
     }
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
@@ -629,26 +513,12 @@ __global__ __launch_bounds__(64 * RB) void attn_sk_kernel(AttnArgs a, SkArgs k) 
       lds_barrier();        // ... everyone's, and everyone left tile it-1
       {
         const bool live = it + S - 1 < ntiles;
-        if constexpr (FP8)
-          issue8(ic, live, (it + S - 1) % S);
-        else
-          issue(ic, live, ring + ((it + S - 1) % S) * STAGE);
+        issue(ic, live, ring + ((it + S - 1) % S) * STAGE);
         if (live) cursor_next(ic, plen, B, Hkv, k.cap, ttree);
       }
       const int off = cc.off + j;
       const int st = it % S;
-      if constexpr (FP8) {
-        if (MASKED && off >= cc.tpre) {  // tree tile (bf16): straight into the buffer, waited here
-          Cursor tc = cc;
-          tc.off = off;
-          issue(tc, true, ring + BUF);
-          wait_vmcnt<0>();
-        } else {
-          convert8(st);
-        }
-        lds_barrier();  // the buffer holds the whole tile
-      }
-      const char AS3* Kr = (const char AS3*)smem + (FP8 ? BUF : st * STAGE);
+      const char AS3* Kr = (const char AS3*)smem + st * STAGE;
       const char AS3* Vr = Kr + REG;
       uint64_t bits[QB];
       int lim = kTK;
@@ -663,11 +533,7 @@ __global__ __launch_bounds__(64 * RB) void attn_sk_kernel(AttnArgs a, SkArgs k) 
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) bits[qb] = 0ull;
       }
-      // fp8 prefix tiles hold unscaled codes: the key scale joins the score scale
-      // and the value scale multiplies the probabilities entering the PV product
-      const float slt = (FP8 && !tree) ? sl2 * a.k_scale : sl2;
-      sk_tile<E, D, QB, MASKED, FP8>(Kr, Vr, qop, O, m_run, lsum, ltree, kofs, vofs, slt, a.v_scale, lim, tree,
-                                     bits, hh);
+      sk_tile<E, D, QB, MASKED>(Kr, Vr, qop, O, m_run, lsum, kofs, vofs, sl2, lim, tree, bits, hh);
       ++it;
     };
     const int nfull = max(0, min(seg_len, cc.L / kTK - cc.off));  // full prefix tiles come first
@@ -679,8 +545,7 @@ __global__ __launch_bounds__(64 * RB) void attn_sk_kernel(AttnArgs a, SkArgs k) 
     const int slot = 2 * v + (seg == 0 ? 0 : 1);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      // fp8 cache: the prefix sum holds v_scale * p; the tree keys' sum is plain
-      const float lp = FP8 ? lsum[qb] / a.v_scale + ltree[qb] : lsum[qb];
+      const float lp = lsum[qb];
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lp), __float_as_uint(lp), false, false);
       const float ltot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
       const int row = rowbase + 32 * qb + col;
@@ -822,18 +687,17 @@ hipError_t launch_attn_sk(const AttnArgs& a, const AttnPlan& p, void* ws, hipStr
   k.cap = p.cap;
   const dim3 grid(NV * rsplit), block(512 / kSkQB);
   constexpr int RB = 8 / kSkQB;
-  // an fp8 cache is not planned here (the host refuses it for more than 128 rows per KV
-  // head); the kernel's fp8 path (a 6-stage fp8 ring plus a bf16 tile buffer) is kept but
-  // not instantiated
+  // an fp8 cache has no many-row plan: the host refuses it for more than 128 query rows
+  // per KV head, so it cannot reach this launcher
   if (a.kv_fp8) return hipErrorInvalidConfiguration;
   if (a.D == 64 && a.f16)
-    hipLaunchKernelGGL((attn_sk_kernel<true, false, 64, kSkQB, RB, 4>), grid, block, 0, s, a, k);
+    hipLaunchKernelGGL((attn_sk_kernel<true, 64, kSkQB, RB, 4>), grid, block, 0, s, a, k);
   else if (a.D == 64)
-    hipLaunchKernelGGL((attn_sk_kernel<false, false, 64, kSkQB, RB, 4>), grid, block, 0, s, a, k);
+    hipLaunchKernelGGL((attn_sk_kernel<false, 64, kSkQB, RB, 4>), grid, block, 0, s, a, k);
   else if (a.f16)
-    hipLaunchKernelGGL((attn_sk_kernel<true, false, 128, kSkQB, RB, 4>), grid, block, 0, s, a, k);
+    hipLaunchKernelGGL((attn_sk_kernel<true, 128, kSkQB, RB, 4>), grid, block, 0, s, a, k);
   else
-    hipLaunchKernelGGL((attn_sk_kernel<false, false, 128, kSkQB, RB, 4>), grid, block, 0, s, a, k);
+    hipLaunchKernelGGL((attn_sk_kernel<false, 128, kSkQB, RB, 4>), grid, block, 0, s, a, k);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int chunks = RW / 64;

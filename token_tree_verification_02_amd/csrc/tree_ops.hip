@@ -156,7 +156,9 @@ __global__ __launch_bounds__(256) void argmax_kernel(const void* __restrict__ lo
         e = __uint_as_float(w1) == vbest ? 1 : e;
         e = __uint_as_float(w0) == vbest ? 0 : e;
       }
-      bi = vidx * EPV + e;
+      // no element compares equal only when vbest is NaN (out of contract): the
+      // index still stays inside the winning vector, so inside [0, V)
+      bi = vidx * EPV + min(e, EPV - 1);
       bv = vbest;
     }
     done = nv * EPV;
