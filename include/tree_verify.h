@@ -41,7 +41,9 @@
  *   - Ancestor masks: W = ceil(n/64) uint64 words per node; bit (v & 63) of
  *     word (v >> 6) is set iff node v is on the path root..u (u included).
  *   - The library allocates no device memory.  tree_attention takes a caller
- *     workspace whose size tree_attention_workspace_size() reports.
+ *     workspace whose size tree_attention_workspace_size() reports;
+ *     tree_attention_noalloc instead uses a fixed scratch array that the
+ *     library's code object holds in each GPU's memory from load time.
  */
 #ifndef TREE_VERIFY_H
 #define TREE_VERIFY_H
@@ -171,6 +173,36 @@ int tree_attention(const tv_attn_desc* desc, const void* q,
                    const uint64_t* anc_mask, void* out, float* lse,
                    int32_t* status, void* workspace, size_t workspace_bytes,
                    void* stream);
+
+/* ---------------------------------------------------------------------------
+ * tree_attention_noalloc: tree_attention with no workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).
+ *
+ * Same arguments (minus workspace), layouts, results and error behaviour as
+ * tree_attention, computed by the same kernels.  The partial results that
+ * tree_attention keeps in the caller's workspace go to a scratch array the
+ * library holds in each GPU's memory, TV_NOALLOC_SCRATCH_BYTES long (every
+ * plan of the numbered workloads fits; tree_attention_workspace_size gives a
+ * descriptor's need).  A descriptor needing more returns TV_EWORKSPACE before
+ * anything is enqueued.  The call itself allocates nothing: the array exists
+ * from the library's load until the process ends, and its address on the
+ * current device is looked up once, on the first call there.
+ *
+ * The array of the CURRENT device is used, so `stream` must belong to it.
+ * All calls on one GPU share that array: two calls that may run at the same
+ * time on one GPU (different streams, or different host threads) race and
+ * may return wrong results.  Calls in one stream are ordered and safe.
+ * Nothing in the array needs to start at zero.
+ * ------------------------------------------------------------------------- */
+#define TV_NOALLOC_SCRATCH_BYTES ((size_t)72 << 20)
+
+int tree_attention_noalloc(const tv_attn_desc* desc, const void* q,
+                           const void* k_cache, const void* v_cache,
+                           const int32_t* block_table, const int32_t* prefix_len,
+                           const void* k_tree, const void* v_tree,
+                           const uint64_t* anc_mask, void* out, float* lse,
+                           int32_t* status, void* stream);
 
 /* ---------------------------------------------------------------------------
  * tree_verify_greedy: greedy verification of the token tree.

@@ -217,3 +217,20 @@ def test_fp8_cache_contract(lib):
     assert call_attn(lib, desc(kv_dtype=tv.TV_FP8_E4M3, k_scale=0.0, v_scale=1.0)) == tv.TV_EINVAL
     assert call_attn(lib, desc(kv_dtype=9)) == tv.TV_EUNSUPPORTED
     assert call_commit(lib, desc(**fp8)) == tv.TV_EUNSUPPORTED
+
+
+def test_noalloc_host_checks(lib):
+    """tree_attention_noalloc refuses, before any HIP call, descriptors that are invalid or
+    need more scratch than it holds; the limit covers the numbered workloads."""
+    p = [0x100000] * 11
+    call = lambda d: lib.tree_attention_noalloc(ctypes.byref(d), *p, None)
+    assert call(desc(Hq=30, Hkv=8)) == tv.TV_EUNSUPPORTED
+    big = desc(B=1, n=256, Hq=1024, Hkv=1)                    # 262144 rows per KV head
+    assert tv.workspace_size(big) > tv.TV_NOALLOC_SCRATCH_BYTES
+    assert call(big) == tv.TV_EWORKSPACE
+    assert "scratch" in tv.last_error()
+    for d in (desc(B=32, n=32, Hq=64, Hkv=8, paged=True, max_blocks=2048, num_blocks=41000),
+              desc(B=16, n=64, Hq=64, Hkv=8, Lmax=2048), desc(B=64, n=128, Hq=32, Hkv=8, Lmax=8192),
+              desc(B=8, n=21, Hq=32, Hkv=32, Lmax=1024)):
+        assert tv.workspace_size(d) <= tv.TV_NOALLOC_SCRATCH_BYTES
+    assert lib.tree_attention_noalloc(ctypes.byref(desc(B=0)), *([None] * 11), None) == tv.TV_OK

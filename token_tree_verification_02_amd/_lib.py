@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_PKG, "libtreeverify.so")
 TV_OK, TV_EINVAL, TV_ETOPOLOGY, TV_EUNSUPPORTED, TV_EWORKSPACE, TV_EHIP = range(6)
 TV_F32, TV_BF16, TV_F16, TV_FP8_E4M3 = 0, 1, 2, 3
 TV_NMAX, TV_PAGE, TV_MSS_VMAX, TV_TOPK_MAX, TV_MERGE_MMAX = 256, 16, 1 << 20, 16, 64
+TV_NOALLOC_SCRATCH_BYTES = 72 << 20
 
 _c_int, _c_float, _vp, _size_t = ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
 
@@ -47,6 +48,8 @@ SIGNATURES = {
     "tree_attention_workspace_size": (_size_t, [ctypes.POINTER(AttnDesc)]),
     "tree_attention": (_c_int, [ctypes.POINTER(AttnDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                 _vp, _vp, _size_t, _vp]),
+    "tree_attention_noalloc": (_c_int, [ctypes.POINTER(AttnDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                        _vp, _vp, _vp]),
     "tree_verify_greedy": (_c_int, [_c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "tree_verify_stochastic_workspace_size": (_size_t, [_c_int, _c_int, _c_int]),
     "tree_verify_stochastic": (_c_int, [_c_int] * 5 + [_vp] * 11 + [_size_t, _vp]),
@@ -155,18 +158,10 @@ def tree_attention(q, k_cache, v_cache, prefix_len, k_tree, v_tree, mask, *, blo
     paged when block_table is given (k, v [blocks][Hkv][16][D]); uint8 caches hold
     fp8 E4M3 codes with per-tensor k_scale / v_scale; k_tree, v_tree [B][n][Hkv][D];
     mask from tree_build."""
-    B, n, Hq, D = q.shape
-    Hkv = k_tree.shape[2]
-    paged = block_table is not None
-    fp8 = dict(kv_dtype=TV_FP8_E4M3, k_scale=k_scale, v_scale=v_scale) if k_cache.dtype == torch.uint8 else {}
-    if paged:
-        desc = attn_desc(B, n, Hq, Hkv, D, _dtype_code(q), paged=True, max_blocks=block_table.shape[1],
-                         num_blocks=num_blocks or k_cache.shape[0], scale=scale, **fp8)
-    else:
-        desc = attn_desc(B, n, Hq, Hkv, D, _dtype_code(q), Lmax=k_cache.shape[2], scale=scale, **fp8)
+    desc = _desc_for(q, k_cache, k_tree, block_table, num_blocks, scale, k_scale, v_scale)
     out = torch.empty_like(q) if out is None else out
     if want_lse and lse is None:
-        lse = torch.empty((B, n, Hq), dtype=torch.float32, device=q.device)
+        lse = torch.empty((q.shape[0], q.shape[1], q.shape[2]), dtype=torch.float32, device=q.device)
     ws = checked_workspace_size(desc)
     if workspace is None and ws > 0:
         workspace = torch.empty(ws, dtype=torch.uint8, device=q.device)
@@ -175,6 +170,33 @@ def tree_attention(q, k_cache, v_cache, prefix_len, k_tree, v_tree, mask, *, blo
                                _ptr(prefix_len), _ptr(k_tree), _ptr(v_tree), _ptr(mask), _ptr(out), _ptr(lse),
                                _ptr(status), _ptr(workspace), wbytes, _stream(stream))
     _check(rc, "tree_attention")
+    return (out, lse) if want_lse else out
+
+
+def _desc_for(q, k_cache, k_tree, block_table, num_blocks, scale, k_scale, v_scale) -> AttnDesc:
+    B, n, Hq, D = q.shape
+    Hkv = k_tree.shape[2]
+    fp8 = dict(kv_dtype=TV_FP8_E4M3, k_scale=k_scale, v_scale=v_scale) if k_cache.dtype == torch.uint8 else {}
+    if block_table is not None:
+        return attn_desc(B, n, Hq, Hkv, D, _dtype_code(q), paged=True, max_blocks=block_table.shape[1],
+                         num_blocks=num_blocks or k_cache.shape[0], scale=scale, **fp8)
+    return attn_desc(B, n, Hq, Hkv, D, _dtype_code(q), Lmax=k_cache.shape[2], scale=scale, **fp8)
+
+
+def tree_attention_noalloc(q, k_cache, v_cache, prefix_len, k_tree, v_tree, mask, *, block_table=None,
+                           num_blocks=0, scale=0.0, out=None, lse=None, status=None, want_lse=False,
+                           k_scale=0.0, v_scale=0.0, stream=None):
+    """tree_attention without a workspace: the library's fixed per-GPU scratch array
+    (TV_NOALLOC_SCRATCH_BYTES) holds the partial results.  Pass `out` (and `lse`) to
+    keep the call itself free of allocations; calls that overlap on one GPU race."""
+    desc = _desc_for(q, k_cache, k_tree, block_table, num_blocks, scale, k_scale, v_scale)
+    out = torch.empty_like(q) if out is None else out
+    if want_lse and lse is None:
+        lse = torch.empty((q.shape[0], q.shape[1], q.shape[2]), dtype=torch.float32, device=q.device)
+    rc = load().tree_attention_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                       _ptr(block_table), _ptr(prefix_len), _ptr(k_tree), _ptr(v_tree), _ptr(mask),
+                                       _ptr(out), _ptr(lse), _ptr(status), _stream(stream))
+    _check(rc, "tree_attention_noalloc")
     return (out, lse) if want_lse else out
 
 

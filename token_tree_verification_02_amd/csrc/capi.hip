@@ -11,9 +11,10 @@
 #include "tv_internal.h"
 
 namespace {
-
 thread_local std::string g_err;
+}  // namespace
 
+namespace tv {
 int fail(int code, const char* fmt, ...) {
   char buf[512];
   va_list ap;
@@ -23,6 +24,10 @@ int fail(int code, const char* fmt, ...) {
   g_err = buf;
   return code;
 }
+}  // namespace tv
+
+namespace {
+using tv::fail;
 
 int hip_fail(hipError_t e, const char* what) {
   return fail(TV_EHIP, "%s: %s", what, hipGetErrorString(e));
@@ -132,6 +137,15 @@ int plan_attention(const tv_attn_desc* d, AttnPlan* p, int cus) {
   return TV_OK;
 }
 
+int attention_workspace_bytes(const tv_attn_desc* d, size_t* bytes) {
+  const int rc = check_desc(d);
+  if (rc != TV_OK) return rc;
+  AttnPlan p;
+  plan_attention(d, &p, num_cus());
+  *bytes = p.ws_bytes;
+  return TV_OK;
+}
+
 }  // namespace tv
 
 extern "C" {
@@ -180,10 +194,8 @@ int tree_build(int B, int n, const int32_t* parent, const int32_t* depth, const 
 }
 
 size_t tree_attention_workspace_size(const tv_attn_desc* desc) {
-  if (check_desc(desc) != TV_OK) return (size_t)-1;
-  tv::AttnPlan p;
-  tv::plan_attention(desc, &p, num_cus());
-  return p.ws_bytes;
+  size_t b = 0;
+  return tv::attention_workspace_bytes(desc, &b) == TV_OK ? b : (size_t)-1;
 }
 
 int tree_attention(const tv_attn_desc* desc, const void* q, const void* k_cache, const void* v_cache,

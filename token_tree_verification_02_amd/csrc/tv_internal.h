@@ -39,6 +39,11 @@ struct AttnPlan {
 };
 
 int plan_attention(const tv_attn_desc* d, AttnPlan* p, int num_cus);
+// Validates the descriptor and gives the workspace tree_attention needs for it
+// (TV_OK, or the status with the message set as for a failed call).
+int attention_workspace_bytes(const tv_attn_desc* d, size_t* bytes);
+// Sets the calling thread's last-error message; returns `code`.
+int fail(int code, const char* fmt, ...);
 
 struct AttnArgs {
   const void* q;
