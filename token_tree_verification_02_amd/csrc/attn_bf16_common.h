@@ -102,6 +102,23 @@ __device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, uint32_
       : "v"(voff), "s"(ub), "s"(__builtin_amdgcn_readfirstlane(lds_line)));
 }
 
+// The same for the streaming prefix tiles: `nt` marks the lines non-temporal (each
+// is read once), so they displace less of what the caches hold.
+__device__ __forceinline__ void dma16s_nt(const void* sbase, uint32_t voff, uint32_t lds_line) {
+  const uint64_t b = (uint64_t)sbase;
+  const uint64_t ub = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2 nt\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(ub), "s"(__builtin_amdgcn_readfirstlane(lds_line)));
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt");

@@ -44,6 +44,7 @@ namespace {
 using namespace attn;
 
 constexpr int kTK = 64;  // keys per tile
+constexpr float kSumCap = 256.f;  // 2^kTau: a lane's block sum above this triggers a rescale
 constexpr int kSkQB = 1;  // 32-row query blocks per wave (256 rows per workgroup)
 
 __device__ __attribute__((aligned(4096))) uint4 sk_zero_page[256];
@@ -289,6 +290,27 @@ __device__ __forceinline__ void sk_tile(const char AS3* Kr, const char AS3* Vr,
   f32x16 Sa[2][1];
   sk_qk<E, D, 1>(Kr, 0, qop, kofs, Sa[0]);
   sk_qk<E, D, 1>(Kr, 1, qop, kofs, Sa[1]);
+  if constexpr (!MASKED) {
+    // Full prefix tile with the reference max already set (the first tile of a
+    // segment takes the masked path): the probabilities are taken against the
+    // reference directly, and the block's maximum is only computed, with a
+    // rescale, when a lane's sum of 16 probabilities exceeds 2^kTau, i.e.
+    // whenever some probability might (the same bound the masked path keeps).
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      typename E::V8 P[1][2];
+      float lb = 0.f;
+      sk_probs<E>(Sa[kb][0], P[0], lb, slt, m_run[0]);
+      if (__builtin_expect(__any(lb > kSumCap), 0)) {
+        sk_rescale<D>(O[0], m_run[0], lsum[0], sk_colmax(Sa[kb][0]) * slt);
+        lb = 0.f;
+        sk_probs<E>(Sa[kb][0], P[0], lb, slt, m_run[0]);
+      }
+      lsum[0] += lb;
+      sk_pv<E, D, 1>(Vr, kb, P, O, vofs);
+    }
+    return;
+  }
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
     if constexpr (MASKED) sk_mask(Sa[kb][0], kb, lim, tree, bits[0], hh);
@@ -315,7 +337,8 @@ __global__ __launch_bounds__(64 * RB) void attn_sk_kernel(AttnArgs a, SkArgs k) 
   constexpr int GPR = D / 8;                // 16-byte granules per row
   constexpr int SD = D / 16, DB = D / 32;
   constexpr int WAITN = (S - 2) * LPW;      // loads a wave may leave in flight
-  static_assert(HL % RB == 0 && LPW * (S - 2) < 64, "pipeline shape");
+  constexpr int NID = LPW / 2;              // paged: distinct blocks among a wave's K (= V) lines
+  static_assert(HL % RB == 0 && LPW * (S - 2) < 64 && LPW % 2 == 0, "pipeline shape");
   __shared__ __attribute__((aligned(1024))) char smem[S * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -368,10 +391,29 @@ __global__ __launch_bounds__(64 * RB) void attn_sk_kernel(AttnArgs a, SkArgs k) 
     const int key = q * RB >= HL ? lrow : perm_row(lrow);
     voff[q] = (uint32_t)(((a.paged ? (key & 15) : key) * D + gran_of(lane, q) * 8) * 2);
   }
+  // Paged cache: the wave's K lines t < NID and V lines NID + t cover the same
+  // token rows, so a tile needs NID block ids per wave: block kq[t] of the tile's
+  // four.  They are loaded one tile ahead of their DMA (load_ids), so the
+  // scalar-load latency never sits between the barrier and the tile's compute.
+  int kq[NID];
+#pragma unroll
+  for (int t = 0; t < NID; ++t) kq[t] = ((t * RB + rb) * RPL) >> 4;
+  const int max_blocks = a.max_blocks, num_blocks = a.num_blocks;
+  auto load_ids = [&](const Cursor& c, int (&ids)[NID]) {
+#pragma unroll
+    for (int t = 0; t < NID; ++t) ids[t] = -1;
+    if (!a.paged || c.b >= B || c.off >= c.tpre) return;
+    const AS4 int32_t* row = btc + (size_t)c.b * max_blocks;
+#pragma unroll
+    for (int t = 0; t < NID; ++t) {
+      const int bi = c.off * (kTK / TV_PAGE) + kq[t];
+      ids[t] = bi < max_blocks ? row[bi] : -1;
+    }
+  };
 
   // DMA of this wave's lines of the bf16 tile at cursor c to LDS address gbase
-  // (!live: zeros)
-  auto issue = [=](const Cursor& c, bool live, uint32_t gbase) {
+  // (!live: zeros); ids: the tile's block ids from load_ids (paged prefix tiles)
+  auto issue = [=](const Cursor& c, bool live, uint32_t gbase, const int (&ids)[NID]) {
     // an opaque copy of the lane id keeps the compiler from hoisting the
     // per-line geometry of the rare paths out of the loop (it would hold dozens
     // of registers for them)
@@ -397,22 +439,19 @@ __global__ __launch_bounds__(64 * RB) void attn_sk_kernel(AttnArgs a, SkArgs k) 
     const int tstart = c.off * kTK;
     const bool full = tstart + kTK <= c.L;
     if (a.paged) {
-      const int b0 = tstart >> 4;
-      const AS4 int32_t* row = btc + (size_t)b * a.max_blocks;
-      const int id0 = b0 < a.max_blocks ? row[b0] : -1;
-      const int id1 = b0 + 1 < a.max_blocks ? row[b0 + 1] : -1;
-      const int id2 = b0 + 2 < a.max_blocks ? row[b0 + 2] : -1;
-      const int id3 = b0 + 3 < a.max_blocks ? row[b0 + 3] : -1;
+      size_t boff[NID];  // byte offset of (block, KV head) in either cache; ~0 for a bad id
+#pragma unroll
+      for (int t = 0; t < NID; ++t)
+        boff[t] = (ids[t] >= 0 && ids[t] < num_blocks) ? ((size_t)ids[t] * Hkv + g) * (TV_PAGE * D * 2) : ~(size_t)0;
 #pragma unroll
       for (int q = 0; q < LPW; ++q) {
-        const bool isv = q * RB >= HL;
+        const bool isv = q >= NID;
         const int line = q * RB + rb;
-        const int kq = ((isv ? line - HL : line) * RPL) >> 4;  // 16-token block of the line
-        const int blk = kq == 0 ? id0 : (kq == 1 ? id1 : (kq == 2 ? id2 : id3));
-        const bool bok = blk >= 0 && blk < a.num_blocks;
-        const char* lbase = (isv ? vc : kc) + ((size_t)blk * Hkv + g) * TV_PAGE * D * 2;
+        const size_t bo = boff[q % NID];
+        const bool bok = bo != ~(size_t)0;
+        const char* lbase = (isv ? vc : kc) + bo;
         if (full) {
-          dma16s(bok ? lbase : zero, voff[q], gbase + line * 1024);
+          dma16s_nt(bok ? lbase : zero, voff[q], gbase + line * 1024);
         } else {
           const int j = tstart + (isv ? lrow_of(ln, q) : perm_row(lrow_of(ln, q)));
           dma16(bok && j < c.L ? lbase + voff[q] : zsrc, gbase + line * 1024);
@@ -427,7 +466,7 @@ __global__ __launch_bounds__(64 * RB) void attn_sk_kernel(AttnArgs a, SkArgs k) 
         const bool isv = q * RB >= HL;
         const int line = q * RB + rb;
         if (full) {
-          dma16s(isv ? vb : kb, voff[q], gbase + line * 1024);
+          dma16s_nt(isv ? vb : kb, voff[q], gbase + line * 1024);
         } else {
           const int j = tstart + (isv ? lrow_of(ln, q) : perm_row(lrow_of(ln, q)));
           dma16(j < c.L ? (isv ? vb : kb) + voff[q] : zsrc, gbase + line * 1024);
@@ -453,13 +492,16 @@ __global__ __launch_bounds__(64 * RB) void attn_sk_kernel(AttnArgs a, SkArgs k) 
   const int rowbase = rs * RW + 32 * QB * rb;  // first query row of this wave within an item
   const float sl2 = a.scale_log2;
 
-  // prologue: S-1 tiles in flight
+  // prologue: S-1 tiles in flight, then the block ids of the next tile
+  int ids[NID];
 #pragma unroll
   for (int i = 0; i < S - 1; ++i) {
     const bool live = i < ntiles;
-    issue(ic, live, ring + i * STAGE);
+    load_ids(ic, ids);
+    issue(ic, live, ring + i * STAGE, ids);
     if (live) cursor_next(ic, plen, B, Hkv, k.cap, ttree);
   }
+  load_ids(ic, ids);
 
   // Segments: the part of one item inside this range.  Queries, masks and
   // accumulators are set up before a segment's tile loop and written out after
@@ -513,8 +555,11 @@ __global__ __launch_bounds__(64 * RB) void attn_sk_kernel(AttnArgs a, SkArgs k) 
       lds_barrier();        // ... everyone's, and everyone left tile it-1
       {
         const bool live = it + S - 1 < ntiles;
-        issue(ic, live, ring + ((it + S - 1) % S) * STAGE);
-        if (live) cursor_next(ic, plen, B, Hkv, k.cap, ttree);
+        issue(ic, live, ring + ((it + S - 1) % S) * STAGE, ids);
+        if (live) {
+          cursor_next(ic, plen, B, Hkv, k.cap, ttree);
+          load_ids(ic, ids);  // consumed by the next tile's issue
+        }
       }
       const int off = cc.off + j;
       const int st = it % S;
@@ -536,9 +581,12 @@ __global__ __launch_bounds__(64 * RB) void attn_sk_kernel(AttnArgs a, SkArgs k) 
       sk_tile<E, D, QB, MASKED>(Kr, Vr, qop, O, m_run, lsum, kofs, vofs, sl2, lim, tree, bits, hh);
       ++it;
     };
-    const int nfull = max(0, min(seg_len, cc.L / kTK - cc.off));  // full prefix tiles come first
-    for (int j = 0; j < nfull; ++j) step(std::integral_constant<bool, false>(), j);
-    for (int j = nfull; j < seg_len; ++j) step(std::integral_constant<bool, true>(), j);
+    // full prefix tiles come first; the segment's first tile always takes the
+    // masked path, which sets the reference max the full-tile path builds on
+    const int nfull = max(0, min(seg_len, cc.L / kTK - cc.off));
+    step(std::integral_constant<bool, true>(), 0);
+    for (int j = 1; j < nfull; ++j) step(std::integral_constant<bool, false>(), j);
+    for (int j = max(nfull, 1); j < seg_len; ++j) step(std::integral_constant<bool, true>(), j);
 
     // write the segment out: whole items directly, pieces into this range's slots
     const bool whole = seg_whole && item_end;
