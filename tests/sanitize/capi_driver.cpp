@@ -78,6 +78,8 @@ hipError_t launch_attn_bf16(const AttnArgs& a, const AttnPlan& p, hipStream_t) {
   CHECK(p.sk_nv == 0, "few-row plan with a tile schedule");
   CHECK(p.rsplit >= 1 && (long long)p.rsplit * 32 * p.rb >= p.rows, "rsplit %d does not cover %d rows", p.rsplit,
         p.rows);
+  // plans of at most 4 row waves stream their tiles non-temporal: one row slice, so one reader per tile
+  CHECK(p.rb > 4 || p.rsplit == 1, "rb %d with %d row slices", p.rb, p.rsplit);
   CHECK(p.tk == 32 || p.tk == 64, "tile keys %d", p.tk);
   CHECK(p.nchunks >= 1 && p.chunk_len >= p.tk && p.chunk_len % p.tk == 0, "chunks %d x %d", p.nchunks, p.chunk_len);
   CHECK((long long)p.nchunks * p.chunk_len >= p.cap, "chunks do not cover the capacity");

@@ -158,6 +158,15 @@ __global__ __launch_bounds__(64 * RB * KS) void attn_bf16_kernel(AttnArgs a, int
   const char* ktr = (const char*)a.kt;
   const char* vtr = (const char*)a.vt;
   const char* zero = (const char*)tv_zero_page;
+  // Full prefix tiles: with at most 4 row waves the plan has one row slice, so every
+  // tile is read by exactly one workgroup and streams non-temporal (each line is read
+  // once); the 8-row-wave plan may split rows over workgroups that share the tiles.
+  auto dma_full = [](const void* sbase, uint32_t voff, uint32_t lds_line) {
+    if constexpr (RB <= 4)
+      dma16s_nt(sbase, voff, lds_line);
+    else
+      dma16s(sbase, voff, lds_line);
+  };
   const uint32_t ring = (uint32_t)(uintptr_t)(AS3 void*)smem;
   const size_t rowbase = ((size_t)b * Hkv + g) * a.Lmax;  // contiguous cache row of token 0
 
@@ -219,7 +228,7 @@ __global__ __launch_bounds__(64 * RB * KS) void attn_bf16_kernel(AttnArgs a, int
         const bool bok = blk >= 0 && blk < a.num_blocks;
         const char* lbase = (isv ? vc : kc) + ((size_t)blk * Hkv + g) * TV_PAGE * D * 2;
         if (full) {
-          dma16s(bok ? lbase : zero, voff[q], gbase + line * 1024);
+          dma_full(bok ? lbase : zero, voff[q], gbase + line * 1024);
         } else {
           const int j = tstart + (isv ? lrow_[q] : perm_row(lrow_[q]));
           dma16(bok && j < k1 ? lbase + voff[q] : zsrc, gbase + line * 1024);
@@ -233,7 +242,7 @@ __global__ __launch_bounds__(64 * RB * KS) void attn_bf16_kernel(AttnArgs a, int
         const bool isv = q * RB >= C::HL;
         const int line = q * RB + rb;
         if (full) {
-          dma16s(isv ? vb : kb, voff[q], gbase + line * 1024);
+          dma_full(isv ? vb : kb, voff[q], gbase + line * 1024);
         } else {
           const int j = tstart + (isv ? lrow_[q] : perm_row(lrow_[q]));
           dma16(j < k1 ? (isv ? vb : kb) + voff[q] : zsrc, gbase + line * 1024);

@@ -323,7 +323,10 @@ __device__ __forceinline__ void sk_tile(const char AS3* Kr, const char AS3* Vr,
   }
 }
 
-template <bool F16, int D, int QB, int RB, int S>
+// NT: every tile is read by exactly one workgroup (one row slice per item), so the
+// full prefix tiles stream non-temporal; with several row slices the later ones
+// find the tiles in cache, so they are read normally.
+template <bool F16, bool NT, int D, int QB, int RB, int S>
 __global__ __launch_bounds__(64 * RB) void attn_sk_kernel(AttnArgs a, SkArgs k) {
   using E = Elt<F16>;
   constexpr int RW = 32 * QB * RB;          // query rows per workgroup
@@ -372,6 +375,12 @@ __global__ __launch_bounds__(64 * RB) void attn_sk_kernel(AttnArgs a, SkArgs k) 
   const char* zsrc = zero + lane * 16;
   const uint32_t ring = (uint32_t)(uintptr_t)(AS3 void*)smem;
   const AS4 int32_t* btc = (const AS4 int32_t*)a.bt;
+  auto dma_full = [](const void* sbase, uint32_t voff, uint32_t lds_line) {
+    if constexpr (NT)
+      dma16s_nt(sbase, voff, lds_line);
+    else
+      dma16s(sbase, voff, lds_line);
+  };
 
   // per-lane DMA geometry: line q*RB + rb of the tile belongs to this wave; the
   // lane's token row within the tile and its source granule (swizzled) follow
@@ -451,7 +460,7 @@ __global__ __launch_bounds__(64 * RB) void attn_sk_kernel(AttnArgs a, SkArgs k) 
         const bool bok = bo != ~(size_t)0;
         const char* lbase = (isv ? vc : kc) + bo;
         if (full) {
-          dma16s_nt(bok ? lbase : zero, voff[q], gbase + line * 1024);
+          dma_full(bok ? lbase : zero, voff[q], gbase + line * 1024);
         } else {
           const int j = tstart + (isv ? lrow_of(ln, q) : perm_row(lrow_of(ln, q)));
           dma16(bok && j < c.L ? lbase + voff[q] : zsrc, gbase + line * 1024);
@@ -466,7 +475,7 @@ __global__ __launch_bounds__(64 * RB) void attn_sk_kernel(AttnArgs a, SkArgs k) 
         const bool isv = q * RB >= HL;
         const int line = q * RB + rb;
         if (full) {
-          dma16s_nt(isv ? vb : kb, voff[q], gbase + line * 1024);
+          dma_full(isv ? vb : kb, voff[q], gbase + line * 1024);
         } else {
           const int j = tstart + (isv ? lrow_of(ln, q) : perm_row(lrow_of(ln, q)));
           dma16(j < c.L ? (isv ? vb : kb) + voff[q] : zsrc, gbase + line * 1024);
@@ -738,14 +747,23 @@ hipError_t launch_attn_sk(const AttnArgs& a, const AttnPlan& p, void* ws, hipStr
   // an fp8 cache has no many-row plan: the host refuses it for more than 128 query rows
   // per KV head, so it cannot reach this launcher
   if (a.kv_fp8) return hipErrorInvalidConfiguration;
+  const bool nt = rsplit == 1;
+#define TV_SK_LAUNCH(F16, D)                                                                        \
+  do {                                                                                              \
+    if (nt)                                                                                         \
+      hipLaunchKernelGGL((attn_sk_kernel<F16, true, D, kSkQB, RB, 4>), grid, block, 0, s, a, k);  \
+    else                                                                                            \
+      hipLaunchKernelGGL((attn_sk_kernel<F16, false, D, kSkQB, RB, 4>), grid, block, 0, s, a, k); \
+  } while (0)
   if (a.D == 64 && a.f16)
-    hipLaunchKernelGGL((attn_sk_kernel<true, 64, kSkQB, RB, 4>), grid, block, 0, s, a, k);
+    TV_SK_LAUNCH(true, 64);
   else if (a.D == 64)
-    hipLaunchKernelGGL((attn_sk_kernel<false, 64, kSkQB, RB, 4>), grid, block, 0, s, a, k);
+    TV_SK_LAUNCH(false, 64);
   else if (a.f16)
-    hipLaunchKernelGGL((attn_sk_kernel<true, 128, kSkQB, RB, 4>), grid, block, 0, s, a, k);
+    TV_SK_LAUNCH(true, 128);
   else
-    hipLaunchKernelGGL((attn_sk_kernel<false, 128, kSkQB, RB, 4>), grid, block, 0, s, a, k);
+    TV_SK_LAUNCH(false, 128);
+#undef TV_SK_LAUNCH
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int chunks = RW / 64;
