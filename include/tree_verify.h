@@ -195,7 +195,7 @@ int tree_attention(const tv_attn_desc* desc, const void* q,
  * may return wrong results.  Calls in one stream are ordered and safe.
  * Nothing in the array needs to start at zero.
  * ------------------------------------------------------------------------- */
-#define TV_NOALLOC_SCRATCH_BYTES ((size_t)72 << 20)
+#define TV_NOALLOC_SCRATCH_BYTES ((size_t)40 << 20)
 
 int tree_attention_noalloc(const tv_attn_desc* desc, const void* q,
                            const void* k_cache, const void* v_cache,

@@ -106,7 +106,8 @@ hipError_t launch_attn_sk(const AttnArgs& a, const AttnPlan& p, void* ws, hipStr
         p.sk_nv, p.rsplit, p.rows);
   CHECK((uintptr_t)ws == g_ws && p.ws_bytes > 0, "schedule workspace");
   const size_t slots = (size_t)2 * p.sk_nv * p.rsplit * 256;
-  CHECK(p.ws_bytes >= sk_sched_bytes(a.B) + slots * (a.D + 2) * sizeof(float), "schedule workspace too small");
+  CHECK(p.ws_bytes >= sk_sched_bytes(a.B) + slots * (a.D * sizeof(uint16_t) + 4 * sizeof(float)),
+        "schedule workspace too small");
   return stub();
 }
 

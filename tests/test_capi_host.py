@@ -234,3 +234,10 @@ def test_noalloc_host_checks(lib):
               desc(B=8, n=21, Hq=32, Hkv=32, Lmax=1024)):
         assert tv.workspace_size(d) <= tv.TV_NOALLOC_SCRATCH_BYTES
     assert lib.tree_attention_noalloc(ctypes.byref(desc(B=0)), *([None] * 11), None) == tv.TV_OK
+
+
+def test_noalloc_limit_matches_header():
+    src = open(os.path.join(ROOT, "include", "tree_verify.h")).read()
+    m = re.search(r"#define TV_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", src)
+    assert m, "TV_NOALLOC_SCRATCH_BYTES not found"
+    assert int(m.group(1)) << int(m.group(2)) == tv.TV_NOALLOC_SCRATCH_BYTES

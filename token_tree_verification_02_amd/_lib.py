@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_PKG, "libtreeverify.so")
 TV_OK, TV_EINVAL, TV_ETOPOLOGY, TV_EUNSUPPORTED, TV_EWORKSPACE, TV_EHIP = range(6)
 TV_F32, TV_BF16, TV_F16, TV_FP8_E4M3 = 0, 1, 2, 3
 TV_NMAX, TV_PAGE, TV_MSS_VMAX, TV_TOPK_MAX, TV_MERGE_MMAX = 256, 16, 1 << 20, 16, 64
-TV_NOALLOC_SCRATCH_BYTES = 72 << 20
+TV_NOALLOC_SCRATCH_BYTES = 40 << 20
 
 _c_int, _c_float, _vp, _size_t = ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
 

@@ -58,8 +58,8 @@ __device__ __forceinline__ int clamp_len(int L, int cap) { return L < 0 ? 0 : (L
 
 struct SkArgs {
   int32_t* sched;
-  float* po;   // [2*NV][rsplit][RW][D] partial O (unnormalised)
-  float* pml;  // [2*NV][rsplit][RW][2]  (max in the log2 domain, sum)
+  uint16_t* po;  // [2*NV][rsplit][RW][D] a piece's O / (sum * scale), fp16
+  float* pml;    // [2*NV][rsplit][RW][4]  (max in the log2 domain, sum, scale, unused)
   int rsplit, NV, cap;
 };
 
@@ -624,20 +624,38 @@ __global__ __launch_bounds__(64 * RB) void attn_sk_kernel(AttnArgs a, SkArgs k) 
         if (a.lse != nullptr && hh == 0)
           a.lse[(size_t)(cc.b * n + u) * a.Hq + h] = (m_run[qb] + __log2f(ltot)) * kLn2;
       } else {
+        // a piece: O over its own sum is a weighted mean of value entries; it is
+        // stored in fp16 times a power of two that puts the row's largest entry in
+        // [2^14, 2^15), so every entry keeps fp16's relative precision (2^-12)
+        // whatever the values' range, in half the bytes of fp32.  The merge
+        // weights the piece by its sum and undoes the scale; a row with no key in
+        // the piece has sum 0 and weight 0.
         const size_t pidx = ((size_t)slot * k.rsplit + rs) * RW + (row - rs * RW);
-        float* wo = k.po + pidx * D;
+        const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+        float amax = 0.f;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) amax = fmaxf(amax, fabsf(O[qb][db][r]));
+        {
+          const auto ms = __builtin_amdgcn_permlane32_swap(__float_as_uint(amax), __float_as_uint(amax), false, false);
+          amax = fmaxf(__uint_as_float(ms[0]), __uint_as_float(ms[1])) * inv;
+        }
+        // amax < 2^(ex + 15); the floor keeps 2^-ex finite for rows of near-zero values
+        const int ex = amax > 0.f ? max(__builtin_amdgcn_frexp_expf(amax) - 15, -96) : 0;
+        const float sc = __builtin_amdgcn_ldexpf(inv, -ex);
+        uint16_t* wo = k.po + pidx * D;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
           for (int rq = 0; rq < 4; ++rq) {
             const int d0 = 32 * db + 8 * rq + 4 * hh;
-            *(float4*)(wo + d0) = make_float4(O[qb][db][4 * rq], O[qb][db][4 * rq + 1], O[qb][db][4 * rq + 2],
-                                              O[qb][db][4 * rq + 3]);
+            uint2 w;
+            w.x = Elt<true>::bits(O[qb][db][4 * rq] * sc) | (Elt<true>::bits(O[qb][db][4 * rq + 1] * sc) << 16);
+            w.y = Elt<true>::bits(O[qb][db][4 * rq + 2] * sc) | (Elt<true>::bits(O[qb][db][4 * rq + 3] * sc) << 16);
+            *(uint2*)(wo + d0) = w;
           }
-        if (hh == 0) {
-          k.pml[2 * pidx] = m_run[qb];
-          k.pml[2 * pidx + 1] = ltot;
-        }
+        if (hh == 0) *(float4*)(k.pml + 4 * pidx) = make_float4(m_run[qb], ltot, __builtin_amdgcn_ldexpf(1.f, ex), 0.f);
       }
     }
     // on to the next item
@@ -696,21 +714,23 @@ __global__ __launch_bounds__(256) void sk_merge_kernel(AttnArgs a, SkArgs k, int
     for (int w = ws; w <= we; ++w) {
       const int slot = (s0 <= (long long)w * per) ? 2 * w : 2 * w + 1;
       const size_t pi = ((size_t)slot * k.rsplit + rs) * RW + rloc;
-      M = fmaxf(M, k.pml[2 * pi]);
+      M = fmaxf(M, k.pml[4 * pi]);
     }
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     float lt = 0.f;
     for (int w = ws; w <= we; ++w) {
       const int slot = (s0 <= (long long)w * per) ? 2 * w : 2 * w + 1;
       const size_t pi = ((size_t)slot * k.rsplit + rs) * RW + rloc;
-      const float mc = k.pml[2 * pi], lc = k.pml[2 * pi + 1];
-      const float wgt = (mc == -INFINITY) ? 0.f : exp2f(mc - M);
-      const float4 oc = *(const float4*)(k.po + pi * D + d0);
-      acc.x += wgt * oc.x;
-      acc.y += wgt * oc.y;
-      acc.z += wgt * oc.z;
-      acc.w += wgt * oc.w;
-      lt += wgt * lc;
+      const float4 mls = *(const float4*)(k.pml + 4 * pi);  // max, sum, scale
+      if (mls.x == -INFINITY) continue;  // no attended key in this piece
+      const float wl = exp2f(mls.x - M) * mls.y;
+      const float wo = wl * mls.z;
+      const uint2 oc = *(const uint2*)(k.po + pi * D + d0);
+      acc.x += wo * f16_to_f32((uint16_t)oc.x);
+      acc.y += wo * f16_to_f32((uint16_t)(oc.x >> 16));
+      acc.z += wo * f16_to_f32((uint16_t)oc.y);
+      acc.w += wo * f16_to_f32((uint16_t)(oc.y >> 16));
+      lt += wl;
     }
     const float inv = 1.f / lt;
     const int u = row / a.G, gi = row % a.G, h = g * a.G + gi;
@@ -737,8 +757,8 @@ hipError_t launch_attn_sk(const AttnArgs& a, const AttnPlan& p, void* ws, hipStr
   k.sched = (int32_t*)ws;
   const size_t sb = sk_sched_bytes(a.B);
   const size_t slots = (size_t)2 * NV * rsplit * RW;
-  k.po = (float*)((char*)ws + sb);
-  k.pml = (float*)((char*)ws + sb + ((slots * a.D * sizeof(float) + 255) & ~(size_t)255));
+  k.po = (uint16_t*)((char*)ws + sb);
+  k.pml = (float*)((char*)ws + sb + ((slots * a.D * sizeof(uint16_t) + 255) & ~(size_t)255));
   k.rsplit = rsplit;
   k.NV = NV;
   k.cap = p.cap;

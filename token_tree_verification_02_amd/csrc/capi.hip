@@ -107,8 +107,9 @@ int plan_attention(const tv_attn_desc* d, AttnPlan* p, int cus) {
       p->rsplit = (int)rs;
       p->sk_nv = (int)(rs >= cus ? 1 : cus / rs);
       const size_t slots = (size_t)2 * p->sk_nv * p->rsplit * 256;
-      p->ws_bytes = tv::sk_sched_bytes(d->B) + ((slots * d->D * sizeof(float) + 255) & ~(size_t)255) +
-                    ((slots * 2 * sizeof(float) + 255) & ~(size_t)255);
+      // per slot: a piece's scaled, normalised O in fp16, then (max, sum, scale, -) in fp32
+      p->ws_bytes = tv::sk_sched_bytes(d->B) + ((slots * d->D * sizeof(uint16_t) + 255) & ~(size_t)255) +
+                    ((slots * 4 * sizeof(float) + 255) & ~(size_t)255);
       return TV_OK;
     }
     p->rb = 8, p->ks = 1, p->tk = 64;
