@@ -257,8 +257,16 @@ int tree_verify_greedy(int B, int n, int V, int logits_dtype, const void* logits
  *     rows it visits (the statistics of a visited node's rows are gathered
  *     by the walk); 2 = a parallel pass first gathers the statistics of every
  *     LLM and SSM row (reads all of them once), and the walk then reads rows
- *     only for residuals and the final draw.  0 takes 2 while all rows
- *     together are at most 1 GiB.  The results are the same in every mode.
+ *     only for residuals and the final draw; 3 = mode 1 with each sequence's
+ *     walk spread over up to 16 workgroups, each owning a slice of the
+ *     vocabulary, which exchange row statistics through the workspace at each
+ *     step (B * slices <= 512, so the grid is resident at once; it needs
+ *     `status`, else mode 1 runs).  0 takes 2 while all rows together are at
+ *     most 1 GiB, else 3.  The results are the same in every mode.  In mode 3
+ *     the exchange waits are bounded: if the slices of a sequence cannot all
+ *     run at once (another process holding the GPU's compute units), a slice
+ *     gives up, the sequence's status is TV_EHIP and its outputs are
+ *     unspecified; every workgroup still exits.
  *   workspace: tree_verify_stochastic_workspace_size(B, n, V) bytes (fp32
  *     residual rows and row statistics), 16-byte aligned; contents on entry
  *     do not matter.

@@ -156,7 +156,9 @@ def test_commit_argument_errors(lib):
 
 def test_stochastic_argument_errors(lib):
     ws = lib.tree_verify_stochastic_workspace_size
-    assert ws(8, 21, 32000) == 8 * 2 * 32768 * 4 + 8 * 21 * 2 * 16   # two fp32 rows per sequence + row statistics
+    # two fp32 rows per sequence, row statistics, then the sliced walk's two slots of 16
+    # exchange records (16 tagged 64-bit words) per sequence
+    assert ws(8, 21, 32000) == 8 * 2 * 32768 * 4 + 8 * 21 * 2 * 16 + 8 * 2 * 16 * 16 * 8
     assert ws(0, 5, 5) == 0
     assert ws(-1, 5, 5) == SIZE_MAX and ws(2, 5, 0) == SIZE_MAX and ws(2, 5, tv.TV_MSS_VMAX + 1) == SIZE_MAX
     assert ws(2, 0, 5) == SIZE_MAX and ws(2, 257, 5) == SIZE_MAX
@@ -171,7 +173,8 @@ def test_stochastic_argument_errors(lib):
     assert call(2, 7, 10, tv.TV_F32, ptrs=[None] * 10) == tv.TV_EINVAL
     assert call(2, 7, 10, tv.TV_F32, w=None) == tv.TV_EWORKSPACE
     assert call(2, 7, 10, tv.TV_F32, wb=ws(2, 7, 10) - 1) == tv.TV_EWORKSPACE
-    assert call(2, 7, 10, tv.TV_F32, mode=3) == tv.TV_EINVAL
+    assert call(2, 7, 10, tv.TV_F32, mode=4) == tv.TV_EINVAL
+    assert call(2, 7, 10, tv.TV_F32, mode=-1) == tv.TV_EINVAL
     assert call(2, 7, 10, tv.TV_F32, ptrs=[0x100004] + [0x100000] * 9) == tv.TV_EINVAL   # misaligned logits
     assert call(0, 7, 10, tv.TV_F32, ptrs=[None] * 10, w=None, wb=0) == tv.TV_OK
 

@@ -110,18 +110,19 @@ CASES = {
 }
 
 
-@pytest.mark.parametrize("mode", [1, 2])
+@pytest.mark.parametrize("mode", [1, 2, 3])
 @pytest.mark.parametrize("name", list(CASES))
 def test_stochastic_parity(name, mode):
     """mode 1: the walk gathers the statistics of the rows it visits; mode 2: all
-    row statistics first, in parallel."""
+    row statistics first, in parallel; mode 3: mode 1 with each sequence's walk
+    spread over several workgroups, each owning a slice of the vocabulary."""
     cfg, noise = CASES[name]
     log(f"case stochastic {name} mode {mode}")
     w = W.make_stochastic(cfg, seed=17, ssm_noise=noise)
     check(w, mode=mode)
 
 
-@pytest.mark.parametrize("mode", [1, 2])
+@pytest.mark.parametrize("mode", [1, 2, 3])
 def test_stochastic_invalid_sequences_reported(mode):
     log("case stochastic invalid")
     cfg = W.config(2, B=4, L_lo=16, L_hi=16, vocab=500)
@@ -132,6 +133,21 @@ def test_stochastic_invalid_sequences_reported(mode):
     w["tokens"][2, 3] = -2
     w["parent"][3, 4] = 9                                 # a parent after its child
     check(w, mode=mode)
+
+
+@pytest.mark.parametrize("name", ["llama_v32000", "v200k_chain", "star_low_accept", "odd_v1001_f32"])
+def test_stochastic_modes_agree(name):
+    """Every mode takes the same decisions on the same inputs: paths, lengths, bonus
+    tokens and statuses are identical (the modes sum the same fp32 terms in fp64,
+    in different groupings)."""
+    cfg, noise = CASES[name]
+    log(f"case stochastic modes agree {name}")
+    w = W.make_stochastic(cfg, seed=23, ssm_noise=noise)
+    ref = run_gpu(w, 1)
+    for mode in (2, 3, 0):
+        got = run_gpu(w, mode)
+        for a, b_, what in zip(ref, got, ("path", "path_len", "bonus", "status")):
+            np.testing.assert_array_equal(a, b_, err_msg=f"mode {mode} {what}")
 
 
 def test_gpu_emits_the_llm_distribution():

@@ -301,7 +301,7 @@ int tree_verify_stochastic(int B, int n, int V, int logits_dtype, int mode, cons
   if (V < 1 || V > TV_MSS_VMAX) return fail(TV_EINVAL, "V=%d outside [1, %d]", V, TV_MSS_VMAX);
   if (logits_dtype != TV_F32 && logits_dtype != TV_BF16)
     return fail(TV_EUNSUPPORTED, "logits dtype %d", logits_dtype);
-  if (mode < 0 || mode > 2) return fail(TV_EINVAL, "mode=%d outside [0, 2]", mode);
+  if (mode < 0 || mode > 3) return fail(TV_EINVAL, "mode=%d outside [0, 3]", mode);
   if ((long long)B * n * 2 > 0x7fffffffLL) return fail(TV_EINVAL, "B*n too large");
   if (B == 0) return TV_OK;
   if (!logits || !ssm_logits || !tokens || !parent || !u_accept || !u_sample || !path_out || !path_len || !bonus)

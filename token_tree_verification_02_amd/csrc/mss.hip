@@ -10,8 +10,11 @@
 // from the current distribution by inverse CDF.  The uniforms are inputs.
 //
 // The walk is sequential per sequence and touches only the rows of the nodes it
-// visits, so it runs as one 512-thread workgroup per sequence that streams
-// just those vocab rows (the rows of a node already visited stay in L2/MALL):
+// visits.  It runs as one 512-thread workgroup per sequence that streams just
+// those vocab rows (the rows of a node already visited stay in L2/MALL), or,
+// sliced, as up to 16 workgroups of 256 threads per sequence, each streaming its
+// own range of chunks of those rows and exchanging per-slice statistics at each
+// step of the walk:
 //   node entry     one pass: online (max, sum) of the node's LLM logits and of
 //                  its first child's SSM logits
 //   child test     scalar loads of the two logits at the draft token
@@ -22,8 +25,9 @@
 //   final draw     one pass of per-segment sums (512 elements per segment),
 //                  a prefix over segments in fp64 by one wave, and a scan
 //                  inside the chosen segment
-// Element e of a row belongs to thread (e % 4096) / 8 in every pass, so a thread
-// only ever reads back residual values it wrote itself.
+// Element e of a row belongs to thread (e % chunk) / 8 of the workgroup owning
+// its chunk in every pass, so a thread only ever reads back residual values it
+// wrote itself.
 #include <limits.h>
 
 #include "tv_internal.h"
@@ -31,12 +35,15 @@
 namespace tv {
 namespace {
 
-constexpr int kThreads = 512;
-constexpr int kWaves = kThreads / 64;
+constexpr int kThreads = 512;             // one workgroup per sequence
+constexpr int kThreadsSliced = 256;        // several per sequence: two fit on a CU
 constexpr int kEPT = 8;                      // elements per thread per chunk
-constexpr int kChunk = kThreads * kEPT;      // 4096
+constexpr int kChunk = kThreads * kEPT;      // 4096 (the workspace's row padding)
 constexpr int kSeg = 64 * kEPT;              // 512 elements: one wave's share of a chunk
 constexpr int kMaxSeg = TV_MSS_VMAX / kSeg;  // 2048
+constexpr int kMaxNS = 16;                   // vocabulary slices per sequence (sliced walk)
+constexpr int kXRec = 8;                     // doubles per exchange record
+constexpr int kSpinMax = 1 << 18;            // polls before a slice gives up on its peers
 // A pass over a row visits chunks in groups of kU whose loads are all issued
 // before any of them is used, so a workgroup keeps kU * 8 KB of each
 // row in flight instead of waiting out one memory latency per chunk.
@@ -146,6 +153,7 @@ __device__ __forceinline__ void stat_merge(Stat& a, float R, double S) {
   a.R = M;
 }
 
+template <int NW>
 struct Shared {
   int par[TV_NMAX];
   int tok[TV_NMAX];
@@ -153,10 +161,13 @@ struct Shared {
   int child[TV_NMAX];
   int path[TV_NMAX];
   unsigned long long ball[4];
-  float rR[2][2][kWaves];
-  double rS[2][3][kWaves];
+  float rR[2][2][NW];
+  double rS[2][3][NW];
   float cap_prev[2], cap_r[2];  // by pass parity: a pass never overwrites what the last one caught
   double segd[kMaxSeg];
+  double xr[kMaxNS][kXRec];     // the slices' exchange records, in slice order
+  double xtot;
+  int xok;
   int result;
 };
 
@@ -182,7 +193,8 @@ __device__ __forceinline__ Stat wave_stat(Stat a) {
 // Every thread ends with the same values, merged in the same order from LDS.
 // One barrier; alternating LDS slots so back-to-back calls never overwrite
 // values another wave is still reading.
-__device__ __forceinline__ void block_reduce(Shared& S, int& slot, Stat& a, Stat& b, double& t) {
+template <int NW>
+__device__ __forceinline__ void block_reduce(Shared<NW>& S, int& slot, Stat& a, Stat& b, double& t) {
   const Stat wa = wave_stat(a), wb = wave_stat(b);
   const double wt = wave_sum(t);
   const int w = threadIdx.x >> 6;
@@ -193,12 +205,65 @@ __device__ __forceinline__ void block_reduce(Shared& S, int& slot, Stat& a, Stat
   }
   __syncthreads();
   a = Stat{}, b = Stat{}, t = 0.0;
-  for (int k = 0; k < kWaves; ++k) {
+  for (int k = 0; k < NW; ++k) {
     stat_merge(a, S.rR[slot][0][k], S.rS[slot][0][k]);
     stat_merge(b, S.rR[slot][1][k], S.rS[slot][1][k]);
     t += S.rS[slot][2][k];
   }
   slot ^= 1;
+}
+
+// Exchange between the NS slices (workgroups) of one sequence's walk: each
+// publishes its record for reduction r and reads every slice's record; all
+// slices then merge the NS records in slice order, so they take the same
+// decisions.
+//   - A record is kXRec doubles as 2 * kXRec 64-bit words: the low 32 bits carry
+//     half of a value, the high 32 bits the tag r + 1.  Words are written and
+//     read with relaxed device-scope atomics (coherent across the XCDs' caches,
+//     no cache flush, each word single-copy atomic), so a reader that sees tag
+//     r + 1 in both words of a value has that value of reduction r.  No counter
+//     and no wait for the writes: a reader polls the words themselves.
+//   - Two record slots alternate (tags r + 1 and r + 3 differ): a slice writes
+//     slot r & 1 again only at r + 2, after it has read every slice's record of
+//     r + 1, which each slice wrote after reading reduction r.  The tags start at
+//     0 (mss_clear_kernel), so a record of an earlier call is never taken.
+//   - The wait is bounded: after kSpinMax polls of a word the slice gives up and
+//     the caller ends the walk with an error, so every workgroup exits.
+// Wave 0 does it (lane j < 2 kXRec writes word j; every lane polls up to
+// 2 kXRec * NS / 64 words); returns false (uniformly) on a timeout.
+constexpr int kXW = 2 * kXRec;  // 64-bit words per record
+template <int NW>
+__device__ __forceinline__ bool exchange(Shared<NW>& S, const double (&mine)[kXRec], uint64_t* rec, int NS, int s,
+                                         int r) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    uint64_t* slot = rec + (size_t)(r & 1) * NS * kXW;
+    const uint32_t tag = (uint32_t)(r + 1);
+#pragma unroll
+    for (int i = 0; i < kXRec; ++i) {  // lanes 2i, 2i + 1: the halves of value i
+      const uint64_t bits = __builtin_bit_cast(uint64_t, mine[i]);
+      const uint32_t half = (lane & 1) ? (uint32_t)(bits >> 32) : (uint32_t)bits;
+      if ((lane >> 1) == i)
+        __hip_atomic_store(slot + s * kXW + lane, ((uint64_t)tag << 32) | half, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
+    int ok = 1;
+    for (int idx = lane; idx < NS * kXW; idx += 64) {
+      uint64_t w = 0;
+      int it = 0;
+      for (; it < kSpinMax; ++it) {
+        w = __hip_atomic_load(slot + idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if ((uint32_t)(w >> 32) == tag) break;
+        __builtin_amdgcn_s_sleep(1);
+      }
+      ok &= it < kSpinMax;
+      ((uint32_t*)&S.xr[0][0])[idx] = (uint32_t)w;  // word t*2*kXRec + j: half (j & 1) of value j/2 of slice t
+    }
+    ok = __all(ok);
+    if (lane == 0) S.xok = ok;
+  }
+  __syncthreads();
+  return S.xok != 0;
 }
 
 // One chunk of a residual pass: p (from raw logits via max/normaliser, or from
@@ -254,13 +319,14 @@ __device__ __forceinline__ void split2(double d, float& hi, float& lo) {
 }
 
 // fp64 sum of one wave's 512 values of a chunk into its segment slot
-__device__ __forceinline__ void seg_store(Shared& S, int ch, const float (&v)[kEPT]) {
+template <int NW>
+__device__ __forceinline__ void seg_store(Shared<NW>& S, int ch, const float (&v)[kEPT]) {
   double sd = 0.0;
 #pragma unroll
   for (int j = 0; j < kEPT; ++j) sd += (double)v[j];
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) sd += __shfl_xor(sd, o);
-  if ((threadIdx.x & 63) == 0) S.segd[ch * kWaves + (threadIdx.x >> 6)] = sd;
+  if ((threadIdx.x & 63) == 0) S.segd[ch * NW + (threadIdx.x >> 6)] = sd;
 }
 
 // Precomputed statistics of one row (the second mode: every LLM and SSM row's
@@ -315,26 +381,60 @@ __global__ __launch_bounds__(256) void row_stats_kernel(int n, int V, int vec, c
   }
 }
 
-template <bool BF16>
-__global__ __launch_bounds__(kThreads) void mss_kernel(int n, int V, int vec, const void* __restrict__ logits,
-                                                       const void* __restrict__ ssm,
-                                                       const int32_t* __restrict__ tokens,
-                                                       const int32_t* __restrict__ parent,
-                                                       const float* __restrict__ u_acc,
-                                                       const float* __restrict__ u_smp, float* __restrict__ ws,
-                                                       int Vpad, const StatRec* __restrict__ pre,
-                                                       int32_t* __restrict__ path_out,
-                                                       int32_t* __restrict__ plen_out, int32_t* __restrict__ bonus,
-                                                       int32_t* __restrict__ status) {
-  __shared__ Shared S;
-  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+// Before a sliced walk: every exchange word's tag at 0 and every status at TV_OK
+// (a slice that gives up raises it to TV_EHIP with an atomic max).
+__global__ __launch_bounds__(256) void mss_clear_kernel(int B, uint64_t* __restrict__ xrec,
+                                                        int32_t* __restrict__ status) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < (size_t)B * 2 * kMaxNS * kXW) xrec[i] = 0ull;
+  if (i < (size_t)B) status[i] = TV_OK;
+}
+
+// The walk of one sequence.  NS == 1: one workgroup per sequence (grid B),
+// everything below without exchanges.  NS > 1: NS workgroups per sequence, each
+// owning a contiguous range of chunks of every row (its vocabulary slice); the
+// row statistics, residual sums, caught values and the draw's slice totals
+// are exchanged at each reduction (see exchange), and the slice holding the
+// drawn token writes the outputs.
+// Sliced walk (256 threads): two waves per SIMD at least (the register budget
+// that lets two of its workgroups share a CU), so its grid of up to 512
+// workgroups is resident at once and no slice waits on a peer that cannot start.
+template <bool BF16, int NTH>
+__global__ __launch_bounds__(NTH, NTH == kThreadsSliced ? 2 : 1) void mss_kernel(int n, int V, int vec, const void* __restrict__ logits,
+                                                  const void* __restrict__ ssm, const int32_t* __restrict__ tokens,
+                                                  const int32_t* __restrict__ parent,
+                                                  const float* __restrict__ u_acc, const float* __restrict__ u_smp,
+                                                  float* __restrict__ ws, int Vpad, const StatRec* __restrict__ pre,
+                                                  int NS, uint64_t* __restrict__ xrec,
+                                                  int32_t* __restrict__ path_out, int32_t* __restrict__ plen_out,
+                                                  int32_t* __restrict__ bonus, int32_t* __restrict__ status) {
+  constexpr int NW = NTH / 64;
+  constexpr int CH = NTH * kEPT;  // elements per chunk
+  __shared__ Shared<NW> S;
+  // sequence b, slice s; with NS > 1 consecutive logical ids (a sequence's
+  // slices) are placed on one XCD, so their exchanges stay close
+  int b = blockIdx.x, s = 0;
+  if (NS > 1) {
+    const int nwg = gridDim.x, wg = blockIdx.x;
+    const int perx = nwg >> 3, rem = nwg & 7, xcd = wg & 7;
+    const int lid = xcd * perx + min(xcd, rem) + (wg >> 3);
+    b = lid / NS;
+    s = lid % NS;
+  }
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const size_t es = BF16 ? 2 : 4;
   const char* lbase = (const char*)logits + (size_t)b * n * V * es;
   const char* sbase = (const char*)ssm + (size_t)b * n * V * es;
   float* const rbase = ws + (size_t)b * 2 * Vpad;  // two residual rows: rbase + ib * Vpad
-  const int nch = (V + kChunk - 1) / kChunk;
-  const int nfull = vec ? V / kChunk : 0;  // chunks wholly inside the row, read with vector loads
+  const int nch = (V + CH - 1) / CH;
+  const int nfull = vec ? V / CH : 0;  // chunks wholly inside the row, read with vector loads
+  const int cps = (nch + NS - 1) / NS;
+  const int c0 = min(nch, s * cps), c1 = min(nch, c0 + cps);  // this slice's chunks
+  const int cf = min(c1, nfull);
+  uint64_t* const rec = NS > 1 ? xrec + (size_t)b * 2 * NS * kXW : nullptr;
+  int xr = 0;  // exchanges so far
   constexpr int kU = kGroup<BF16>;
+  int32_t* pr = path_out + (size_t)b * n;
 
   // ---- load and check the tree: parents before children, tokens inside the vocabulary
   int bad = 0;
@@ -347,8 +447,7 @@ __global__ __launch_bounds__(kThreads) void mss_kernel(int n, int V, int vec, co
     bad = tid == 0 ? p != -1 : (p < 0 || p >= tid || t < 0 || t >= V);
   }
   bad = __syncthreads_or(bad);
-  int32_t* pr = path_out + (size_t)b * n;
-  if (bad) {
+  if (bad) {  // every slice sees the same tree and writes the same values
     if (tid < n) pr[tid] = -1;
     if (tid == 0) {
       plen_out[b] = 0;
@@ -357,6 +456,11 @@ __global__ __launch_bounds__(kThreads) void mss_kernel(int n, int V, int vec, co
     }
     return;
   }
+  // a slice that gave up on its peers: the sequence's status goes to TV_EHIP
+  // (outputs then unspecified) and the walk ends
+  auto give_up = [&]() {
+    if (tid == 0) atomicMax(status + b, TV_EHIP);
+  };
 
   int slot = 0;
   int cur = 0, len = 1;
@@ -379,30 +483,42 @@ __global__ __launch_bounds__(kThreads) void mss_kernel(int n, int V, int vec, co
     }
     __syncthreads();  // S.child visible
     const char* lrow = lbase + (size_t)cur * V * es;
-    const int c1 = k > 0 ? S.child[0] : -1;
-    const char* srow = c1 >= 0 && !pre ? sbase + (size_t)c1 * V * es : nullptr;
+    const int c1st = k > 0 ? S.child[0] : -1;
+    const char* srow = c1st >= 0 && !pre ? sbase + (size_t)c1st * V * es : nullptr;
+    // the two logits the first child's acceptance test reads, loaded now so their
+    // latency hides behind the entry pass (the next child's, behind each residual pass)
+    float lx = 0.f, qxl = 0.f;
+    if (c1st >= 0) {
+      const int x0 = S.tok[c1st];
+      lx = load1<BF16>(lrow, x0);
+      qxl = load1<BF16>(sbase + (size_t)c1st * V * es, x0);
+    }
 
     // ---- node entry: statistics of the LLM row and the first child's SSM row,
-    // precomputed or in one pass
+    // precomputed or in one pass (over this slice, then exchanged)
     Stat sl, sq;
     if (pre) {
       const StatRec a = pre[((size_t)b * n + cur) * 2];
       sl = Stat{a.R, a.S};
-      if (c1 >= 0) {
-        const StatRec q = pre[((size_t)b * n + c1) * 2 + 1];
+      if (c1st >= 0) {
+        const StatRec q = pre[((size_t)b * n + c1st) * 2 + 1];
         sq = Stat{q.R, q.S};
       }
     } else {
-      int c = 0;
-      for (; c + kU <= nfull; c += kU) {
+      // full chunks in groups of kU, every load of a group in flight before any
+      // is used; a last, partial group loads in-range chunks in the missing
+      // places and skips them (the group bound is uniform)
+      int c = c0;
+      for (; c < cf; c += kU) {
         Raw<BF16> a[kU], q[kU];
 #pragma unroll
-        for (int u = 0; u < kU; ++u) a[u].load(lrow, (c + u) * kChunk + tid * kEPT);
+        for (int u = 0; u < kU; ++u) a[u].load(lrow, min(c + u, cf - 1) * CH + tid * kEPT);
         if (srow) {
 #pragma unroll
-          for (int u = 0; u < kU; ++u) q[u].load(srow, (c + u) * kChunk + tid * kEPT);
+          for (int u = 0; u < kU; ++u) q[u].load(srow, min(c + u, cf - 1) * CH + tid * kEPT);
 #pragma unroll
           for (int u = 0; u < kU; ++u) {
+            if (c + u >= cf) break;
             float v[kEPT];
             q[u].unpack(v);
             stat_add8(sq, v);
@@ -410,13 +526,15 @@ __global__ __launch_bounds__(kThreads) void mss_kernel(int n, int V, int vec, co
         }
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
+          if (c + u >= cf) break;
           float v[kEPT];
           a[u].unpack(v);
           stat_add8(sl, v);
         }
       }
-      for (; c < nch; ++c) {
-        const int e0 = c * kChunk + tid * kEPT;
+      c = max(c0, cf);
+      for (; c < c1; ++c) {
+        const int e0 = c * CH + tid * kEPT;
         float v[kEPT];
         load8<BF16>(lrow, e0, V, vec, v);
         stat_add8(sl, v);
@@ -426,7 +544,16 @@ __global__ __launch_bounds__(kThreads) void mss_kernel(int n, int V, int vec, co
         }
       }
       double unused = 0.0;
-      block_reduce(S, slot, sl, sq, unused);
+      block_reduce<NW>(S, slot, sl, sq, unused);
+      if (NS > 1) {
+        const double mine[kXRec] = {sl.R, sl.S, sq.R, sq.S, 0.0, 0.0, 0.0, 0.0};
+        if (!exchange<NW>(S, mine, rec, NS, s, xr++)) return give_up();
+        sl = Stat{}, sq = Stat{};
+        for (int t = 0; t < NS; ++t) {
+          stat_merge(sl, (float)S.xr[t][0], S.xr[t][1]);
+          stat_merge(sq, (float)S.xr[t][2], S.xr[t][3]);
+        }
+      }
     }
 
     // ---- children in order
@@ -437,10 +564,9 @@ __global__ __launch_bounds__(kThreads) void mss_kernel(int n, int V, int vec, co
     int accepted = -1;
     for (int i = 0; i < k; ++i) {
       const int c = S.child[i];
-      const int x = S.tok[c];
       const char* crow = sbase + (size_t)c * V * es;
-      const double px = from_logits ? (double)ex(load1<BF16>(lrow, x), -sl.R) / sl.S : pnext;
-      const double qx = (double)ex(load1<BF16>(crow, x), -sq.R) / sq.S;
+      const double px = from_logits ? (double)ex(lx, -sl.R) / sl.S : pnext;
+      const double qx = (double)ex(qxl, -sq.R) / sq.S;
       if ((double)S.uacc[c] * qx < px) {
         accepted = c;
         break;
@@ -450,6 +576,10 @@ __global__ __launch_bounds__(kThreads) void mss_kernel(int n, int V, int vec, co
       const int cn = i + 1 < k ? S.child[i + 1] : -1;
       const char* nrow = cn >= 0 && !pre ? sbase + (size_t)cn * V * es : nullptr;
       const int xn = cn >= 0 ? S.tok[cn] : -1;
+      if (cn >= 0) {  // the next test's SSM logit (its p comes from the residual pass)
+        qxl = load1<BF16>(sbase + (size_t)cn * V * es, xn);
+        lx = load1<BF16>(lrow, xn);
+      }
       const float* rin = rbase + (size_t)ib * Vpad;
       float* rout = rbase + (size_t)(ib ^ 1) * Vpad;
       Resid R{from_logits, -sl.R, 0.f, 0.f, -sq.R, 0.f, 0.f, rout, xn, S.cap_prev + (i & 1), S.cap_r + (i & 1)};
@@ -458,14 +588,14 @@ __global__ __launch_bounds__(kThreads) void mss_kernel(int n, int V, int vec, co
       double tsum = 0.0;
       Stat sn, unused;  // the next child's SSM row
       {
-        int ch = 0;
+        int ch = c0;
         constexpr int kR = BF16 ? 4 : 2;  // three rows in flight here, so a smaller group
-        for (; ch + kR <= nfull; ch += kR) {
+        for (; ch < cf; ch += kR) {  // partial last group as in the entry pass
           Raw<false> pq[kR];  // the current distribution: raw logits (bf16 uses half) or residual
           Raw<BF16> qq[kR], nq[kR];
 #pragma unroll
           for (int u = 0; u < kR; ++u) {
-            const int e0 = (ch + u) * kChunk + tid * kEPT;
+            const int e0 = min(ch + u, cf - 1) * CH + tid * kEPT;
             if (from_logits) {
               if (BF16)
                 pq[u].w[0] = *(const uint4*)((const uint16_t*)lrow + e0);
@@ -476,12 +606,13 @@ __global__ __launch_bounds__(kThreads) void mss_kernel(int n, int V, int vec, co
             }
           }
 #pragma unroll
-          for (int u = 0; u < kR; ++u) qq[u].load(crow, (ch + u) * kChunk + tid * kEPT);
+          for (int u = 0; u < kR; ++u) qq[u].load(crow, min(ch + u, cf - 1) * CH + tid * kEPT);
           if (nrow) {
 #pragma unroll
-            for (int u = 0; u < kR; ++u) nq[u].load(nrow, (ch + u) * kChunk + tid * kEPT);
+            for (int u = 0; u < kR; ++u) nq[u].load(nrow, min(ch + u, cf - 1) * CH + tid * kEPT);
 #pragma unroll
             for (int u = 0; u < kR; ++u) {
+              if (ch + u >= cf) break;
               float v[kEPT];
               nq[u].unpack(v);
               stat_add8(sn, v);
@@ -489,6 +620,7 @@ __global__ __launch_bounds__(kThreads) void mss_kernel(int n, int V, int vec, co
           }
 #pragma unroll
           for (int u = 0; u < kR; ++u) {
+            if (ch + u >= cf) break;
             float pv[kEPT], qv[kEPT];
             if (from_logits && BF16) {
               Raw<true> t;
@@ -498,11 +630,11 @@ __global__ __launch_bounds__(kThreads) void mss_kernel(int n, int V, int vec, co
               pq[u].unpack(pv);
             }
             qq[u].unpack(qv);
-            tsum += (double)R.chunk((ch + u) * kChunk + tid * kEPT, pv, qv);
+            tsum += (double)R.chunk((ch + u) * CH + tid * kEPT, pv, qv);
           }
         }
-        for (; ch < nch; ++ch) {
-          const int e0 = ch * kChunk + tid * kEPT;
+        for (ch = max(c0, cf); ch < c1; ++ch) {
+          const int e0 = ch * CH + tid * kEPT;
           float pv[kEPT], qv[kEPT];
           if (from_logits) {
             load8<BF16>(lrow, e0, V, vec, pv);
@@ -519,14 +651,27 @@ __global__ __launch_bounds__(kThreads) void mss_kernel(int n, int V, int vec, co
           }
         }
       }
-      block_reduce(S, slot, sn, unused, tsum);
+      block_reduce<NW>(S, slot, sn, unused, tsum);
+      float capp = S.cap_prev[i & 1], capr = S.cap_r[i & 1];  // caught by the thread owning xn
+      if (NS > 1) {
+        const bool own = xn >= c0 * CH && xn < c1 * CH;
+        const double mine[kXRec] = {sn.R, sn.S, tsum, own ? (double)capp : 0.0, own ? (double)capr : 0.0,
+                                    own ? 1.0 : 0.0, 0.0, 0.0};
+        if (!exchange<NW>(S, mine, rec, NS, s, xr++)) return give_up();
+        sn = Stat{}, tsum = 0.0;
+        for (int t = 0; t < NS; ++t) {
+          stat_merge(sn, (float)S.xr[t][0], S.xr[t][1]);
+          tsum += S.xr[t][2];
+          if (S.xr[t][5] != 0.0) capp = (float)S.xr[t][3], capr = (float)S.xr[t][4];
+        }
+      }
       if (tsum > 0.0) {
-        pnext = cn >= 0 ? (double)S.cap_r[i & 1] / tsum : 0.0;
+        pnext = cn >= 0 ? (double)capr / tsum : 0.0;
         from_logits = false;
         ib ^= 1;
         T = tsum;
       } else {
-        pnext = cn >= 0 ? (double)S.cap_prev[i & 1] : 0.0;
+        pnext = cn >= 0 ? (double)capp : 0.0;
       }
       if (pre && cn >= 0) {
         const StatRec q = pre[((size_t)b * n + cn) * 2 + 1];
@@ -544,19 +689,20 @@ __global__ __launch_bounds__(kThreads) void mss_kernel(int n, int V, int vec, co
     // ---- final draw from the current distribution (unnormalised values v)
     const float* rin = rbase + (size_t)ib * Vpad;
     {
-      int ch = 0;
-      for (; ch + kU <= nfull; ch += kU) {
+      int ch = c0;
+      for (; ch < cf; ch += kU) {  // partial last group as in the entry pass
         Raw<BF16> lq[kU];
         Raw<false> rq[kU];
         if (from_logits) {
 #pragma unroll
-          for (int u = 0; u < kU; ++u) lq[u].load(lrow, (ch + u) * kChunk + tid * kEPT);
+          for (int u = 0; u < kU; ++u) lq[u].load(lrow, min(ch + u, cf - 1) * CH + tid * kEPT);
         } else {
 #pragma unroll
-          for (int u = 0; u < kU; ++u) rq[u].load(rin, (ch + u) * kChunk + tid * kEPT);
+          for (int u = 0; u < kU; ++u) rq[u].load(rin, min(ch + u, cf - 1) * CH + tid * kEPT);
         }
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
+          if (ch + u >= cf) break;
           float v[kEPT];
           if (from_logits) {
             lq[u].unpack(v);
@@ -565,11 +711,11 @@ __global__ __launch_bounds__(kThreads) void mss_kernel(int n, int V, int vec, co
           } else {
             rq[u].unpack(v);
           }
-          seg_store(S, ch + u, v);
+          seg_store<NW>(S, ch + u, v);
         }
       }
-      for (; ch < nch; ++ch) {
-        const int e0 = ch * kChunk + tid * kEPT;
+      for (ch = max(c0, cf); ch < c1; ++ch) {
+        const int e0 = ch * CH + tid * kEPT;
         float v[kEPT];
         if (from_logits) {
           load8<BF16>(lrow, e0, V, vec, v);
@@ -580,26 +726,51 @@ __global__ __launch_bounds__(kThreads) void mss_kernel(int n, int V, int vec, co
           r1.load(rin, e0);
           r1.unpack(v);
         }
-        seg_store(S, ch, v);
+        seg_store<NW>(S, ch, v);
       }
     }
     __syncthreads();
+    // the slice's total mass (segments [sg0, sg1) in order), then with NS > 1 the
+    // slices' totals: the first slice whose running total passes u * total owns
+    // the draw (the last slice with mass, if rounding leaves none)
+    const int sg0 = c0 * NW, sg1 = c1 * NW;
     if (wv == 0) {
-      const int nseg = nch * kWaves;
-      const float u = u_smp[(size_t)b * n + cur];
-      // total mass, then the first segment whose running sum passes u * total
       double tot = 0.0;
-      for (int s0 = 0; s0 < nseg; s0 += 64) {
-        double x = s0 + lane < nseg ? S.segd[s0 + lane] : 0.0;
+      for (int s0 = sg0; s0 < sg1; s0 += 64) {
+        double x = s0 + lane < sg1 ? S.segd[s0 + lane] : 0.0;
 #pragma unroll
         for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
         tot += x;
       }
-      const double target = (double)u * tot;
-      double run = 0.0;
+      if (lane == 0) S.xtot = tot;
+    }
+    __syncthreads();
+    const float u = u_smp[(size_t)b * n + cur];
+    double target = (double)u * S.xtot, run0 = 0.0;
+    int owner = 0;
+    if (NS > 1) {
+      const double mine[kXRec] = {S.xtot, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+      if (!exchange<NW>(S, mine, rec, NS, s, xr++)) return give_up();
+      double grand = 0.0;
+      for (int t = 0; t < NS; ++t) grand += S.xr[t][0];
+      target = (double)u * grand;
+      owner = -1;
+      int lastm = 0;
+      double prefix = 0.0, pre_last = 0.0;
+      for (int t = 0; t < NS; ++t) {
+        const double tt = S.xr[t][0];
+        if (owner < 0 && prefix + tt > target) owner = t, run0 = prefix;
+        if (tt > 0.0) lastm = t, pre_last = prefix;
+        prefix += tt;
+      }
+      if (owner < 0) owner = lastm, run0 = pre_last;
+    }
+    if (s != owner) return;
+    if (wv == 0) {
+      double run = run0;
       int seg = -1;
-      for (int s0 = 0; s0 < nseg && seg < 0; s0 += 64) {
-        const double x = s0 + lane < nseg ? S.segd[s0 + lane] : 0.0;
+      for (int s0 = sg0; s0 < sg1 && seg < 0; s0 += 64) {
+        const double x = s0 + lane < sg1 ? S.segd[s0 + lane] : 0.0;
         double inc = x;  // inclusive prefix over the lanes
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) {
@@ -618,8 +789,8 @@ __global__ __launch_bounds__(kThreads) void mss_kernel(int n, int V, int vec, co
       int y = -1;
       if (seg >= 0) {
         // the segment's 512 elements: lane l holds elements seg_base + l*8 .. +8
-        const int ch = seg / kWaves, w = seg % kWaves;
-        const int e0 = ch * kChunk + (w * 64 + lane) * kEPT;
+        const int ch = seg / NW, w = seg % NW;
+        const int e0 = ch * CH + (w * 64 + lane) * kEPT;
         float v[kEPT];
         if (from_logits) {
           load8<BF16>(lrow, e0, V, vec, v);
@@ -656,11 +827,12 @@ __global__ __launch_bounds__(kThreads) void mss_kernel(int n, int V, int vec, co
         }
       }
       if (y < 0) {
-        // rounding left u * total at or past the end: the last element with mass
+        // rounding left u * total at or past the end (of this slice, the last
+        // one with mass): the last element with mass
         int last = -1;
-        for (int ch = nch - 1; ch >= 0 && last < 0; --ch) {
-          for (int part = 0; part < kWaves && last < 0; ++part) {
-            const int e0 = ch * kChunk + ((kWaves - 1 - part) * 64 + lane) * kEPT;
+        for (int ch = c1 - 1; ch >= c0 && last < 0; --ch) {
+          for (int part = 0; part < NW && last < 0; ++part) {
+            const int e0 = ch * CH + ((NW - 1 - part) * 64 + lane) * kEPT;
             float v[kEPT];
             if (from_logits) {
               load8<BF16>(lrow, e0, V, vec, v);
@@ -688,7 +860,7 @@ __global__ __launch_bounds__(kThreads) void mss_kernel(int n, int V, int vec, co
     if (tid == 0) {
       plen_out[b] = len;
       bonus[b] = S.result;
-      if (status) status[b] = TV_OK;
+      if (status && NS == 1) status[b] = TV_OK;  // sliced: set to TV_OK before the walk
     }
     return;
   }
@@ -696,9 +868,14 @@ __global__ __launch_bounds__(kThreads) void mss_kernel(int n, int V, int vec, co
 
 }  // namespace
 
+// Workspace: two fp32 residual rows per sequence, the precomputed row statistics,
+// and for the sliced walk two slots of exchange records (kMaxNS slices) per
+// sequence.
 size_t mss_workspace_bytes(int B, int n, int V) {
   const size_t vpad = (size_t)(V + kChunk - 1) / kChunk * kChunk;
-  return (size_t)B * 2 * vpad * sizeof(float) + (size_t)B * n * 2 * sizeof(StatRec);
+  const size_t rows = (size_t)B * 2 * vpad * sizeof(float);
+  const size_t stats = ((size_t)B * n * 2 * sizeof(StatRec) + 255) & ~(size_t)255;
+  return rows + stats + (size_t)B * 2 * kMaxNS * kXW * sizeof(uint64_t);
 }
 
 int mss_precompute(int B, int n, int V, int bf16, int mode) {
@@ -708,15 +885,38 @@ int mss_precompute(int B, int n, int V, int bf16, int mode) {
   return (double)B * n * V * (bf16 ? 2 : 4) * 2 <= (double)(1u << 30);
 }
 
+// Slices per sequence for the sliced walk: as many as keep the whole grid
+// resident at once (the workgroups of the sliced kernel that fit on one CU, as
+// the runtime reports for the current device, times its CUs) and give every
+// slice at least one chunk; 1 when that is a single slice (or the query fails).
+int mss_slices(int B, int V, int bf16) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 1;
+  const hipError_t e =
+      bf16 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mss_kernel<true, kThreadsSliced>, kThreadsSliced, 0)
+           : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mss_kernel<false, kThreadsSliced>, kThreadsSliced, 0);
+  if (e != hipSuccess || per_cu < 1 || cus < 1) return 1;
+  const int nch = (V + kThreadsSliced * kEPT - 1) / (kThreadsSliced * kEPT);
+  const long long resident = (long long)per_cu * cus;
+  int ns = (int)min((long long)min(kMaxNS, nch), resident / max(B, 1));
+  if (ns < 2) return 1;
+  const int cps = (nch + ns - 1) / ns;
+  return (nch + cps - 1) / cps;  // no empty slice
+}
+
 hipError_t launch_mss(int B, int n, int V, int bf16, int mode, const void* logits, const void* ssm,
                       const int32_t* tokens, const int32_t* parent, const float* u_acc, const float* u_smp,
                       float* ws, int32_t* path, int32_t* plen, int32_t* bonus, int32_t* status, hipStream_t s) {
   if (B == 0) return hipSuccess;
   const int vpad = (V + kChunk - 1) / kChunk * kChunk;
   const int vec = ((size_t)V * (bf16 ? 2 : 4)) % 16 == 0;
+  char* base = (char*)ws + (size_t)B * 2 * vpad * sizeof(float);
   StatRec* pre = nullptr;
-  if (mss_precompute(B, n, V, bf16, mode)) {
-    pre = (StatRec*)(ws + (size_t)B * 2 * vpad);
+  const int pc = mss_precompute(B, n, V, bf16, mode);
+  if (pc) {
+    pre = (StatRec*)base;
     if (bf16)
       hipLaunchKernelGGL(row_stats_kernel<true>, dim3(B * n * 2), dim3(256), 0, s, n, V, vec, logits, ssm, pre);
     else
@@ -724,12 +924,30 @@ hipError_t launch_mss(int B, int n, int V, int bf16, int mode, const void* logit
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  base += ((size_t)B * n * 2 * sizeof(StatRec) + 255) & ~(size_t)255;
+  uint64_t* xrec = (uint64_t*)base;
+  const int ns = (!pc && status != nullptr && (mode == 0 || mode == 3)) ? mss_slices(B, V, bf16) : 1;
+  if (ns > 1) {
+    const size_t words = (size_t)B * 2 * kMaxNS * kXW;
+    hipLaunchKernelGGL(mss_clear_kernel, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, s, B, xrec, status);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (bf16)
+      hipLaunchKernelGGL((mss_kernel<true, kThreadsSliced>), dim3(B * ns), dim3(kThreadsSliced), 0, s, n, V, vec,
+                         logits, ssm, tokens, parent, u_acc, u_smp, ws, vpad, nullptr, ns, xrec, path, plen,
+                         bonus, status);
+    else
+      hipLaunchKernelGGL((mss_kernel<false, kThreadsSliced>), dim3(B * ns), dim3(kThreadsSliced), 0, s, n, V, vec,
+                         logits, ssm, tokens, parent, u_acc, u_smp, ws, vpad, nullptr, ns, xrec, path, plen,
+                         bonus, status);
+    return hipGetLastError();
+  }
   if (bf16)
-    hipLaunchKernelGGL(mss_kernel<true>, dim3(B), dim3(kThreads), 0, s, n, V, vec, logits, ssm, tokens, parent,
-                       u_acc, u_smp, ws, vpad, pre, path, plen, bonus, status);
+    hipLaunchKernelGGL((mss_kernel<true, kThreads>), dim3(B), dim3(kThreads), 0, s, n, V, vec, logits, ssm, tokens,
+                       parent, u_acc, u_smp, ws, vpad, pre, 1, nullptr, path, plen, bonus, status);
   else
-    hipLaunchKernelGGL(mss_kernel<false>, dim3(B), dim3(kThreads), 0, s, n, V, vec, logits, ssm, tokens, parent,
-                       u_acc, u_smp, ws, vpad, pre, path, plen, bonus, status);
+    hipLaunchKernelGGL((mss_kernel<false, kThreads>), dim3(B), dim3(kThreads), 0, s, n, V, vec, logits, ssm, tokens,
+                       parent, u_acc, u_smp, ws, vpad, pre, 1, nullptr, path, plen, bonus, status);
   return hipGetLastError();
 }
 
