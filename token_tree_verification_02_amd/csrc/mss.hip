@@ -102,6 +102,17 @@ template <bool BF16>
 __device__ __forceinline__ float load1(const void* row, int x) {
   return BF16 ? bf16_to_f32(((const uint16_t*)row)[x]) : ((const float*)row)[x];
 }
+// The same as raw bits, decoded by use1 where the value is needed: a load issued
+// early then waits there, not right after its issue.
+template <bool BF16>
+__device__ __forceinline__ uint32_t load1raw(const void* row, int x) {
+  return BF16 ? (uint32_t)((const uint16_t*)row)[x] : ((const uint32_t*)row)[x];
+}
+template <bool BF16>
+__device__ __forceinline__ float use1(uint32_t raw) {
+  asm volatile("" : "+v"(raw));  // the decode stays here
+  return BF16 ? bf16_to_f32((uint16_t)raw) : __uint_as_float(raw);
+}
 
 // exp(v - r / log2(e)) as exp2(v * log2(e) - r): one FMA and the hardware exp2;
 // the FMA rounds the argument once, so a value carries about 1e-7 relative error.
@@ -487,11 +498,11 @@ __global__ __launch_bounds__(NTH, NTH == kThreadsSliced ? 2 : 1) void mss_kernel
     const char* srow = c1st >= 0 && !pre ? sbase + (size_t)c1st * V * es : nullptr;
     // the two logits the first child's acceptance test reads, loaded now so their
     // latency hides behind the entry pass (the next child's, behind each residual pass)
-    float lx = 0.f, qxl = 0.f;
+    uint32_t lx = 0, qxl = 0;
     if (c1st >= 0) {
       const int x0 = S.tok[c1st];
-      lx = load1<BF16>(lrow, x0);
-      qxl = load1<BF16>(sbase + (size_t)c1st * V * es, x0);
+      lx = load1raw<BF16>(lrow, x0);
+      qxl = load1raw<BF16>(sbase + (size_t)c1st * V * es, x0);
     }
 
     // ---- node entry: statistics of the LLM row and the first child's SSM row,
@@ -565,8 +576,8 @@ __global__ __launch_bounds__(NTH, NTH == kThreadsSliced ? 2 : 1) void mss_kernel
     for (int i = 0; i < k; ++i) {
       const int c = S.child[i];
       const char* crow = sbase + (size_t)c * V * es;
-      const double px = from_logits ? (double)ex(lx, -sl.R) / sl.S : pnext;
-      const double qx = (double)ex(qxl, -sq.R) / sq.S;
+      const double px = from_logits ? (double)ex(use1<BF16>(lx), -sl.R) / sl.S : pnext;
+      const double qx = (double)ex(use1<BF16>(qxl), -sq.R) / sq.S;
       if ((double)S.uacc[c] * qx < px) {
         accepted = c;
         break;
@@ -577,8 +588,8 @@ __global__ __launch_bounds__(NTH, NTH == kThreadsSliced ? 2 : 1) void mss_kernel
       const char* nrow = cn >= 0 && !pre ? sbase + (size_t)cn * V * es : nullptr;
       const int xn = cn >= 0 ? S.tok[cn] : -1;
       if (cn >= 0) {  // the next test's SSM logit (its p comes from the residual pass)
-        qxl = load1<BF16>(sbase + (size_t)cn * V * es, xn);
-        lx = load1<BF16>(lrow, xn);
+        qxl = load1raw<BF16>(sbase + (size_t)cn * V * es, xn);
+        lx = load1raw<BF16>(lrow, xn);
       }
       const float* rin = rbase + (size_t)ib * Vpad;
       float* rout = rbase + (size_t)(ib ^ 1) * Vpad;
@@ -589,7 +600,9 @@ __global__ __launch_bounds__(NTH, NTH == kThreadsSliced ? 2 : 1) void mss_kernel
       Stat sn, unused;  // the next child's SSM row
       {
         int ch = c0;
-        constexpr int kR = BF16 ? 4 : 2;  // three rows in flight here, so a smaller group
+        // three rows in flight here, so a smaller group; a slice of the sliced walk
+        // holds few chunks, so there the whole slice goes in one group
+        constexpr int kR = NTH == kThreadsSliced ? (BF16 ? 8 : 4) : (BF16 ? 4 : 2);
         for (; ch < cf; ch += kR) {  // partial last group as in the entry pass
           Raw<false> pq[kR];  // the current distribution: raw logits (bf16 uses half) or residual
           Raw<BF16> qq[kR], nq[kR];
