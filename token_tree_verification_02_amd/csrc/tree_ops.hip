@@ -102,7 +102,7 @@ __global__ __launch_bounds__(256) void argmax_kernel(const void* __restrict__ lo
                                                      int32_t* __restrict__ am) {
   constexpr bool W16 = DT != TV_F32;
   constexpr int EPV = W16 ? 8 : 4;  // elements per 16-byte vector
-  constexpr int R = 8;               // vectors in flight per thread
+  constexpr int R = 16;              // vectors in flight per thread (a 32000-entry bf16 row in one round)
   const size_t row = blockIdx.x;
   const int tid = threadIdx.x;
   const size_t es = W16 ? 2 : 4;
