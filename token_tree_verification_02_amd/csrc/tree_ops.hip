@@ -81,7 +81,7 @@ __device__ __forceinline__ bool beats(float v2, int i2, float v1, int i1) {
   return v2 > v1 || (v2 == v1 && i2 < i1) || (i1 == INT_MAX && i2 != INT_MAX);
 }
 
-// One workgroup of 256 threads per logits row.  Each thread loads 8 16-byte
+// One workgroup of 256 threads per logits row.  Each thread loads 16 16-byte
 // vectors per round before it compares anything, keeps the index of the first
 // vector whose maximum beats its running best, and at the end re-reads that one
 // vector (a cache hit) to find the lowest index of the maximum inside it; a wave
