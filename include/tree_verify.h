@@ -260,9 +260,9 @@ int tree_verify_greedy(int B, int n, int V, int logits_dtype, const void* logits
  *     only for residuals and the final draw; 3 = mode 1 with each sequence's
  *     walk spread over up to 16 workgroups, each owning a slice of the
  *     vocabulary, which exchange row statistics through the workspace at each
- *     step (B * slices <= 512, so the grid is resident at once; it needs
- *     `status`, else mode 1 runs).  0 takes 2 while all rows together are at
- *     most 1 GiB, else 3.  The results are the same in every mode.  In mode 3
+ *     step (slices chosen so that all B * slices workgroups fit on the device
+ *     at once, 512 on MI355X; it needs `status`, else mode 1 runs).  0 takes
+ *     2 while all rows together are at most 1 GiB, else 3.  The results are the same in every mode.  In mode 3
  *     the exchange waits are bounded: if the slices of a sequence cannot all
  *     run at once (another process holding the GPU's compute units), a slice
  *     gives up, the sequence's status is TV_EHIP and its outputs are
@@ -283,6 +283,16 @@ int tree_verify_stochastic(int B, int n, int V, int logits_dtype, int mode, cons
                            const float* u_sample, int32_t* path_out,
                            int32_t* path_len, int32_t* bonus, int32_t* status,
                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* tree_verify_stochastic_set_poll_limit: the bound on mode 3's waits.  A slice
+ * reads each word of its peers' exchange records at most `polls` times
+ * (default 262144, each poll a device-scope load and a short sleep) before it
+ * gives up as described above.  The limit is process-wide and is read when a
+ * call is enqueued; calls already enqueued keep theirs.  0 makes every slice
+ * give up at its first exchange, so the give-up path can be exercised from the
+ * host.  polls < 0: TV_EINVAL.  *previous (if not NULL) receives the limit in
+ * force before the call. */
+int tree_verify_stochastic_set_poll_limit(int polls, int* previous);
 
 /* ---------------------------------------------------------------------------
  * Token-tree construction (the explainer's multi-draft section): the

@@ -68,6 +68,12 @@ namespace tv {
 
 size_t sk_sched_bytes(int B) { return (((size_t)B + 5) * sizeof(int32_t) + 255) & ~(size_t)255; }
 size_t mss_workspace_bytes(int B, int n, int V) { return (size_t)B * 2 * (size_t)V * sizeof(float) + (size_t)n; }
+int mss_set_poll_limit(int polls) {
+  static int limit = 1 << 18;
+  const int prev = limit;
+  limit = polls;
+  return prev;
+}
 
 hipError_t launch_attn_bf16(const AttnArgs& a, const AttnPlan& p, hipStream_t) {
   check_plan_common(a, p);
@@ -288,6 +294,11 @@ void sweep_others(int iters) {
                                         (const float*)P(kDev), (const float*)P(kDev), O, O, O, O,
                                         rnd() % 3 ? P(kDev + 0x20000) : nullptr,
                                         rnd() % 4 ? sws : sws / 2, nullptr));
+    {
+      int prev = -7;
+      const int polls = pick({-1, 0, 1, 1 << 18});
+      check_status(tree_verify_stochastic_set_poll_limit(polls, rnd() % 2 ? &prev : nullptr));
+    }
     check_status(tree_expand_topk(B, pick({-1, 0, 1, 4}), V, pick({0, 1, 4, 16, 17}), pick({0, 1, 64, 256, 300}), dt,
                                   nul ? nullptr : P(kDev), I, I, O, O, O, (float*)O, O, O, nullptr));
     check_status(tree_merge_drafts(B, pick({0, 1, 8, 64, 65}), pick({-1, 0, 8, 255}), pick({0, 1, 256, 257}),

@@ -179,6 +179,22 @@ def test_stochastic_argument_errors(lib):
     assert call(0, 7, 10, tv.TV_F32, ptrs=[None] * 10, w=None, wb=0) == tv.TV_OK
 
 
+def test_stochastic_poll_limit(lib):
+    """The bound on the sliced walk's waits: set and read back; a negative value is
+    refused and leaves the limit alone."""
+    prev = tv.stochastic_set_poll_limit(7)
+    try:
+        assert prev == 1 << 18
+        assert tv.stochastic_set_poll_limit(0) == 7
+        old = ctypes.c_int32(-5)
+        assert lib.tree_verify_stochastic_set_poll_limit(-1, ctypes.byref(old)) == tv.TV_EINVAL
+        assert old.value == -5
+        assert lib.tree_verify_stochastic_set_poll_limit(3, None) == tv.TV_OK
+        assert tv.stochastic_set_poll_limit(0) == 3
+    finally:
+        tv.stochastic_set_poll_limit(prev)
+
+
 def test_construction_argument_errors(lib):
     P = [0x100000] * 9
     ex = lambda B, F, V, k, n_max, dt=tv.TV_BF16, ptrs=P: lib.tree_expand_topk(B, F, V, k, n_max, dt, *ptrs, None)

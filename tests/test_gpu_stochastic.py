@@ -150,6 +150,27 @@ def test_stochastic_modes_agree(name):
             np.testing.assert_array_equal(a, b_, err_msg=f"mode {mode} {what}")
 
 
+def test_sliced_walk_give_up_path():
+    """The sliced walk's bounded wait, forced from the host: with a poll limit of 0
+    every slice gives up at its first exchange, the call still completes and every
+    sequence reports TV_EHIP; with the limit restored, the next call on the same
+    workspace agrees with mode 1 again (the exchange words are cleared per call)."""
+    cfg, noise = CASES["llama_v32000"]                    # 16 sequences, V = 32000: 16 slices each
+    log("case stochastic give-up path (poll limit 0)")
+    w = W.make_stochastic(cfg, seed=29, ssm_noise=noise)
+    prev = _lib.stochastic_set_poll_limit(0)
+    try:
+        status = run_gpu(w, 3)[3]
+    finally:
+        _lib.stochastic_set_poll_limit(prev)
+    assert prev == 1 << 18
+    assert (status == _lib.TV_EHIP).all(), status
+    ref, got = run_gpu(w, 1), run_gpu(w, 3)
+    for a, b_, what in zip(ref, got, ("path", "path_len", "bonus", "status")):
+        np.testing.assert_array_equal(a, b_, err_msg=what)
+    assert (got[3] == 0).all()
+
+
 def test_gpu_emits_the_llm_distribution():
     """The pages' guarantee, on the GPU: 20000 verification steps of one small
     tree with fresh draft tokens and uniforms; the first emitted token follows

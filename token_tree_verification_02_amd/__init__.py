@@ -13,4 +13,5 @@ from ._lib import (TV_BF16, TV_EHIP, TV_EINVAL, TV_ETOPOLOGY, TV_EUNSUPPORTED, T
                    tree_attention, tree_attention_noalloc, tree_build, tree_commit_kv, tree_expand_topk,
                    tree_merge_drafts,
                    tree_verify_greedy,
-                   tree_verify_stochastic, stochastic_workspace_size, validate_host, workspace_size)
+                   tree_verify_stochastic, stochastic_workspace_size, stochastic_set_poll_limit, validate_host,
+                   workspace_size)

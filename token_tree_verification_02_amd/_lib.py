@@ -53,6 +53,7 @@ SIGNATURES = {
     "tree_verify_greedy": (_c_int, [_c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "tree_verify_stochastic_workspace_size": (_size_t, [_c_int, _c_int, _c_int]),
     "tree_verify_stochastic": (_c_int, [_c_int] * 5 + [_vp] * 11 + [_size_t, _vp]),
+    "tree_verify_stochastic_set_poll_limit": (_c_int, [_c_int, ctypes.POINTER(_c_int)]),
     "tree_expand_topk": (_c_int, [_c_int] * 6 + [_vp] * 9 + [_vp]),
     "tree_merge_drafts": (_c_int, [_c_int] * 4 + [_vp] * 9 + [_vp]),
     "tree_commit_kv": (_c_int, [ctypes.POINTER(AttnDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
@@ -241,6 +242,15 @@ def tree_verify_stochastic(logits, ssm_logits, tokens, parent, u_accept, u_sampl
                                        _ptr(bonus), _ptr(status), _ptr(workspace), wbytes, _stream(stream))
     _check(rc, "tree_verify_stochastic")
     return path, path_len, bonus, status
+
+
+def stochastic_set_poll_limit(polls: int) -> int:
+    """Bound on the polls of one exchange word in stochastic mode 3 (process-wide);
+    returns the previous limit."""
+    prev = _c_int(0)
+    _check(load().tree_verify_stochastic_set_poll_limit(int(polls), ctypes.byref(prev)),
+           "tree_verify_stochastic_set_poll_limit")
+    return int(prev.value)
 
 
 def tree_expand_topk(ssm_logits, frontier, n_cur, parent, depth, tokens, k, *, scores=None, n_out=None, status=None,

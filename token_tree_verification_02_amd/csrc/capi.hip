@@ -317,6 +317,13 @@ int tree_verify_stochastic(int B, int n, int V, int logits_dtype, int mode, cons
   return TV_OK;
 }
 
+int tree_verify_stochastic_set_poll_limit(int polls, int* previous) {
+  if (polls < 0) return fail(TV_EINVAL, "polls=%d < 0", polls);
+  const int prev = tv::mss_set_poll_limit(polls);
+  if (previous) *previous = prev;
+  return TV_OK;
+}
+
 int tree_expand_topk(int B, int F, int V, int k, int n_max, int logits_dtype, const void* ssm_logits,
                      const int32_t* frontier, const int32_t* n_cur, int32_t* parent, int32_t* depth, int32_t* tokens,
                      float* scores, int32_t* n_out, int32_t* status, void* stream) {

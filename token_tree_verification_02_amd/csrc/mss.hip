@@ -30,6 +30,8 @@
 // wrote itself.
 #include <limits.h>
 
+#include <atomic>
+
 #include "tv_internal.h"
 
 namespace tv {
@@ -43,7 +45,7 @@ constexpr int kSeg = 64 * kEPT;              // 512 elements: one wave's share o
 constexpr int kMaxSeg = TV_MSS_VMAX / kSeg;  // 2048
 constexpr int kMaxNS = 16;                   // vocabulary slices per sequence (sliced walk)
 constexpr int kXRec = 8;                     // doubles per exchange record
-constexpr int kSpinMax = 1 << 18;            // polls before a slice gives up on its peers
+constexpr int kSpinMax = 1 << 18;            // default: polls before a slice gives up on its peers
 // A pass over a row visits chunks in groups of kU whose loads are all issued
 // before any of them is used, so a workgroup keeps kU * 8 KB of each
 // row in flight instead of waiting out one memory latency per chunk.
@@ -238,14 +240,15 @@ __device__ __forceinline__ void block_reduce(Shared<NW>& S, int& slot, Stat& a, 
 //     slot r & 1 again only at r + 2, after it has read every slice's record of
 //     r + 1, which each slice wrote after reading reduction r.  The tags start at
 //     0 (mss_clear_kernel), so a record of an earlier call is never taken.
-//   - The wait is bounded: after kSpinMax polls of a word the slice gives up and
+//   - The wait is bounded: after `spin` polls of a word (kSpinMax unless the
+//     host set another limit) the slice gives up and
 //     the caller ends the walk with an error, so every workgroup exits.
 // Wave 0 does it (lane j < 2 kXRec writes word j; every lane polls up to
 // 2 kXRec * NS / 64 words); returns false (uniformly) on a timeout.
 constexpr int kXW = 2 * kXRec;  // 64-bit words per record
 template <int NW>
 __device__ __forceinline__ bool exchange(Shared<NW>& S, const double (&mine)[kXRec], uint64_t* rec, int NS, int s,
-                                         int r) {
+                                         int r, int spin) {
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
     uint64_t* slot = rec + (size_t)(r & 1) * NS * kXW;
@@ -262,12 +265,12 @@ __device__ __forceinline__ bool exchange(Shared<NW>& S, const double (&mine)[kXR
     for (int idx = lane; idx < NS * kXW; idx += 64) {
       uint64_t w = 0;
       int it = 0;
-      for (; it < kSpinMax; ++it) {
+      for (; it < spin; ++it) {
         w = __hip_atomic_load(slot + idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if ((uint32_t)(w >> 32) == tag) break;
         __builtin_amdgcn_s_sleep(1);
       }
-      ok &= it < kSpinMax;
+      ok &= it < spin;
       ((uint32_t*)&S.xr[0][0])[idx] = (uint32_t)w;  // word t*2*kXRec + j: half (j & 1) of value j/2 of slice t
     }
     ok = __all(ok);
@@ -416,7 +419,7 @@ __global__ __launch_bounds__(NTH, NTH == kThreadsSliced ? 2 : 1) void mss_kernel
                                                   const int32_t* __restrict__ parent,
                                                   const float* __restrict__ u_acc, const float* __restrict__ u_smp,
                                                   float* __restrict__ ws, int Vpad, const StatRec* __restrict__ pre,
-                                                  int NS, uint64_t* __restrict__ xrec,
+                                                  int NS, uint64_t* __restrict__ xrec, int spin,
                                                   int32_t* __restrict__ path_out, int32_t* __restrict__ plen_out,
                                                   int32_t* __restrict__ bonus, int32_t* __restrict__ status) {
   constexpr int NW = NTH / 64;
@@ -558,7 +561,7 @@ __global__ __launch_bounds__(NTH, NTH == kThreadsSliced ? 2 : 1) void mss_kernel
       block_reduce<NW>(S, slot, sl, sq, unused);
       if (NS > 1) {
         const double mine[kXRec] = {sl.R, sl.S, sq.R, sq.S, 0.0, 0.0, 0.0, 0.0};
-        if (!exchange<NW>(S, mine, rec, NS, s, xr++)) return give_up();
+        if (!exchange<NW>(S, mine, rec, NS, s, xr++, spin)) return give_up();
         sl = Stat{}, sq = Stat{};
         for (int t = 0; t < NS; ++t) {
           stat_merge(sl, (float)S.xr[t][0], S.xr[t][1]);
@@ -670,7 +673,7 @@ __global__ __launch_bounds__(NTH, NTH == kThreadsSliced ? 2 : 1) void mss_kernel
         const bool own = xn >= c0 * CH && xn < c1 * CH;
         const double mine[kXRec] = {sn.R, sn.S, tsum, own ? (double)capp : 0.0, own ? (double)capr : 0.0,
                                     own ? 1.0 : 0.0, 0.0, 0.0};
-        if (!exchange<NW>(S, mine, rec, NS, s, xr++)) return give_up();
+        if (!exchange<NW>(S, mine, rec, NS, s, xr++, spin)) return give_up();
         sn = Stat{}, tsum = 0.0;
         for (int t = 0; t < NS; ++t) {
           stat_merge(sn, (float)S.xr[t][0], S.xr[t][1]);
@@ -763,7 +766,7 @@ __global__ __launch_bounds__(NTH, NTH == kThreadsSliced ? 2 : 1) void mss_kernel
     int owner = 0;
     if (NS > 1) {
       const double mine[kXRec] = {S.xtot, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
-      if (!exchange<NW>(S, mine, rec, NS, s, xr++)) return give_up();
+      if (!exchange<NW>(S, mine, rec, NS, s, xr++, spin)) return give_up();
       double grand = 0.0;
       for (int t = 0; t < NS; ++t) grand += S.xr[t][0];
       target = (double)u * grand;
@@ -879,7 +882,13 @@ __global__ __launch_bounds__(NTH, NTH == kThreadsSliced ? 2 : 1) void mss_kernel
   }
 }
 
+// Polls of one exchange word before a slice gives up (the host may lower it to
+// exercise the give-up path; 0 makes every slice give up at its first exchange).
+std::atomic<int> g_spin{kSpinMax};
+
 }  // namespace
+
+int mss_set_poll_limit(int polls) { return g_spin.exchange(polls); }
 
 // Workspace: two fp32 residual rows per sequence, the precomputed row statistics,
 // and for the sliced walk two slots of exchange records (kMaxNS slices) per
@@ -941,26 +950,27 @@ hipError_t launch_mss(int B, int n, int V, int bf16, int mode, const void* logit
   uint64_t* xrec = (uint64_t*)base;
   const int ns = (!pc && status != nullptr && (mode == 0 || mode == 3)) ? mss_slices(B, V, bf16) : 1;
   if (ns > 1) {
+    const int spin = g_spin.load();
     const size_t words = (size_t)B * 2 * kMaxNS * kXW;
     hipLaunchKernelGGL(mss_clear_kernel, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, s, B, xrec, status);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (bf16)
       hipLaunchKernelGGL((mss_kernel<true, kThreadsSliced>), dim3(B * ns), dim3(kThreadsSliced), 0, s, n, V, vec,
-                         logits, ssm, tokens, parent, u_acc, u_smp, ws, vpad, nullptr, ns, xrec, path, plen,
+                         logits, ssm, tokens, parent, u_acc, u_smp, ws, vpad, nullptr, ns, xrec, spin, path, plen,
                          bonus, status);
     else
       hipLaunchKernelGGL((mss_kernel<false, kThreadsSliced>), dim3(B * ns), dim3(kThreadsSliced), 0, s, n, V, vec,
-                         logits, ssm, tokens, parent, u_acc, u_smp, ws, vpad, nullptr, ns, xrec, path, plen,
+                         logits, ssm, tokens, parent, u_acc, u_smp, ws, vpad, nullptr, ns, xrec, spin, path, plen,
                          bonus, status);
     return hipGetLastError();
   }
   if (bf16)
     hipLaunchKernelGGL((mss_kernel<true, kThreads>), dim3(B), dim3(kThreads), 0, s, n, V, vec, logits, ssm, tokens,
-                       parent, u_acc, u_smp, ws, vpad, pre, 1, nullptr, path, plen, bonus, status);
+                       parent, u_acc, u_smp, ws, vpad, pre, 1, nullptr, 0, path, plen, bonus, status);
   else
     hipLaunchKernelGGL((mss_kernel<false, kThreads>), dim3(B), dim3(kThreads), 0, s, n, V, vec, logits, ssm, tokens,
-                       parent, u_acc, u_smp, ws, vpad, pre, 1, nullptr, path, plen, bonus, status);
+                       parent, u_acc, u_smp, ws, vpad, pre, 1, nullptr, 0, path, plen, bonus, status);
   return hipGetLastError();
 }
 

@@ -79,6 +79,7 @@ hipError_t launch_commit(const tv_attn_desc* d, void* kc, void* vc, const int32_
                          const void* kt, const void* vt, const int32_t* path, const int32_t* path_len,
                          int32_t* new_len, int32_t* status, hipStream_t s);
 size_t mss_workspace_bytes(int B, int n, int V);
+int mss_set_poll_limit(int polls);  // returns the previous limit
 hipError_t launch_mss(int B, int n, int V, int bf16, int mode, const void* logits, const void* ssm,
                       const int32_t* tokens, const int32_t* parent, const float* u_acc, const float* u_smp,
                       float* ws, int32_t* path, int32_t* plen, int32_t* bonus, int32_t* status, hipStream_t s);
