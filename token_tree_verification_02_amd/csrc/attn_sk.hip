@@ -670,6 +670,10 @@ __global__ __launch_bounds__(64 * RB) void attn_sk_kernel(AttnArgs a, SkArgs k) 
 
 // Combines the pieces of items that were split between ranges, and reports bad
 // prefix lengths and block ids.  One workgroup per (item, row slice, 64 rows).
+// The kernel is a short chain of memory round trips, so each phase issues all of
+// a thread's loads before it uses any: the block ids of the status check in groups
+// of 8 per thread, then the pieces' (max, sum, scale) records and values for all of
+// the thread's rows (both pieces at once for an item split in two).
 template <bool F16>
 __global__ __launch_bounds__(256) void sk_merge_kernel(AttnArgs a, SkArgs k, int RW, int chunks) {
   const int D = a.D, rows = a.n * a.G, Hkv = a.Hkv;
@@ -687,9 +691,16 @@ __global__ __launch_bounds__(256) void sk_merge_kernel(AttnArgs a, SkArgs k, int
     if (a.paged) {
       const int L = clamp_len(Lraw, k.cap);
       const int nb = (L + TV_PAGE - 1) / TV_PAGE;
-      for (int i = tid; i < nb; i += 256) {
-        const int id = a.bt[(size_t)b * a.max_blocks + i];
-        bad |= (id < 0 || id >= a.num_blocks);
+      const int32_t* bt = a.bt + (size_t)b * a.max_blocks;
+      for (int i0 = 0; i0 < nb; i0 += 8 * 256) {
+        int id[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int i = i0 + u * 256 + tid;
+          id[u] = i < nb ? bt[i] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) bad |= (id[u] < 0 || id[u] >= a.num_blocks);
       }
     }
     bad = __syncthreads_or(bad);
@@ -703,46 +714,94 @@ __global__ __launch_bounds__(256) void sk_merge_kernel(AttnArgs a, SkArgs k, int
   const int ws = s0 / per, we = (e0 - 1) / per;
   if (ws == we || T == 0) return;  // one range held the whole item and wrote it
 
-  const int tpr = D / 4;  // threads per row (4 values each)
+  // thread layout: tpr threads per row (4 values each), rpp rows side by side, so a
+  // thread owns rows r0, r0 + rpp, ... of the 64 (8 of them for D = 128, 4 for 64)
+  constexpr int NRM = 8;
+  const int tpr = D / 4;
   const int rpp = 256 / tpr;
-  for (int rr = tid / tpr; rr < 64; rr += rpp) {
-    const int rloc = ch * 64 + rr;  // row within the slice
-    const int row = rs * RW + rloc;
-    if (rloc >= RW || row >= rows) continue;
-    const int d0 = (tid % tpr) * 4;
-    float M = -INFINITY;
-    for (int w = ws; w <= we; ++w) {
-      const int slot = (s0 <= (long long)w * per) ? 2 * w : 2 * w + 1;
-      const size_t pi = ((size_t)slot * k.rsplit + rs) * RW + rloc;
-      M = fmaxf(M, k.pml[4 * pi]);
+  const int nr = 64 / rpp;
+  const int r0 = tid / tpr, d0 = (tid % tpr) * 4;
+  auto piece = [&](int w, int j) -> size_t {  // index of this row's piece in range w's slot
+    const int slot = (s0 <= (long long)w * per) ? 2 * w : 2 * w + 1;
+    return ((size_t)slot * k.rsplit + rs) * RW + (ch * 64 + r0 + j * rpp);
+  };
+  float M[NRM];
+  float4 acc[NRM];
+  float lt[NRM];
+#pragma unroll
+  for (int j = 0; j < NRM; ++j) M[j] = -INFINITY, acc[j] = make_float4(0.f, 0.f, 0.f, 0.f), lt[j] = 0.f;
+  auto add = [&](int j, const float4& mls, const uint2& oc) {  // one piece into row j
+    if (mls.x == -INFINITY) return;                             // no attended key in this piece
+    const float wl = exp2f(mls.x - M[j]) * mls.y;
+    const float wo = wl * mls.z;
+    acc[j].x += wo * f16_to_f32((uint16_t)oc.x);
+    acc[j].y += wo * f16_to_f32((uint16_t)(oc.x >> 16));
+    acc[j].z += wo * f16_to_f32((uint16_t)oc.y);
+    acc[j].w += wo * f16_to_f32((uint16_t)(oc.y >> 16));
+    lt[j] += wl;
+  };
+  if (we == ws + 1) {
+    // two pieces (the usual split): both pieces' records and values for all rows in
+    // one round of loads
+    float4 ma[NRM], mb[NRM];  // max, sum, scale
+    uint2 oa[NRM], ob[NRM];
+#pragma unroll
+    for (int j = 0; j < NRM; ++j) {
+      if (j < nr) {
+        const size_t pa = piece(ws, j), pb = piece(we, j);
+        ma[j] = *(const float4*)(k.pml + 4 * pa);
+        mb[j] = *(const float4*)(k.pml + 4 * pb);
+        oa[j] = *(const uint2*)(k.po + pa * D + d0);
+        ob[j] = *(const uint2*)(k.po + pb * D + d0);
+      }
     }
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    float lt = 0.f;
-    for (int w = ws; w <= we; ++w) {
-      const int slot = (s0 <= (long long)w * per) ? 2 * w : 2 * w + 1;
-      const size_t pi = ((size_t)slot * k.rsplit + rs) * RW + rloc;
-      const float4 mls = *(const float4*)(k.pml + 4 * pi);  // max, sum, scale
-      if (mls.x == -INFINITY) continue;  // no attended key in this piece
-      const float wl = exp2f(mls.x - M) * mls.y;
-      const float wo = wl * mls.z;
-      const uint2 oc = *(const uint2*)(k.po + pi * D + d0);
-      acc.x += wo * f16_to_f32((uint16_t)oc.x);
-      acc.y += wo * f16_to_f32((uint16_t)(oc.x >> 16));
-      acc.z += wo * f16_to_f32((uint16_t)oc.y);
-      acc.w += wo * f16_to_f32((uint16_t)(oc.y >> 16));
-      lt += wl;
+#pragma unroll
+    for (int j = 0; j < NRM; ++j) {
+      if (j < nr) {
+        M[j] = fmaxf(fmaxf(M[j], ma[j].x), mb[j].x);
+        add(j, ma[j], oa[j]);
+        add(j, mb[j], ob[j]);
+      }
     }
-    const float inv = 1.f / lt;
+  } else {
+    // an item over three or more ranges: the maxima of one piece for all rows, then
+    // one piece's records and values for all rows, piece by piece
+    for (int w = ws; w <= we; ++w) {
+      float mx[NRM];
+#pragma unroll
+      for (int j = 0; j < NRM; ++j) mx[j] = j < nr ? k.pml[4 * piece(w, j)] : -INFINITY;
+#pragma unroll
+      for (int j = 0; j < NRM; ++j) M[j] = fmaxf(M[j], mx[j]);
+    }
+    for (int w = ws; w <= we; ++w) {
+      float4 mls[NRM];
+      uint2 oc[NRM];
+#pragma unroll
+      for (int j = 0; j < NRM; ++j) {
+        if (j < nr) {
+          const size_t pi = piece(w, j);
+          mls[j] = *(const float4*)(k.pml + 4 * pi);
+          oc[j] = *(const uint2*)(k.po + pi * D + d0);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < NRM; ++j)
+        if (j < nr) add(j, mls[j], oc[j]);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NRM; ++j) {
+    const int row = rs * RW + ch * 64 + r0 + j * rpp;
+    if (j >= nr || row >= rows) continue;
+    const float inv = 1.f / lt[j];
     const int u = row / a.G, gi = row % a.G, h = g * a.G + gi;
     const size_t oi = ((size_t)(b * a.n + u) * a.Hq + h) * D + d0;
-    {
-      using E = Elt<F16>;
-      uint2 wv;
-      wv.x = E::bits(acc.x * inv) | (E::bits(acc.y * inv) << 16);
-      wv.y = E::bits(acc.z * inv) | (E::bits(acc.w * inv) << 16);
-      *(uint2*)((uint16_t*)a.out + oi) = wv;
-    }
-    if (a.lse != nullptr && d0 == 0) a.lse[(size_t)(b * a.n + u) * a.Hq + h] = (M + log2f(lt)) * kLn2;
+    using E = Elt<F16>;
+    uint2 wv;
+    wv.x = E::bits(acc[j].x * inv) | (E::bits(acc[j].y * inv) << 16);
+    wv.y = E::bits(acc[j].z * inv) | (E::bits(acc[j].w * inv) << 16);
+    *(uint2*)((uint16_t*)a.out + oi) = wv;
+    if (a.lse != nullptr && d0 == 0) a.lse[(size_t)(b * a.n + u) * a.Hq + h] = (M[j] + log2f(lt[j])) * kLn2;
   }
 }
 
