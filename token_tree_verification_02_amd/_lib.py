@@ -225,7 +225,8 @@ def tree_verify_stochastic(logits, ssm_logits, tokens, parent, u_accept, u_sampl
     """Stochastic (multi-step speculative sampling) verification.  logits, ssm_logits
     [B][n][V]; tokens, parent [B][n] int32; u_accept, u_sample [B][n] float32 uniforms;
     mode 0 auto, 1 walk reads only visited rows, 2 all row statistics first, 3 mode 1 with each
-    sequence's walk spread over several workgroups (vocabulary slices).
+    sequence's walk spread over several workgroups (vocabulary slices); mode 2 slices its walk
+    the same way.
     Returns (path [B][n], path_len [B], bonus [B], status [B]) int32."""
     B, n, V = logits.shape
     dev = logits.device

@@ -948,7 +948,9 @@ hipError_t launch_mss(int B, int n, int V, int bf16, int mode, const void* logit
   }
   base += ((size_t)B * n * 2 * sizeof(StatRec) + 255) & ~(size_t)255;
   uint64_t* xrec = (uint64_t*)base;
-  const int ns = (!pc && status != nullptr && (mode == 0 || mode == 3)) ? mss_slices(B, V, bf16) : 1;
+  // modes 0, 2 and 3 spread each walk over vocabulary slices (with precomputed
+  // statistics the slices exchange only at residual passes and the draw)
+  const int ns = (status != nullptr && mode != 1) ? mss_slices(B, V, bf16) : 1;
   if (ns > 1) {
     const int spin = g_spin.load();
     const size_t words = (size_t)B * 2 * kMaxNS * kXW;
@@ -957,11 +959,11 @@ hipError_t launch_mss(int B, int n, int V, int bf16, int mode, const void* logit
     if (e != hipSuccess) return e;
     if (bf16)
       hipLaunchKernelGGL((mss_kernel<true, kThreadsSliced>), dim3(B * ns), dim3(kThreadsSliced), 0, s, n, V, vec,
-                         logits, ssm, tokens, parent, u_acc, u_smp, ws, vpad, nullptr, ns, xrec, spin, path, plen,
+                         logits, ssm, tokens, parent, u_acc, u_smp, ws, vpad, pre, ns, xrec, spin, path, plen,
                          bonus, status);
     else
       hipLaunchKernelGGL((mss_kernel<false, kThreadsSliced>), dim3(B * ns), dim3(kThreadsSliced), 0, s, n, V, vec,
-                         logits, ssm, tokens, parent, u_acc, u_smp, ws, vpad, nullptr, ns, xrec, spin, path, plen,
+                         logits, ssm, tokens, parent, u_acc, u_smp, ws, vpad, pre, ns, xrec, spin, path, plen,
                          bonus, status);
     return hipGetLastError();
   }
