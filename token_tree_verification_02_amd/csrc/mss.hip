@@ -368,19 +368,23 @@ __global__ __launch_bounds__(256) void row_stats_kernel(int n, int V, int vec, c
   const int nch = (V + kC - 1) / kC, nfull = vec ? V / kC : 0;
   Stat st;
   int c = 0;
+  // full chunks in groups of kG, every load of a group in flight before any is
+  // used; a last, partial group loads in-range chunks in the missing places and
+  // skips them, so a row is a few rounds of loads, not one per chunk
   constexpr int kG = BF16 ? 8 : 4;
-  for (; c + kG <= nfull; c += kG) {
+  for (; c < nfull; c += kG) {
     Raw<BF16> q[kG];
 #pragma unroll
-    for (int u = 0; u < kG; ++u) q[u].load(row, (c + u) * kC + tid * kEPT);
+    for (int u = 0; u < kG; ++u) q[u].load(row, min(c + u, nfull - 1) * kC + tid * kEPT);
 #pragma unroll
     for (int u = 0; u < kG; ++u) {
+      if (c + u >= nfull) break;
       float v[kEPT];
       q[u].unpack(v);
       stat_add8(st, v);
     }
   }
-  for (; c < nch; ++c) {
+  for (c = nfull; c < nch; ++c) {
     float v[kEPT];
     load8<BF16>(row, c * kC + tid * kEPT, V, vec, v);
     stat_add8(st, v);
