@@ -280,14 +280,15 @@ def main():
     # on the SSM rows) and a merge of 8 drafts of 8 tokens per sequence
     cons_out = None
     if mss is not None:
-        Fx, kx = min(4, cfg.n), 4
+        Fx, kx = min(4, cfg.n - 1), 4
         nmx = cfg.n + Fx * kx
         pad = lambda a: np.pad(a, ((0, 0), (0, nmx - cfg.n)), constant_values=-1).astype(np.int32)
         ex_par = torch.from_numpy(pad(w["parent"])).cuda()
         ex_dep = torch.from_numpy(pad(w["depth"])).cuda()
         ex_tok = torch.from_numpy(pad(w["tokens"])).cuda()
-        ex_rows = mss[0]["ssm"][:, :Fx].contiguous()
-        ex_front = torch.arange(Fx, dtype=torch.int32, device="cuda").repeat(cfg.B, 1).contiguous()
+        # frontier nodes 1..Fx and their SSM rows (the root's SSM row is a constant placeholder)
+        ex_rows = mss[0]["ssm"][:, 1:1 + Fx].contiguous()
+        ex_front = torch.arange(1, 1 + Fx, dtype=torch.int32, device="cuda").repeat(cfg.B, 1).contiguous()
         ex_ncur = torch.full((cfg.B,), cfg.n, dtype=torch.int32, device="cuda")
         ex_nout = torch.empty(cfg.B, dtype=torch.int32, device="cuda")
         ex_st = torch.empty(cfg.B, dtype=torch.int32, device="cuda")

@@ -83,6 +83,25 @@ def test_expand_parity(V, dtype, k, ties):
     log(f"  appended {list(r[4] - n_cur)}")
 
 
+@pytest.mark.parametrize("V,dtype,k", [(128000, "bf16", 4), (32000, "bf16", 16), (1000, "f32", 7)])
+def test_expand_constant_rows(V, dtype, k):
+    """Rows whose entries tie at the row maximum: the top k are then the lowest
+    indices.  Per sequence, two frontier rows are constant (0 and -1.5), one is 0
+    but for three larger entries at its end, one is 0 with 0.5 at every 97th entry."""
+    log(f"case expand constant rows V={V} {dtype} k={k}")
+    B, F, n_max = 4, 4, 128
+    n_cur = np.full(B, 8, np.int32)
+    parent, depth, tokens = start_trees(B, n_cur, n_max, seed=5)
+    frontier = np.tile(np.arange(1, F + 1, dtype=np.int32), (B, 1))
+    x = np.zeros((B, F, V), np.float32)
+    x[:, 1] = -1.5
+    x[:, 2, V - 3:] = 2.0                                 # three winners at the end, then ties at 0
+    x[:, 3, ::97] = 0.5
+    st = W.f32_to_bf16_bits(x) if dtype == "bf16" else x
+    r = check_expand(st, dtype, frontier, n_cur, parent, depth, tokens, k, n_max)
+    log(f"  appended {list(r[4] - n_cur)}")
+
+
 def test_expand_rejections_leave_trees_unchanged():
     log("case expand rejections")
     B, F, V, k, n_max = 4, 4, 500, 3, 40

@@ -175,7 +175,10 @@ __global__ __launch_bounds__(256) void topk_kernel(int F, int V, int k, int n_ma
                   fmaxf(fmaxf(bf16lo(q[2]), bf16hi(q[2])), fmaxf(bf16lo(q[3]), bf16hi(q[3]))));
       else
         m = fmaxf(fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1])), fmaxf(__uint_as_float(q[2]), __uint_as_float(q[3])));
-      if (vi < nv && m >= thr) {
+      // a full list takes only values above its last entry (an equal value comes
+      // with a larger index, so it ranks after it): such vectors are skipped whole
+      const bool full = li[kKeep - 1] != INT_MAX;
+      if (vi < nv && (full ? m > lv[kKeep - 1] : m >= thr)) {
 #pragma unroll
         for (int e = 0; e < EPV; ++e) {
           const float x = BF16 ? ((e & 1) ? bf16hi(q[e >> 1]) : bf16lo(q[e >> 1])) : __uint_as_float(q[e]);
