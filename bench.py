@@ -273,7 +273,7 @@ def main():
         if pre:   # every LLM row and every non-root SSM row, then the walk's residual and draw passes
             rows_all = cfg.B * (2 * cfg.n - 1)
         mss_out = {"us": round(t_mss * 1e6, 2), "mean_path_len": round(float(plen_h.mean()), 3),
-                   "mode": "all-row statistics" if pre else "visited rows, vocabulary slices per sequence",
+                   "mode": "all-row statistics, walk over vocabulary slices" if pre else "visited rows, walk over vocabulary slices",
                    "rows_read": rows_all if pre else rows,
                    "hbm_gbs": round((rows_all if pre else rows) * cfg.vocab * es_l / t_mss / 1e9, 1)}
     # tree construction: one expansion step (4 frontier nodes per sequence, k = 4,
