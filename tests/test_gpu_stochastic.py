@@ -171,6 +171,34 @@ def test_sliced_walk_give_up_path():
     assert (got[3] == 0).all()
 
 
+@pytest.mark.parametrize("mode", [0, 1, 2, 3])
+def test_stochastic_without_status(mode):
+    """status may be NULL: the walk then runs one workgroup per sequence in every
+    mode (the sliced walk needs it), with the same outputs as a call that passes it."""
+    cfg, noise = CASES["llama_v32000"]
+    log(f"case stochastic without status mode {mode}")
+    w = W.make_stochastic(cfg, seed=31, ssm_noise=noise)
+    bf = cfg.dtype == "bf16"
+    ref = run_gpu(w, 1)
+    B, n, V = cfg.B, cfg.n, cfg.vocab
+    args = [dev(w["logits"], bf), dev(w["ssm_logits"], bf), dev(w["tokens"], False), dev(w["parent"], False),
+            dev(w["u_accept"], False), dev(w["u_sample"], False)]
+    path = torch.full((B, n), -7, dtype=torch.int32, device="cuda")
+    plen = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+    bonus = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+    wsb = _lib.stochastic_workspace_size(B, n, V)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    rc = _lib.load().tree_verify_stochastic(B, n, V, _lib.TV_BF16 if bf else _lib.TV_F32, mode,
+                                            *[a.data_ptr() for a in args], path.data_ptr(), plen.data_ptr(),
+                                            bonus.data_ptr(), None, ws.data_ptr(), wsb,
+                                            torch.cuda.current_stream().cuda_stream)
+    assert rc == _lib.TV_OK
+    torch.cuda.synchronize()
+    for a, b_, what in zip(ref[:3], (path.cpu().numpy(), plen.cpu().numpy(), bonus.cpu().numpy()),
+                           ("path", "path_len", "bonus")):
+        np.testing.assert_array_equal(a, b_, err_msg=what)
+
+
 def test_gpu_emits_the_llm_distribution():
     """The pages' guarantee, on the GPU: 20000 verification steps of one small
     tree with fresh draft tokens and uniforms; the first emitted token follows
