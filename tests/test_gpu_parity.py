@@ -21,7 +21,7 @@ import pytest
 import torch
 
 import oracle
-from token_tree_verification_02_amd import runner
+from token_tree_verification_02_amd import _lib, runner
 from token_tree_verification_02_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
@@ -259,6 +259,25 @@ def test_deterministic():
     runner.step(d)
     torch.cuda.synchronize()
     assert torch.equal(o1, d["out"]) and torch.equal(l1, d["lse"])
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "llama_L1000", "merge_L2900_split", "paged_ragged_split",
+                                  "d64_f16_chunks", "llama_fp8"])
+def test_attention_without_lse_and_status(name):
+    """lse and status may be NULL: every plan (fp32 with chunk merge, few-row,
+    many-row with split items, chunked prefixes, fp8 cache) writes the same
+    output bits as the call that passes both."""
+    log(f"case attention without lse/status {name}")
+    w = W.make(SMALL[name], seed=13)
+    d = run(w)
+    ref = d["out"].clone()
+    d["out"].zero_()
+    _lib.tree_attention(d["q"], d["k_cache"], d["v_cache"], d["prefix_len"], d["k_tree"], d["v_tree"], d["mask"],
+                        block_table=d["block_table"], num_blocks=d["num_blocks"], out=d["out"], lse=None,
+                        want_lse=False, status=None, workspace=d["workspace"], k_scale=d["k_scale"],
+                        v_scale=d["v_scale"])
+    torch.cuda.synchronize()
+    assert torch.equal(ref, d["out"])
 
 
 # ----------------------------------------------------------------------------- full sizes
