@@ -6,6 +6,7 @@ must match exactly.  Paths are chosen on the host from the tree (root paths to
 random nodes, the whole chain, empty) or come from the oracle's greedy
 verification, never from the GPU.
 """
+import ctypes
 import sys
 
 import numpy as np
@@ -13,7 +14,7 @@ import pytest
 import torch
 
 import oracle
-from token_tree_verification_02_amd import runner
+from token_tree_verification_02_amd import _lib, runner
 from token_tree_verification_02_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
@@ -180,3 +181,31 @@ def test_commit_full_size(index):
     path, plen = random_paths(w, np.random.default_rng(index))
     log("  running")
     commit_and_check(w, path, plen)
+
+
+def test_commit_without_status():
+    """status may be NULL: the cache and the new lengths are those of the call that
+    passes it, a rejected sequence (path length past n) included."""
+    cfg = CASES["paged_ragged"]
+    log("case commit without status")
+    w = W.make(cfg, seed=41, room=cfg.n)
+    path, plen = random_paths(w, np.random.default_rng(3))
+    plen[1] = cfg.n + 1
+    ref = commit_and_check(w, path, plen)
+    d = runner.upload(w)
+    kt = d["k_tree"]
+    B, n, Hkv, D = kt.shape
+    desc = _lib.attn_desc(B, n, Hkv, Hkv, D, _lib._dtype_code(kt), paged=True, max_blocks=d["block_table"].shape[1],
+                          num_blocks=d["num_blocks"])
+    pt = torch.from_numpy(path).cuda()
+    lt = torch.from_numpy(plen).cuda()
+    nl = torch.full((B,), -9, dtype=torch.int32, device="cuda")
+    rc = _lib.load().tree_commit_kv(ctypes.byref(desc), d["k_cache"].data_ptr(), d["v_cache"].data_ptr(),
+                                    d["block_table"].data_ptr(), d["prefix_len"].data_ptr(), kt.data_ptr(),
+                                    d["v_tree"].data_ptr(), pt.data_ptr(), lt.data_ptr(), nl.data_ptr(), None,
+                                    torch.cuda.current_stream().cuda_stream)
+    assert rc == _lib.TV_OK
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(nl.cpu().numpy(), ref["new_len"].cpu().numpy())
+    assert np.array_equal(raw(d["k_cache"]), raw(ref["k_cache"])) and np.array_equal(raw(d["v_cache"]),
+                                                                                     raw(ref["v_cache"]))

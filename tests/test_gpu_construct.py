@@ -170,3 +170,42 @@ def test_merge_figure_overflow_and_bad_lengths():
     assert list(r[3]) == [9, 9, 0, 0]
     r = check_merge(drafts[:1], lens[:1], np.zeros(1, np.int32), 8)    # one node too many
     assert r[5][0] == 1
+
+
+def test_optional_outputs_may_be_null():
+    """scores (expansion), root_token and node_of (merge) may be NULL: the other
+    outputs are those of the call that passes them, and a NULL root token is 0."""
+    log("case construction with NULL optional arguments")
+    lib = _lib.load()
+    sh = torch.cuda.current_stream().cuda_stream
+    B, F, V, k, n_max = 4, 3, 5000, 4, 64
+    rng = np.random.default_rng(77)
+    n_cur = np.full(B, 6, np.int32)
+    parent, depth, tokens = start_trees(B, n_cur, n_max, seed=77)
+    frontier = np.tile(np.array([1, -1, 4], np.int32), (B, 1))
+    x = W.f32_to_bf16_bits(rng.normal(0, 2, size=(B, F, V)).astype(np.float32))
+    ref = run_expand(x, "bf16", frontier, n_cur, parent, depth, tokens, k)
+    P, D, T = dev(parent), dev(depth), dev(tokens)
+    n_out, st = dev(np.zeros(B, np.int32)), dev(np.zeros(B, np.int32))
+    lg, fr, nc = dev(x, True), dev(frontier), dev(n_cur)
+    assert lib.tree_expand_topk(B, F, V, k, n_max, _lib.TV_BF16, lg.data_ptr(), fr.data_ptr(), nc.data_ptr(),
+                                P.data_ptr(), D.data_ptr(), T.data_ptr(), None, n_out.data_ptr(), st.data_ptr(),
+                                sh) == _lib.TV_OK
+    torch.cuda.synchronize()
+    for name, a, e in zip(("parent", "depth", "tokens"), (P, D, T), ref[:3]):
+        np.testing.assert_array_equal(a.cpu().numpy(), e, err_msg=name)
+    np.testing.assert_array_equal(n_out.cpu().numpy(), ref[4])
+    np.testing.assert_array_equal(st.cpu().numpy(), ref[5])
+
+    M, Ld = 5, 7
+    drafts = rng.integers(0, 3, size=(B, M, Ld)).astype(np.int32)
+    lens = rng.integers(0, Ld + 1, size=(B, M)).astype(np.int32)
+    r = oracle.merge_drafts(drafts, lens, np.zeros(B, np.int32), n_max)
+    outs = [dev(np.full((B, n_max), -9, np.int32)) for _ in range(3)] + [dev(np.zeros(B, np.int32)) for _ in range(2)]
+    dr, ln = dev(drafts), dev(lens)
+    assert lib.tree_merge_drafts(B, M, Ld, n_max, dr.data_ptr(), ln.data_ptr(), None, outs[0].data_ptr(),
+                                 outs[1].data_ptr(), outs[2].data_ptr(), outs[3].data_ptr(), None,
+                                 outs[4].data_ptr(), sh) == _lib.TV_OK
+    torch.cuda.synchronize()
+    for name, a, e in zip(("parent", "depth", "tokens", "n", "status"), outs, (r[0], r[1], r[2], r[3], r[5])):
+        np.testing.assert_array_equal(a.cpu().numpy(), e, err_msg=name)
