@@ -280,6 +280,43 @@ def test_attention_without_lse_and_status(name):
     assert torch.equal(ref, d["out"])
 
 
+def random_shapes(count, seed):
+    """Seeded small descriptors across the plans: element type, head dim, GQA group,
+    KV heads, tree shape and size (so both the few-row and the many-row kernels),
+    batch, ragged prefix lengths, paged or contiguous caches, and fp8 caches where
+    they are offered (bf16, at most 128 query rows per KV head)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(count):
+        dtype = str(rng.choice(["bf16", "f16", "f32"], p=[0.5, 0.3, 0.2]))
+        D = int(rng.choice([64, 128]))
+        Hkv = int(rng.choice([1, 2, 4]))
+        G = int(rng.choice([1, 2, 4, 8]))
+        tree = str(rng.choice(["random", "frontier", "chain"]))
+        n = int(rng.integers(2 if tree == "frontier" else 1, 97))
+        lo, hi = sorted(int(x) for x in rng.integers(0, 2500, 2))
+        paged = bool(rng.random() < 0.5)
+        kv = "fp8" if dtype == "bf16" and n * G <= 128 and rng.random() < 0.3 else ""
+        out.append(W.config(4 if paged else 3, B=int(rng.integers(1, 4)), Hq=G * Hkv, Hkv=Hkv, D=D, dtype=dtype,
+                            L_lo=lo, L_hi=hi, paged=paged, tree=tree, n=n, max_depth=int(rng.integers(1, 16)),
+                            vocab=0, Lmax=0 if paged else hi + int(rng.integers(0, 40)), kv=kv))
+    return out
+
+
+RANDOM_SHAPES = random_shapes(48, 2024)
+
+
+@pytest.mark.parametrize("i", range(len(RANDOM_SHAPES)))
+def test_random_shapes(i):
+    cfg = RANDOM_SHAPES[i]
+    log(f"case random shape {i}: {cfg.dtype}{'/fp8' if cfg.kv else ''} D={cfg.D} Hq/Hkv={cfg.Hq}/{cfg.Hkv} "
+        f"{cfg.tree} n={cfg.n} B={cfg.B} L={cfg.L_lo}..{cfg.L_hi} {'paged' if cfg.paged else 'contiguous'}")
+    w = W.make(cfg, seed=100 + i)
+    d = run(w)
+    check_build(w, d)
+    check_attention(w, d)
+
+
 # ----------------------------------------------------------------------------- full sizes
 @pytest.mark.slow
 @pytest.mark.parametrize("index", [2, 3, 4, 5])
