@@ -298,7 +298,7 @@ def random_shapes(count, seed):
         paged = bool(rng.random() < 0.5)
         kv = "fp8" if dtype == "bf16" and n * G <= 128 and rng.random() < 0.3 else ""
         out.append(W.config(4 if paged else 3, B=int(rng.integers(1, 4)), Hq=G * Hkv, Hkv=Hkv, D=D, dtype=dtype,
-                            L_lo=lo, L_hi=hi, paged=paged, tree=tree, n=n, max_depth=int(rng.integers(1, 16)),
+                            L_lo=lo, L_hi=hi, paged=paged, tree=tree, n=n, max_depth=int(rng.integers(8 if tree == "frontier" else 1, 16)),
                             vocab=0, Lmax=0 if paged else hi + int(rng.integers(0, 40)), kv=kv))
     return out
 
@@ -315,6 +315,35 @@ def test_random_shapes(i):
     d = run(w)
     check_build(w, d)
     check_attention(w, d)
+
+
+def random_verify_shapes(count, seed):
+    """Seeded greedy-verification cases: vocabulary sizes (odd, tiny, large), element
+    types, tree shapes and sizes up to 256 nodes; short prefixes (attention is
+    checked too, but the point is the argmax and the walk)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(count):
+        dtype = str(rng.choice(["bf16", "f16", "f32"]))
+        tree = str(rng.choice(["random", "frontier", "chain"]))
+        n = int(rng.integers(2 if tree == "frontier" else 1, 257))
+        V = int(rng.choice([int(rng.integers(1, 64)), int(rng.integers(64, 5000)), int(rng.integers(5000, 140000))]))
+        out.append(W.config(2, B=int(rng.integers(1, 5)), Hq=4, Hkv=4, D=64, dtype=dtype, L_lo=1, L_hi=40,
+                            tree=tree, n=n, max_depth=int(rng.integers(8 if tree == "frontier" else 1, 20)), vocab=V, Lmax=48))
+    return out
+
+
+RANDOM_VERIFY = random_verify_shapes(24, 77)
+
+
+@pytest.mark.parametrize("i", range(len(RANDOM_VERIFY)))
+def test_random_verify_shapes(i):
+    cfg = RANDOM_VERIFY[i]
+    log(f"case random verify {i}: {cfg.dtype} V={cfg.vocab} {cfg.tree} n={cfg.n} B={cfg.B}")
+    w = W.make(cfg, seed=300 + i)
+    d = run(w)
+    check_build(w, d)
+    check_verify(w, d)
 
 
 # ----------------------------------------------------------------------------- full sizes

@@ -199,6 +199,36 @@ def test_stochastic_without_status(mode):
         np.testing.assert_array_equal(a, b_, err_msg=what)
 
 
+def random_stochastic_shapes(count, seed):
+    """Seeded stochastic-verification cases: vocabulary sizes (odd, tiny, large),
+    bf16 or fp32 logits, tree shapes and sizes up to 256 nodes, low and normal
+    acceptance."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(count):
+        dtype = str(rng.choice(["bf16", "f32"]))
+        tree = str(rng.choice(["random", "frontier", "chain"]))
+        n = int(rng.integers(2 if tree == "frontier" else 1, 257))
+        V = int(rng.choice([int(rng.integers(1, 64)), int(rng.integers(64, 5000)), int(rng.integers(5000, 140000))]))
+        cfg = W.config(2, B=int(rng.integers(1, 7)), Hq=4, Hkv=4, D=64, dtype=dtype, L_lo=1, L_hi=16, tree=tree,
+                       n=n, max_depth=int(rng.integers(8 if tree == "frontier" else 1, 20)), vocab=V, Lmax=16)
+        out.append((cfg, float(rng.choice([1.0, 4.0]))))
+    return out
+
+
+RANDOM_STOCHASTIC = random_stochastic_shapes(16, 99)
+
+
+@pytest.mark.parametrize("mode", [0, 1, 3])
+@pytest.mark.parametrize("i", range(len(RANDOM_STOCHASTIC)))
+def test_random_stochastic_shapes(i, mode):
+    cfg, noise = RANDOM_STOCHASTIC[i]
+    log(f"case random stochastic {i} mode {mode}: {cfg.dtype} V={cfg.vocab} {cfg.tree} n={cfg.n} B={cfg.B} "
+        f"noise {noise}")
+    w = W.make_stochastic(cfg, seed=500 + i, ssm_noise=noise)
+    check(w, max_close_frac=0.34, mode=mode)
+
+
 def test_gpu_emits_the_llm_distribution():
     """The pages' guarantee, on the GPU: 20000 verification steps of one small
     tree with fresh draft tokens and uniforms; the first emitted token follows

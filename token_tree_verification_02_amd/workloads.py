@@ -256,8 +256,10 @@ def frontier_tree(rng: np.random.Generator, n: int, max_depth: int, bmin: int = 
     """Repeatedly give a random childless node of depth < max_depth U{bmin..bmax} children.
 
     Nodes are numbered in creation order (a valid topological order that is not BFS).
+    A draw whose frontier runs out before n nodes is redrawn; if 1000 draws all
+    fall short (n out of reach at this depth), ValueError.
     """
-    while True:
+    for _ in range(1000):
         parent, depth, nchild = [-1], [0], [0]
         while len(parent) < n:
             front = [v for v in range(len(parent)) if nchild[v] == 0 and depth[v] < max_depth]
@@ -273,6 +275,7 @@ def frontier_tree(rng: np.random.Generator, n: int, max_depth: int, bmin: int = 
                 nchild[p] += 1
         if len(parent) == n:
             return np.array(parent, np.int32)
+    raise ValueError(f"frontier tree: {n} nodes not reached within depth {max_depth} in 1000 draws")
 
 
 def depths_of(parent: np.ndarray) -> np.ndarray:
