@@ -209,3 +209,33 @@ def test_commit_without_status():
     np.testing.assert_array_equal(nl.cpu().numpy(), ref["new_len"].cpu().numpy())
     assert np.array_equal(raw(d["k_cache"]), raw(ref["k_cache"])) and np.array_equal(raw(d["v_cache"]),
                                                                                      raw(ref["v_cache"]))
+
+
+def random_commit_shapes(count, seed):
+    """Seeded commit cases: element types, head dims, KV heads, paged or contiguous
+    caches, ragged prefixes (empty ones included), tree sizes up to 256."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(count):
+        dtype = str(rng.choice(["bf16", "f16", "f32"]))
+        paged = bool(rng.random() < 0.6)
+        n = int(rng.integers(1, 257))
+        lo, hi = sorted(int(x) for x in rng.integers(0, 700, 2))
+        out.append(W.config(4 if paged else 3, B=int(rng.integers(1, 6)), Hq=4, Hkv=int(rng.choice([1, 2, 4])),
+                            D=int(rng.choice([64, 128])), dtype=dtype, L_lo=lo, L_hi=hi, paged=paged,
+                            tree="random", n=n, max_depth=int(rng.integers(1, 30)), vocab=0,
+                            Lmax=0 if paged else hi + n))
+    return out
+
+
+RANDOM_COMMIT = random_commit_shapes(16, 55)
+
+
+@pytest.mark.parametrize("i", range(len(RANDOM_COMMIT)))
+def test_random_commit_shapes(i):
+    cfg = RANDOM_COMMIT[i]
+    log(f"case random commit {i}: {cfg.dtype} D={cfg.D} Hkv={cfg.Hkv} n={cfg.n} B={cfg.B} "
+        f"L={cfg.L_lo}..{cfg.L_hi} {'paged' if cfg.paged else 'contiguous'}")
+    w = W.make(cfg, seed=700 + i, room=cfg.n)
+    path, plen = random_paths(w, np.random.default_rng(i))
+    commit_and_check(w, path, plen)

@@ -209,3 +209,26 @@ def test_optional_outputs_may_be_null():
     torch.cuda.synchronize()
     for name, a, e in zip(("parent", "depth", "tokens", "n", "status"), outs, (r[0], r[1], r[2], r[3], r[5])):
         np.testing.assert_array_equal(a.cpu().numpy(), e, err_msg=name)
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_random_expand_shapes(i):
+    """Seeded expansion cases: vocabulary size, k, frontier size, element type, and
+    how many entries tie."""
+    rng = np.random.default_rng(900 + i)
+    V = int(rng.choice([int(rng.integers(16, 300)), int(rng.integers(300, 20000)), int(rng.integers(20000, 140000))]))
+    k = int(rng.integers(1, min(16, V) + 1))
+    dtype = str(rng.choice(["bf16", "f32"]))
+    B, F, n_max = int(rng.integers(1, 5)), int(rng.integers(1, 9)), 256
+    log(f"case random expand {i}: V={V} k={k} F={F} B={B} {dtype}")
+    n_cur = rng.integers(1, 60, size=B).astype(np.int32)
+    parent, depth, tokens = start_trees(B, n_cur, n_max, seed=i)
+    frontier = np.full((B, F), -1, np.int32)
+    for b in range(B):
+        m = int(rng.integers(1, F + 1))
+        frontier[b, rng.choice(F, size=m, replace=False)] = rng.choice(n_cur[b], size=m, replace=True)
+    levels = int(rng.choice([3, 30, 0]))
+    x = (rng.integers(-levels, levels + 1, size=(B, F, V)) if levels else rng.normal(0, 2, size=(B, F, V)))
+    x = x.astype(np.float32)
+    st = W.f32_to_bf16_bits(x) if dtype == "bf16" else x
+    check_expand(st, dtype, frontier, n_cur, parent, depth, tokens, k, n_max)
