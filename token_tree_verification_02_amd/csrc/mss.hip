@@ -180,7 +180,6 @@ struct Shared {
   double segd[kMaxSeg];
   double xr[kMaxNS][kXRec];     // the slices' exchange records, in slice order
   double xtot;
-  int xok;
   int result;
 };
 
@@ -243,26 +242,35 @@ __device__ __forceinline__ void block_reduce(Shared<NW>& S, int& slot, Stat& a, 
 //   - The wait is bounded: after `spin` polls of a word (kSpinMax unless the
 //     host set another limit) the slice gives up and
 //     the caller ends the walk with an error, so every workgroup exits.
-// Wave 0 does it (lane j < 2 kXRec writes word j; every lane polls up to
-// 2 kXRec * NS / 64 words); returns false (uniformly) on a timeout.
+// The first 2 kXRec threads write the slice's record (thread j word j); then every
+// thread takes up to 2 kXRec * NS / NTH of the words (one, with 256 threads and
+// up to 16 slices), so all of them are polled at once: its own slice's words come
+// straight from registers.  Returns false (uniformly) on a timeout.
 constexpr int kXW = 2 * kXRec;  // 64-bit words per record
 template <int NW>
 __device__ __forceinline__ bool exchange(Shared<NW>& S, const double (&mine)[kXRec], uint64_t* rec, int NS, int s,
                                          int r, int spin) {
-  if (threadIdx.x < 64) {
-    const int lane = threadIdx.x;
-    uint64_t* slot = rec + (size_t)(r & 1) * NS * kXW;
-    const uint32_t tag = (uint32_t)(r + 1);
+  const int t = threadIdx.x;
+  uint64_t* slot = rec + (size_t)(r & 1) * NS * kXW;
+  const uint32_t tag = (uint32_t)(r + 1);
+  auto own_word = [&](int j) -> uint32_t {  // half (j & 1) of value j / 2 (no dynamic index into mine)
+    uint32_t h = 0;
 #pragma unroll
-    for (int i = 0; i < kXRec; ++i) {  // lanes 2i, 2i + 1: the halves of value i
+    for (int i = 0; i < kXRec; ++i) {
       const uint64_t bits = __builtin_bit_cast(uint64_t, mine[i]);
-      const uint32_t half = (lane & 1) ? (uint32_t)(bits >> 32) : (uint32_t)bits;
-      if ((lane >> 1) == i)
-        __hip_atomic_store(slot + s * kXW + lane, ((uint64_t)tag << 32) | half, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+      h = (j >> 1) == i ? ((j & 1) ? (uint32_t)(bits >> 32) : (uint32_t)bits) : h;
     }
-    int ok = 1;
-    for (int idx = lane; idx < NS * kXW; idx += 64) {
+    return h;
+  };
+  if (t < kXW)
+    __hip_atomic_store(slot + s * kXW + t, ((uint64_t)tag << 32) | own_word(t), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  int ok = 1;
+  for (int idx = t; idx < NS * kXW; idx += NW * 64) {
+    uint32_t v;
+    if (idx / kXW == s) {
+      v = own_word(idx % kXW);
+    } else {
       uint64_t w = 0;
       int it = 0;
       for (; it < spin; ++it) {
@@ -271,13 +279,11 @@ __device__ __forceinline__ bool exchange(Shared<NW>& S, const double (&mine)[kXR
         __builtin_amdgcn_s_sleep(1);
       }
       ok &= it < spin;
-      ((uint32_t*)&S.xr[0][0])[idx] = (uint32_t)w;  // word t*2*kXRec + j: half (j & 1) of value j/2 of slice t
+      v = (uint32_t)w;
     }
-    ok = __all(ok);
-    if (lane == 0) S.xok = ok;
+    ((uint32_t*)&S.xr[0][0])[idx] = v;  // word t*2*kXRec + j: half (j & 1) of value j/2 of slice t
   }
-  __syncthreads();
-  return S.xok != 0;
+  return __syncthreads_and(ok) != 0;
 }
 
 // One chunk of a residual pass: p (from raw logits via max/normaliser, or from
