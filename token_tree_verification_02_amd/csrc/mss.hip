@@ -359,15 +359,25 @@ struct StatRec {
 
 // One 256-thread workgroup per row: row r of the grid is (sequence, node, which)
 // with which 0 = the LLM row, 1 = the SSM row (node 0 has none).  Same exact
-// online statistics as the walk's own passes.
+// online statistics as the walk's own passes.  Before a sliced walk (xrec set)
+// it also does what mss_clear_kernel does, one word per thread (the grid has
+// B * n * 512 threads, the exchange area B * 512 words).
+constexpr int kXWords = 2 * kMaxNS * 2 * kXRec;  // exchange words per sequence
 template <bool BF16>
 __global__ __launch_bounds__(256) void row_stats_kernel(int n, int V, int vec, const void* __restrict__ logits,
-                                                        const void* __restrict__ ssm, StatRec* __restrict__ out) {
+                                                        const void* __restrict__ ssm, StatRec* __restrict__ out,
+                                                        int B, uint64_t* __restrict__ xrec,
+                                                        int32_t* __restrict__ status) {
   __shared__ float sR[4];
   __shared__ double sS[4];
   const int r = blockIdx.x, which = r & 1, node = (r >> 1) % n, b = (r >> 1) / n;
-  if (which == 1 && node == 0) return;
   const int tid = threadIdx.x;
+  if (xrec != nullptr) {
+    const size_t i = (size_t)r * 256 + tid;
+    if (i < (size_t)B * kXWords) xrec[i] = 0ull;
+    if (i < (size_t)B) status[i] = TV_OK;
+  }
+  if (which == 1 && node == 0) return;
   const size_t es = BF16 ? 2 : 4;
   const char* row = (const char*)(which ? ssm : logits) + ((size_t)b * n + node) * V * es;
   constexpr int kC = 256 * kEPT;  // elements per chunk of this kernel
@@ -410,7 +420,7 @@ __global__ __launch_bounds__(256) void row_stats_kernel(int n, int V, int vec, c
 __global__ __launch_bounds__(256) void mss_clear_kernel(int B, uint64_t* __restrict__ xrec,
                                                         int32_t* __restrict__ status) {
   const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (i < (size_t)B * 2 * kMaxNS * kXW) xrec[i] = 0ull;
+  if (i < (size_t)B * kXWords) xrec[i] = 0ull;
   if (i < (size_t)B) status[i] = TV_OK;
 }
 
@@ -947,26 +957,31 @@ hipError_t launch_mss(int B, int n, int V, int bf16, int mode, const void* logit
   char* base = (char*)ws + (size_t)B * 2 * vpad * sizeof(float);
   StatRec* pre = nullptr;
   const int pc = mss_precompute(B, n, V, bf16, mode);
-  if (pc) {
-    pre = (StatRec*)base;
-    if (bf16)
-      hipLaunchKernelGGL(row_stats_kernel<true>, dim3(B * n * 2), dim3(256), 0, s, n, V, vec, logits, ssm, pre);
-    else
-      hipLaunchKernelGGL(row_stats_kernel<false>, dim3(B * n * 2), dim3(256), 0, s, n, V, vec, logits, ssm, pre);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  base += ((size_t)B * n * 2 * sizeof(StatRec) + 255) & ~(size_t)255;
-  uint64_t* xrec = (uint64_t*)base;
+  uint64_t* xrec = (uint64_t*)(base + (((size_t)B * n * 2 * sizeof(StatRec) + 255) & ~(size_t)255));
   // modes 0, 2 and 3 spread each walk over vocabulary slices (with precomputed
   // statistics the slices exchange only at residual passes and the draw)
   const int ns = (status != nullptr && mode != 1) ? mss_slices(B, V, bf16) : 1;
-  if (ns > 1) {
-    const int spin = g_spin.load();
-    const size_t words = (size_t)B * 2 * kMaxNS * kXW;
-    hipLaunchKernelGGL(mss_clear_kernel, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, s, B, xrec, status);
+  if (pc) {
+    pre = (StatRec*)base;
+    uint64_t* clr = ns > 1 ? xrec : nullptr;  // the statistics pass also clears the exchange area
+    if (bf16)
+      hipLaunchKernelGGL(row_stats_kernel<true>, dim3(B * n * 2), dim3(256), 0, s, n, V, vec, logits, ssm, pre, B,
+                         clr, status);
+    else
+      hipLaunchKernelGGL(row_stats_kernel<false>, dim3(B * n * 2), dim3(256), 0, s, n, V, vec, logits, ssm, pre, B,
+                         clr, status);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+  }
+  if (ns > 1) {
+    const int spin = g_spin.load();
+    if (!pc) {
+      const size_t words = (size_t)B * kXWords;
+      hipLaunchKernelGGL(mss_clear_kernel, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, s, B, xrec,
+                         status);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
     if (bf16)
       hipLaunchKernelGGL((mss_kernel<true, kThreadsSliced>), dim3(B * ns), dim3(kThreadsSliced), 0, s, n, V, vec,
                          logits, ssm, tokens, parent, u_acc, u_smp, ws, vpad, pre, ns, xrec, spin, path, plen,
