@@ -286,6 +286,33 @@ __device__ __forceinline__ bool exchange(Shared<NW>& S, const double (&mine)[kXR
   return __syncthreads_and(ok) != 0;
 }
 
+// Combining the slices' records: lane t of every wave takes slice t's entry and a
+// butterfly of shuffles merges the (at most 16) entries; every lane then takes
+// lane 0's result, so all threads of all slices hold the same value (the same
+// data, merged in the same fixed order).  Replaces a serial loop over slices,
+// each step of which waited on an LDS read and an fp64 chain.
+template <int NW>
+__device__ __forceinline__ Stat xmerge_stat(const Shared<NW>& S, int NS, int iR, int iS) {
+  const int lane = threadIdx.x & 63;
+  Stat a;
+  if (lane < NS) a = Stat{(float)S.xr[lane][iR], S.xr[lane][iS]};
+#pragma unroll
+  for (int o = 1; o < kMaxNS; o <<= 1) {
+    const float R2 = __shfl_xor(a.R, o);
+    const double S2 = __shfl_xor(a.S, o);
+    stat_merge(a, R2, S2);
+  }
+  return Stat{__shfl(a.R, 0), __shfl(a.S, 0)};
+}
+template <int NW>
+__device__ __forceinline__ double xsum(const Shared<NW>& S, int NS, int i) {
+  const int lane = threadIdx.x & 63;
+  double x = lane < NS ? S.xr[lane][i] : 0.0;
+#pragma unroll
+  for (int o = 1; o < kMaxNS; o <<= 1) x += __shfl_xor(x, o);
+  return __shfl(x, 0);
+}
+
 // One chunk of a residual pass: p (from raw logits via max/normaliser, or from
 // the previous unnormalised residual via its sum), minus q from its logits;
 // writes r = max(0, p - q) to the output row, catches p and r at the next
@@ -582,11 +609,8 @@ __global__ __launch_bounds__(NTH, NTH == kThreadsSliced ? 2 : 1) void mss_kernel
       if (NS > 1) {
         const double mine[kXRec] = {sl.R, sl.S, sq.R, sq.S, 0.0, 0.0, 0.0, 0.0};
         if (!exchange<NW>(S, mine, rec, NS, s, xr++, spin)) return give_up();
-        sl = Stat{}, sq = Stat{};
-        for (int t = 0; t < NS; ++t) {
-          stat_merge(sl, (float)S.xr[t][0], S.xr[t][1]);
-          stat_merge(sq, (float)S.xr[t][2], S.xr[t][3]);
-        }
+        sl = xmerge_stat(S, NS, 0, 1);
+        sq = xmerge_stat(S, NS, 2, 3);
       }
     }
 
@@ -694,11 +718,15 @@ __global__ __launch_bounds__(NTH, NTH == kThreadsSliced ? 2 : 1) void mss_kernel
         const double mine[kXRec] = {sn.R, sn.S, tsum, own ? (double)capp : 0.0, own ? (double)capr : 0.0,
                                     own ? 1.0 : 0.0, 0.0, 0.0};
         if (!exchange<NW>(S, mine, rec, NS, s, xr++, spin)) return give_up();
-        sn = Stat{}, tsum = 0.0;
-        for (int t = 0; t < NS; ++t) {
-          stat_merge(sn, (float)S.xr[t][0], S.xr[t][1]);
-          tsum += S.xr[t][2];
-          if (S.xr[t][5] != 0.0) capp = (float)S.xr[t][3], capr = (float)S.xr[t][4];
+        sn = xmerge_stat(S, NS, 0, 1);
+        tsum = xsum(S, NS, 2);
+        {  // the caught values come from the one slice that owns the next child's token
+          const int lane = threadIdx.x & 63;
+          const unsigned long long ow = __ballot(lane < NS && S.xr[lane][5] != 0.0);
+          if (ow) {
+            const int t = 63 - __builtin_clzll(ow);
+            capp = (float)S.xr[t][3], capr = (float)S.xr[t][4];
+          }
         }
       }
       if (tsum > 0.0) {
