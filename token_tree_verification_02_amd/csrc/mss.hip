@@ -180,6 +180,7 @@ struct Shared {
   double segd[kMaxSeg];
   double xr[kMaxNS][kXRec];     // the slices' exchange records, in slice order
   double xtot;
+  int wok[NW];  // each wave's exchange status
   int result;
 };
 
@@ -201,6 +202,18 @@ __device__ __forceinline__ Stat wave_stat(Stat a) {
   return Stat{R, wave_sum(s)};
 }
 
+// Workgroup barrier that orders LDS accesses only.  __syncthreads also waits for
+// every outstanding global store (the residual row a pass has just written);
+// nothing after these barriers reads another wave's global stores before the
+// draw pass, whose full barrier waits for them, since a thread only reads back
+// residual values it wrote itself.  So the stores drain while the reduction
+// and the exchange go on.
+__device__ __forceinline__ void lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Workgroup-wide merge of two row statistics and one plain fp64 sum per thread.
 // Every thread ends with the same values, merged in the same order from LDS.
 // One barrier; alternating LDS slots so back-to-back calls never overwrite
@@ -215,7 +228,7 @@ __device__ __forceinline__ void block_reduce(Shared<NW>& S, int& slot, Stat& a, 
     S.rR[slot][1][w] = wb.R, S.rS[slot][1][w] = wb.S;
     S.rS[slot][2][w] = wt;
   }
-  __syncthreads();
+  lds_sync();
   a = Stat{}, b = Stat{}, t = 0.0;
   for (int k = 0; k < NW; ++k) {
     stat_merge(a, S.rR[slot][0][k], S.rS[slot][0][k]);
@@ -283,7 +296,13 @@ __device__ __forceinline__ bool exchange(Shared<NW>& S, const double (&mine)[kXR
     }
     ((uint32_t*)&S.xr[0][0])[idx] = v;  // word t*2*kXRec + j: half (j & 1) of value j/2 of slice t
   }
-  return __syncthreads_and(ok) != 0;
+  ok = __all(ok);
+  if ((t & 63) == 0) S.wok[t >> 6] = ok;
+  lds_sync();
+  int all = 1;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) all &= S.wok[w];
+  return all != 0;
 }
 
 // Combining the slices' records: lane t of every wave takes slice t's entry and a
@@ -303,6 +322,24 @@ __device__ __forceinline__ Stat xmerge_stat(const Shared<NW>& S, int NS, int iR,
     stat_merge(a, R2, S2);
   }
   return Stat{__shfl(a.R, 0), __shfl(a.S, 0)};
+}
+// Two statistics (records' entries iR0/iS0 and iR1/iS1) in one butterfly, so the
+// shuffles of both are in flight together.
+template <int NW>
+__device__ __forceinline__ void xmerge_stat2(const Shared<NW>& S, int NS, int iR0, int iS0, int iR1, int iS1,
+                                             Stat& a, Stat& c) {
+  const int lane = threadIdx.x & 63;
+  a = Stat{}, c = Stat{};
+  if (lane < NS) a = Stat{(float)S.xr[lane][iR0], S.xr[lane][iS0]}, c = Stat{(float)S.xr[lane][iR1], S.xr[lane][iS1]};
+#pragma unroll
+  for (int o = 1; o < kMaxNS; o <<= 1) {
+    const float Ra = __shfl_xor(a.R, o), Rc = __shfl_xor(c.R, o);
+    const double Sa = __shfl_xor(a.S, o), Sc = __shfl_xor(c.S, o);
+    stat_merge(a, Ra, Sa);
+    stat_merge(c, Rc, Sc);
+  }
+  a = Stat{__shfl(a.R, 0), __shfl(a.S, 0)};
+  c = Stat{__shfl(c.R, 0), __shfl(c.S, 0)};
 }
 template <int NW>
 __device__ __forceinline__ double xsum(const Shared<NW>& S, int NS, int i) {
@@ -609,8 +646,7 @@ __global__ __launch_bounds__(NTH, NTH == kThreadsSliced ? 2 : 1) void mss_kernel
       if (NS > 1) {
         const double mine[kXRec] = {sl.R, sl.S, sq.R, sq.S, 0.0, 0.0, 0.0, 0.0};
         if (!exchange<NW>(S, mine, rec, NS, s, xr++, spin)) return give_up();
-        sl = xmerge_stat(S, NS, 0, 1);
-        sq = xmerge_stat(S, NS, 2, 3);
+        xmerge_stat2(S, NS, 0, 1, 2, 3, sl, sq);
       }
     }
 
