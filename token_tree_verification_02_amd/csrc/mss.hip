@@ -251,7 +251,8 @@ __device__ __forceinline__ void block_reduce(Shared<NW>& S, int& slot, Stat& a, 
 //   - Two record slots alternate (tags r + 1 and r + 3 differ): a slice writes
 //     slot r & 1 again only at r + 2, after it has read every slice's record of
 //     r + 1, which each slice wrote after reading reduction r.  The tags start at
-//     0 (mss_clear_kernel), so a record of an earlier call is never taken.
+//     0 (cleared before the walk by mss_clear_kernel, or by the statistics pass
+//     in the all-row mode), so a record of an earlier call is never taken.
 //   - The wait is bounded: after `spin` polls of a word (kSpinMax unless the
 //     host set another limit) the slice gives up and
 //     the caller ends the walk with an error, so every workgroup exits.
