@@ -94,7 +94,49 @@ __device__ __forceinline__ bool sk_plan(const int32_t* __restrict__ plen, int B,
   __shared__ int hit[3];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   auto tiles = [&](int b) { return b < B ? ((clamp_len(plen[b], cap) + kTK - 1) / kTK + ttree) * Hkv : 0; };
-  // pass 1: the total
+  if (B <= NT) {
+    // one pass (a batch of at most NT sequences): each thread's sequence, one
+    // inclusive scan over the workgroup gives the offsets and the total, then the
+    // sequence holding tile r0 reports the cursor
+    const int b = tid;
+    const int t = tiles(b);
+    int x = t;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(x, o);
+      if (lane >= o) x += y;
+    }
+    if (lane == 63) part[wv] = x;
+    __syncthreads();
+    int off = 0, T = 0;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) {
+      off += w < wv ? part[w] : 0;
+      T += part[w];
+    }
+    const int ex = off + x - t;  // tiles before sequence b
+    const int per = (T + NV - 1) / NV;
+    const long long r0 = (long long)v * per;
+    T_out = T;
+    per_out = per;
+    if (rec != nullptr) {
+      if (tid == 0) rec[0] = T, rec[1] = per, rec[2] = NV, rec[3] = 0, rec[4 + B] = T;
+      if (b < B) rec[4 + b] = ex;
+    }
+    if (r0 >= T) return false;  // uniform
+    if (b < B && ex <= r0 && r0 < ex + t) {
+      const int tb = t / Hkv, r = (int)(r0 - ex);
+      hit[0] = b;
+      hit[1] = r / tb;
+      hit[2] = r % tb;
+    }
+    __syncthreads();
+    c.b = hit[0];
+    c.g = hit[1];
+    c.off = hit[2];
+    return true;
+  }
+  // larger batches: pass 1, the total
   int T = 0;
   for (int base = 0; base < B; base += NT) {
     int x = tiles(base + tid);
