@@ -155,6 +155,38 @@ __device__ __forceinline__ void stat_add8(Stat& st, const float (&v)[kEPT]) {
   st.S += (double)s;
 }
 
+// The same statistics over a group of chunks already in registers: the group's
+// largest value first, so the reference moves at most once per group, then per
+// chunk one fp32 sum of its eight terms, added in fp64.  Chunks u >= nv lie past
+// the end of the range (a partial last group) and are skipped.
+template <bool BF16, int G>
+__device__ __forceinline__ void stat_add_group(Stat& st, const Raw<BF16> (&q)[G], int nv) {
+  float cm = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < G; ++u) {
+    if (u >= nv) break;
+    float v[kEPT];
+    q[u].unpack(v);
+    cm = fmaxf(cm, max8(v));
+  }
+  if (cm == -INFINITY) return;
+  const float r = ceilf(cm * kLog2e);
+  if (r > st.R) {
+    st.S = st.R == -INFINITY ? 0.0 : shift(st.S, st.R, r);
+    st.R = r;
+  }
+#pragma unroll
+  for (int u = 0; u < G; ++u) {
+    if (u >= nv) break;
+    float v[kEPT];
+    q[u].unpack(v);
+    float sm = ex(v[0], -st.R);
+#pragma unroll
+    for (int j = 1; j < kEPT; ++j) sm += ex(v[j], -st.R);
+    st.S += (double)sm;
+  }
+}
+
 __device__ __forceinline__ void stat_merge(Stat& a, float R, double S) {
   if (R == -INFINITY) return;
   if (a.R == -INFINITY) {
@@ -184,15 +216,56 @@ struct Shared {
   int result;
 };
 
+// Cross-lane reductions with DPP moves (a few cycles each, no LDS round trip).
+// Within a row of 16 lanes: swap neighbours, swap pairs, take the other quad of
+// the half-row (half-row mirror), take the other half of the row (row mirror);
+// each lane then holds its row's result, and since every step combines its own
+// value with its partner's by a commutative operation, all 16 lanes hold the
+// same bits.  The four rows' results are then read from lanes 0, 16, 32, 48 and
+// combined in that fixed order, uniformly.
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp(double x) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, x);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, 0xF, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, 0xF, 0xF, false);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ float lane_read(float x, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
+}
+__device__ __forceinline__ double lane_read(double x, int l) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, x);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), l);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ float row_max(float x) {
+  x = fmaxf(x, dpp<kDppXor1>(x));
+  x = fmaxf(x, dpp<kDppXor2>(x));
+  x = fmaxf(x, dpp<kDppHalfMirror>(x));
+  return fmaxf(x, dpp<kDppMirror>(x));
+}
+__device__ __forceinline__ double row_sum(double x) {
+  x += dpp<kDppXor1>(x);
+  x += dpp<kDppXor2>(x);
+  x += dpp<kDppHalfMirror>(x);
+  return x + dpp<kDppMirror>(x);
+}
 __device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-  return x;
+  x = row_max(x);
+  return fmaxf(fmaxf(lane_read(x, 0), lane_read(x, 16)), fmaxf(lane_read(x, 32), lane_read(x, 48)));
 }
 __device__ __forceinline__ double wave_sum(double x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-  return x;
+  x = row_sum(x);
+  return (lane_read(x, 0) + lane_read(x, 16)) + (lane_read(x, 32) + lane_read(x, 48));
 }
 // a wave's statistics: the largest reference, every lane's sum moved onto it
 // (exactly), then one plain fp64 sum
@@ -306,57 +379,50 @@ __device__ __forceinline__ bool exchange(Shared<NW>& S, const double (&mine)[kXR
   return all != 0;
 }
 
-// Combining the slices' records: lane t of every wave takes slice t's entry and a
-// butterfly of shuffles merges the (at most 16) entries; every lane then takes
-// lane 0's result, so all threads of all slices hold the same value (the same
-// data, merged in the same fixed order).  Replaces a serial loop over slices,
-// each step of which waited on an LDS read and an fp64 chain.
+// Combining the slices' records: lane t of every wave takes slice t's entry (at
+// most 16 slices, so all in the first row of 16 lanes); the largest reference,
+// every entry moved onto it exactly, and one sum, all with row-wide DPP
+// reductions; every lane then takes lane 0's result, so all threads of all
+// slices hold the same value (the same data, combined in the same fixed order).
+__device__ __forceinline__ Stat row_stat(Stat a) {
+  const float R = row_max(a.R);
+  const double s = a.R == -INFINITY ? 0.0 : shift(a.S, a.R, R);
+  return Stat{lane_read(R, 0), lane_read(row_sum(s), 0)};
+}
 template <int NW>
 __device__ __forceinline__ Stat xmerge_stat(const Shared<NW>& S, int NS, int iR, int iS) {
   const int lane = threadIdx.x & 63;
   Stat a;
   if (lane < NS) a = Stat{(float)S.xr[lane][iR], S.xr[lane][iS]};
-#pragma unroll
-  for (int o = 1; o < kMaxNS; o <<= 1) {
-    const float R2 = __shfl_xor(a.R, o);
-    const double S2 = __shfl_xor(a.S, o);
-    stat_merge(a, R2, S2);
-  }
-  return Stat{__shfl(a.R, 0), __shfl(a.S, 0)};
+  return row_stat(a);
 }
-// Two statistics (records' entries iR0/iS0 and iR1/iS1) in one butterfly, so the
-// shuffles of both are in flight together.
+// Two statistics (records' entries iR0/iS0 and iR1/iS1) side by side, so their
+// reductions overlap.
 template <int NW>
 __device__ __forceinline__ void xmerge_stat2(const Shared<NW>& S, int NS, int iR0, int iS0, int iR1, int iS1,
                                              Stat& a, Stat& c) {
   const int lane = threadIdx.x & 63;
   a = Stat{}, c = Stat{};
   if (lane < NS) a = Stat{(float)S.xr[lane][iR0], S.xr[lane][iS0]}, c = Stat{(float)S.xr[lane][iR1], S.xr[lane][iS1]};
-#pragma unroll
-  for (int o = 1; o < kMaxNS; o <<= 1) {
-    const float Ra = __shfl_xor(a.R, o), Rc = __shfl_xor(c.R, o);
-    const double Sa = __shfl_xor(a.S, o), Sc = __shfl_xor(c.S, o);
-    stat_merge(a, Ra, Sa);
-    stat_merge(c, Rc, Sc);
-  }
-  a = Stat{__shfl(a.R, 0), __shfl(a.S, 0)};
-  c = Stat{__shfl(c.R, 0), __shfl(c.S, 0)};
+  a = row_stat(a);
+  c = row_stat(c);
 }
 template <int NW>
 __device__ __forceinline__ double xsum(const Shared<NW>& S, int NS, int i) {
   const int lane = threadIdx.x & 63;
-  double x = lane < NS ? S.xr[lane][i] : 0.0;
-#pragma unroll
-  for (int o = 1; o < kMaxNS; o <<= 1) x += __shfl_xor(x, o);
-  return __shfl(x, 0);
+  return lane_read(row_sum(lane < NS ? S.xr[lane][i] : 0.0), 0);
 }
+
+template <bool B>  // a compile-time flag as a type (selects a specialised pass)
+struct BoolC {
+  static constexpr bool value = B;
+};
 
 // One chunk of a residual pass: p (from raw logits via max/normaliser, or from
 // the previous unnormalised residual via its sum), minus q from its logits;
 // writes r = max(0, p - q) to the output row, catches p and r at the next
 // child's token, returns the chunk's sum of r.
 struct Resid {
-  bool from_logits;
   float nm;   // -R of the LLM row's statistics
   float sp_hi, sp_lo;  // scale of p (1/S or 1/T) as a two-float sum
   float nmq;  // -R of the SSM row's
@@ -365,10 +431,11 @@ struct Resid {
   int xn;
   float* cap_prev;
   float* cap_r;
+  template <bool FL>  // p from raw logits (else from the residual row)
   __device__ __forceinline__ float chunk(int e0, float (&pv)[kEPT], const float (&qv)[kEPT]) const {
 #pragma unroll
     for (int j = 0; j < kEPT; ++j) {
-      const float e = from_logits ? ex(pv[j], nm) : pv[j];
+      const float e = FL ? ex(pv[j], nm) : pv[j];
       pv[j] = fmaf(e, sp_hi, e * sp_lo);
     }
     float r[kEPT];
@@ -409,8 +476,7 @@ __device__ __forceinline__ void seg_store(Shared<NW>& S, int ch, const float (&v
   double sd = 0.0;
 #pragma unroll
   for (int j = 0; j < kEPT; ++j) sd += (double)v[j];
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) sd += __shfl_xor(sd, o);
+  sd = wave_sum(sd);
   if ((threadIdx.x & 63) == 0) S.segd[ch * NW + (threadIdx.x >> 6)] = sd;
 }
 
@@ -457,13 +523,7 @@ __global__ __launch_bounds__(256) void row_stats_kernel(int n, int V, int vec, c
     Raw<BF16> q[kG];
 #pragma unroll
     for (int u = 0; u < kG; ++u) q[u].load(row, min(c + u, nfull - 1) * kC + tid * kEPT);
-#pragma unroll
-    for (int u = 0; u < kG; ++u) {
-      if (c + u >= nfull) break;
-      float v[kEPT];
-      q[u].unpack(v);
-      stat_add8(st, v);
-    }
+    stat_add_group<BF16, kG>(st, q, nfull - c);
   }
   for (c = nfull; c < nch; ++c) {
     float v[kEPT];
@@ -615,21 +675,9 @@ __global__ __launch_bounds__(NTH, NTH == kThreadsSliced ? 2 : 1) void mss_kernel
         if (srow) {
 #pragma unroll
           for (int u = 0; u < kU; ++u) q[u].load(srow, min(c + u, cf - 1) * CH + tid * kEPT);
-#pragma unroll
-          for (int u = 0; u < kU; ++u) {
-            if (c + u >= cf) break;
-            float v[kEPT];
-            q[u].unpack(v);
-            stat_add8(sq, v);
-          }
+          stat_add_group<BF16, kU>(sq, q, cf - c);
         }
-#pragma unroll
-        for (int u = 0; u < kU; ++u) {
-          if (c + u >= cf) break;
-          float v[kEPT];
-          a[u].unpack(v);
-          stat_add8(sl, v);
-        }
+        stat_add_group<BF16, kU>(sl, a, cf - c);
       }
       c = max(c0, cf);
       for (; c < c1; ++c) {
@@ -677,63 +725,45 @@ __global__ __launch_bounds__(NTH, NTH == kThreadsSliced ? 2 : 1) void mss_kernel
       }
       const float* rin = rbase + (size_t)ib * Vpad;
       float* rout = rbase + (size_t)(ib ^ 1) * Vpad;
-      Resid R{from_logits, -sl.R, 0.f, 0.f, -sq.R, 0.f, 0.f, rout, xn, S.cap_prev + (i & 1), S.cap_r + (i & 1)};
+      Resid R{-sl.R, 0.f, 0.f, -sq.R, 0.f, 0.f, rout, xn, S.cap_prev + (i & 1), S.cap_r + (i & 1)};
       split2(from_logits ? 1.0 / sl.S : 1.0 / T, R.sp_hi, R.sp_lo);
       split2(1.0 / sq.S, R.sq_hi, R.sq_lo);
       double tsum = 0.0;
       Stat sn, unused;  // the next child's SSM row
-      {
+      // the pass, specialised on where p comes from (raw logits or the residual row)
+      auto resid_pass = [&](auto fl) {
+        constexpr bool FL = decltype(fl)::value;
+        using PRaw = Raw<FL ? BF16 : false>;
+        const void* prow = FL ? (const void*)lrow : (const void*)rin;
         int ch = c0;
         // three rows in flight here, so a smaller group; a slice of the sliced walk
         // holds few chunks, so there the whole slice goes in one group
         constexpr int kR = NTH == kThreadsSliced ? (BF16 ? 8 : 4) : (BF16 ? 4 : 2);
         for (; ch < cf; ch += kR) {  // partial last group as in the entry pass
-          Raw<false> pq[kR];  // the current distribution: raw logits (bf16 uses half) or residual
+          PRaw pq[kR];  // the current distribution: raw logits or residual
           Raw<BF16> qq[kR], nq[kR];
 #pragma unroll
-          for (int u = 0; u < kR; ++u) {
-            const int e0 = min(ch + u, cf - 1) * CH + tid * kEPT;
-            if (from_logits) {
-              if (BF16)
-                pq[u].w[0] = *(const uint4*)((const uint16_t*)lrow + e0);
-              else
-                pq[u].load(lrow, e0);
-            } else {
-              pq[u].load(rin, e0);
-            }
-          }
+          for (int u = 0; u < kR; ++u) pq[u].load(prow, min(ch + u, cf - 1) * CH + tid * kEPT);
 #pragma unroll
           for (int u = 0; u < kR; ++u) qq[u].load(crow, min(ch + u, cf - 1) * CH + tid * kEPT);
           if (nrow) {
 #pragma unroll
             for (int u = 0; u < kR; ++u) nq[u].load(nrow, min(ch + u, cf - 1) * CH + tid * kEPT);
-#pragma unroll
-            for (int u = 0; u < kR; ++u) {
-              if (ch + u >= cf) break;
-              float v[kEPT];
-              nq[u].unpack(v);
-              stat_add8(sn, v);
-            }
+            stat_add_group<BF16, kR>(sn, nq, cf - ch);
           }
 #pragma unroll
           for (int u = 0; u < kR; ++u) {
             if (ch + u >= cf) break;
             float pv[kEPT], qv[kEPT];
-            if (from_logits && BF16) {
-              Raw<true> t;
-              t.w[0] = pq[u].w[0];
-              t.unpack(pv);
-            } else {
-              pq[u].unpack(pv);
-            }
+            pq[u].unpack(pv);
             qq[u].unpack(qv);
-            tsum += (double)R.chunk((ch + u) * CH + tid * kEPT, pv, qv);
+            tsum += (double)R.template chunk<FL>((ch + u) * CH + tid * kEPT, pv, qv);
           }
         }
         for (ch = max(c0, cf); ch < c1; ++ch) {
           const int e0 = ch * CH + tid * kEPT;
           float pv[kEPT], qv[kEPT];
-          if (from_logits) {
+          if constexpr (FL) {
             load8<BF16>(lrow, e0, V, vec, pv);
           } else {
             Raw<false> r1;
@@ -741,13 +771,17 @@ __global__ __launch_bounds__(NTH, NTH == kThreadsSliced ? 2 : 1) void mss_kernel
             r1.unpack(pv);
           }
           load8<BF16>(crow, e0, V, vec, qv);
-          tsum += (double)R.chunk(e0, pv, qv);
+          tsum += (double)R.template chunk<FL>(e0, pv, qv);
           if (nrow) {
             load8<BF16>(nrow, e0, V, vec, qv);
             stat_add8(sn, qv);
           }
         }
-      }
+      };
+      if (from_logits)
+        resid_pass(BoolC<true>{});
+      else
+        resid_pass(BoolC<false>{});
       block_reduce<NW>(S, slot, sn, unused, tsum);
       float capp = S.cap_prev[i & 1], capr = S.cap_r[i & 1];  // caught by the thread owning xn
       if (NS > 1) {
@@ -838,10 +872,7 @@ __global__ __launch_bounds__(NTH, NTH == kThreadsSliced ? 2 : 1) void mss_kernel
     if (wv == 0) {
       double tot = 0.0;
       for (int s0 = sg0; s0 < sg1; s0 += 64) {
-        double x = s0 + lane < sg1 ? S.segd[s0 + lane] : 0.0;
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-        tot += x;
+        tot += wave_sum(s0 + lane < sg1 ? S.segd[s0 + lane] : 0.0);
       }
       if (lane == 0) S.xtot = tot;
     }
