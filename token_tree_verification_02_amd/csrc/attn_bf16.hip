@@ -50,6 +50,18 @@ namespace {
 
 using namespace attn;
 
+// A lane's value combined with lane (l ^ 32)'s through the gfx950 lane swap (a
+// VALU op): the swap of a register with itself leaves the lower half's values in
+// every lane of the first result and the upper half's in the second.
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+}
+
 template <int D, int RB, int KS, int TK, int S, bool FP8 = false>
 struct Cfg {
   static constexpr int NT = 64 * RB * KS;      // threads per workgroup
@@ -471,7 +483,7 @@ __global__ __launch_bounds__(64 * RB * KS) void attn_bf16_kernel(AttnArgs a, int
             mx = fmaxf(mx, Scur[r]);
           }
         }
-        mx = fmaxf(mx, __shfl_xor(mx, 32)) * slt;  // scale > 0 commutes with max
+        mx = max_xor32(mx) * slt;  // scale > 0 commutes with max
         if (__any(mx > m_run + kTau)) {
           const float m_new = fmaxf(m_run, mx);
           const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
@@ -536,7 +548,7 @@ __global__ __launch_bounds__(64 * RB * KS) void attn_bf16_kernel(AttnArgs a, int
     }
   }
 
-  const float ltot = lsum + __shfl_xor(lsum, 32);
+  const float ltot = sum_xor32(lsum);
   if (!qvalid) return;
   const int u = qrow / G, gi = qrow % G, h = g * G + gi;
   if (direct) {

@@ -216,37 +216,10 @@ struct Shared {
   int result;
 };
 
-// Cross-lane reductions with DPP moves (a few cycles each, no LDS round trip).
-// Within a row of 16 lanes: swap neighbours, swap pairs, take the other quad of
-// the half-row (half-row mirror), take the other half of the row (row mirror);
-// each lane then holds its row's result, and since every step combines its own
-// value with its partner's by a commutative operation, all 16 lanes hold the
-// same bits.  The four rows' results are then read from lanes 0, 16, 32, 48 and
-// combined in that fixed order, uniformly.
-constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
-constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
-constexpr int kDppHalfMirror = 0x141;
-constexpr int kDppMirror = 0x140;
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
-}
-template <int CTRL>
-__device__ __forceinline__ double dpp(double x) {
-  const uint64_t b = __builtin_bit_cast(uint64_t, x);
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, 0xF, 0xF, false);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, 0xF, 0xF, false);
-  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
-}
-__device__ __forceinline__ float lane_read(float x, int l) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
-}
-__device__ __forceinline__ double lane_read(double x, int l) {
-  const uint64_t b = __builtin_bit_cast(uint64_t, x);
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, l);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), l);
-  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
-}
+// Cross-lane reductions: DPP steps within each row of 16 lanes; since every step
+// combines a lane's own value with its partner's by a commutative operation, all
+// 16 lanes of a row hold the same bits.  The four rows' results are then read from
+// lanes 0, 16, 32, 48 and combined in that fixed order, uniformly.
 __device__ __forceinline__ float row_max(float x) {
   x = fmaxf(x, dpp<kDppXor1>(x));
   x = fmaxf(x, dpp<kDppXor2>(x));

@@ -81,11 +81,22 @@ __device__ __forceinline__ bool beats(float v2, int i2, float v1, int i1) {
   return v2 > v1 || (v2 == v1 && i2 < i1) || (i1 == INT_MAX && i2 != INT_MAX);
 }
 
+// (bv, bi) := the better of itself and its DPP partner's pair
+template <int CTRL>
+__device__ __forceinline__ void best_with(float& bv, int& bi) {
+  const float ov = dpp<CTRL>(bv);
+  const int oi = dpp<CTRL>(bi);
+  if (beats(ov, oi, bv, bi)) {
+    bv = ov;
+    bi = oi;
+  }
+}
+
 // One workgroup of 256 threads per logits row.  Each thread loads 16 16-byte
 // vectors per round before it compares anything, keeps the index of the first
 // vector whose maximum beats its running best, and at the end re-reads that one
-// vector (a cache hit) to find the lowest index of the maximum inside it; a wave
-// shuffle and an LDS step then reduce (value, index) pairs.
+// vector (a cache hit) to find the lowest index of the maximum inside it; DPP moves
+// and an LDS step then reduce (value, index) pairs.
 // the low / high 16-bit element of a 32-bit word, as float (exact)
 template <int DT>
 __device__ __forceinline__ float lo16(uint32_t w) {
@@ -170,10 +181,17 @@ __global__ __launch_bounds__(256) void argmax_kernel(const void* __restrict__ lo
       bi = i;
     }
   }
+  // the wave's best: within rows of 16 lanes by DPP moves, then the other rows'
+  // bests read from lanes 16, 32, 48 (the order is a total one, so any
+  // combination order gives the same pair)
+  best_with<kDppXor1>(bv, bi);
+  best_with<kDppXor2>(bv, bi);
+  best_with<kDppHalfMirror>(bv, bi);
+  best_with<kDppMirror>(bv, bi);
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float ov = __shfl_xor(bv, o);
-    const int oi = __shfl_xor(bi, o);
+  for (int r = 1; r < 4; ++r) {
+    const float ov = lane_read(bv, 16 * r);
+    const int oi = lane_read(bi, 16 * r);
     if (beats(ov, oi, bv, bi)) {
       bv = ov;
       bi = oi;

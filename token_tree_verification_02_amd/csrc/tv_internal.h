@@ -24,6 +24,43 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return __builtin_bit_cast(uint16_t, h);
 }
 
+// ------------------------------------------------------------------ cross-lane moves
+// DPP controls within each row of 16 lanes (a lane reads its partner's register
+// in the same VALU op, no LDS round trip): swap neighbours, swap pairs, take the
+// other quad of the half-row (half-row mirror), take the other half of the row
+// (row mirror).  Combining a lane's value with its partner's over these four
+// steps reduces each row of 16 lanes.
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+template <int CTRL>
+__device__ __forceinline__ int dpp(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, dpp<CTRL>(__builtin_bit_cast(int, x)));
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp(double x) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, x);
+  const uint32_t lo = (uint32_t)dpp<CTRL>((int)(uint32_t)b);
+  const uint32_t hi = (uint32_t)dpp<CTRL>((int)(uint32_t)(b >> 32));
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+// lane l's value, the same in every lane
+__device__ __forceinline__ int lane_read(int x, int l) { return __builtin_amdgcn_readlane(x, l); }
+__device__ __forceinline__ float lane_read(float x, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
+}
+__device__ __forceinline__ double lane_read(double x, int l) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, x);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), l);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
 // ------------------------------------------------------------------ launch plans
 struct AttnPlan {
   int rows;        // n * (Hq/Hkv): query rows per (sequence, KV head)
