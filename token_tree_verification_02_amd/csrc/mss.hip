@@ -260,27 +260,47 @@ __device__ __forceinline__ void lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// Workgroup-wide merge of two row statistics and one plain fp64 sum per thread.
-// Every thread ends with the same values, merged in the same order from LDS.
-// One barrier; alternating LDS slots so back-to-back calls never overwrite
-// values another wave is still reading.
+// The merge of NW entries (R_k, S_k) held in LDS: every entry read at once, the
+// largest reference, each sum moved onto it (exactly: a power-of-two scale), and
+// one fp64 sum in entry order.  Equal, bit for bit, to merging them one by one,
+// since a power-of-two scale of a rounded sum is exact.
 template <int NW>
+__device__ __forceinline__ Stat merge_entries(const float (&R)[NW], const double (&Sv)[NW]) {
+  float r[NW];
+  double sv[NW];
+#pragma unroll
+  for (int k = 0; k < NW; ++k) r[k] = R[k], sv[k] = Sv[k];
+  float M = r[0];
+#pragma unroll
+  for (int k = 1; k < NW; ++k) M = fmaxf(M, r[k]);
+  double t = 0.0;
+#pragma unroll
+  for (int k = 0; k < NW; ++k) t += r[k] == -INFINITY ? 0.0 : shift(sv[k], r[k], M);
+  return Stat{M, t};
+}
+
+// Workgroup-wide merge of one or (TWO) two row statistics and one plain fp64 sum
+// per thread.  Every thread ends with the same values, merged in the same order
+// from LDS.  One barrier; alternating LDS slots so back-to-back calls never
+// overwrite values another wave is still reading.
+template <int NW, bool TWO>
 __device__ __forceinline__ void block_reduce(Shared<NW>& S, int& slot, Stat& a, Stat& b, double& t) {
-  const Stat wa = wave_stat(a), wb = wave_stat(b);
+  const Stat wa = wave_stat(a);
+  Stat wb;
+  if constexpr (TWO) wb = wave_stat(b);
   const double wt = wave_sum(t);
   const int w = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) {
     S.rR[slot][0][w] = wa.R, S.rS[slot][0][w] = wa.S;
-    S.rR[slot][1][w] = wb.R, S.rS[slot][1][w] = wb.S;
+    if constexpr (TWO) S.rR[slot][1][w] = wb.R, S.rS[slot][1][w] = wb.S;
     S.rS[slot][2][w] = wt;
   }
   lds_sync();
-  a = Stat{}, b = Stat{}, t = 0.0;
-  for (int k = 0; k < NW; ++k) {
-    stat_merge(a, S.rR[slot][0][k], S.rS[slot][0][k]);
-    stat_merge(b, S.rR[slot][1][k], S.rS[slot][1][k]);
-    t += S.rS[slot][2][k];
-  }
+  a = merge_entries<NW>(S.rR[slot][0], S.rS[slot][0]);
+  if constexpr (TWO) b = merge_entries<NW>(S.rR[slot][1], S.rS[slot][1]);
+  t = 0.0;
+#pragma unroll
+  for (int k = 0; k < NW; ++k) t += S.rS[slot][2][k];
   slot ^= 1;
 }
 
@@ -599,21 +619,21 @@ __global__ __launch_bounds__(NTH, NTH == kThreadsSliced ? 2 : 1) void mss_kernel
   if (tid == 0) S.path[0] = 0;
   for (;;) {
     // ---- children of cur in node-id order (ballot over node ids)
+    // (each child writes itself at its rank: the children of lower waves, then
+    // those of lower lanes in its own wave)
     const bool isc = tid < n && tid > cur && S.par[tid] == cur;
     const unsigned long long bl = __ballot(isc);
     if (tid < 256 && lane == 0) S.ball[wv] = bl;
-    __syncthreads();
-    int k = 0;
+    lds_sync();  // LDS only: residual stores of the last node may still drain
+    int k = 0, below = 0;
+#pragma unroll
     for (int w = 0; w < 4; ++w) {
-      unsigned long long msk = S.ball[w];
-      while (msk) {
-        const int v = w * 64 + __builtin_ctzll(msk);
-        msk &= msk - 1;
-        if (tid == 0) S.child[k] = v;
-        ++k;
-      }
+      const int cnt = __builtin_popcountll(S.ball[w]);
+      below += w < wv ? cnt : 0;
+      k += cnt;
     }
-    __syncthreads();  // S.child visible
+    if (isc) S.child[below + __builtin_popcountll(bl & ((1ull << lane) - 1))] = tid;
+    lds_sync();  // S.child visible
     const char* lrow = lbase + (size_t)cur * V * es;
     const int c1st = k > 0 ? S.child[0] : -1;
     const char* srow = c1st >= 0 && !pre ? sbase + (size_t)c1st * V * es : nullptr;
@@ -664,7 +684,7 @@ __global__ __launch_bounds__(NTH, NTH == kThreadsSliced ? 2 : 1) void mss_kernel
         }
       }
       double unused = 0.0;
-      block_reduce<NW>(S, slot, sl, sq, unused);
+      block_reduce<NW, true>(S, slot, sl, sq, unused);
       if (NS > 1) {
         const double mine[kXRec] = {sl.R, sl.S, sq.R, sq.S, 0.0, 0.0, 0.0, 0.0};
         if (!exchange<NW>(S, mine, rec, NS, s, xr++, spin)) return give_up();
@@ -755,7 +775,7 @@ __global__ __launch_bounds__(NTH, NTH == kThreadsSliced ? 2 : 1) void mss_kernel
         resid_pass(BoolC<true>{});
       else
         resid_pass(BoolC<false>{});
-      block_reduce<NW>(S, slot, sn, unused, tsum);
+      block_reduce<NW, false>(S, slot, sn, unused, tsum);
       float capp = S.cap_prev[i & 1], capr = S.cap_r[i & 1];  // caught by the thread owning xn
       if (NS > 1) {
         const bool own = xn >= c0 * CH && xn < c1 * CH;
