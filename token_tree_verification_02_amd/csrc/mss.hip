@@ -219,7 +219,8 @@ struct Shared {
 // Cross-lane reductions: DPP steps within each row of 16 lanes; since every step
 // combines a lane's own value with its partner's by a commutative operation, all
 // 16 lanes of a row hold the same bits.  The four rows' results are then read from
-// lanes 0, 16, 32, 48 and combined in that fixed order, uniformly.
+// lanes 0, 16, 32, 48 and combined in that fixed order, uniformly.  Called with
+// every lane of the wave active (the walk's reductions are workgroup-uniform).
 __device__ __forceinline__ float row_max(float x) {
   x = fmaxf(x, dpp<kDppXor1>(x));
   x = fmaxf(x, dpp<kDppXor2>(x));

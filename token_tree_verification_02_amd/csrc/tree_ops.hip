@@ -81,7 +81,8 @@ __device__ __forceinline__ bool beats(float v2, int i2, float v1, int i1) {
   return v2 > v1 || (v2 == v1 && i2 < i1) || (i1 == INT_MAX && i2 != INT_MAX);
 }
 
-// (bv, bi) := the better of itself and its DPP partner's pair
+// (bv, bi) := the better of itself and its DPP partner's pair (all lanes active:
+// a lane reads its partner's register whether or not the partner is active)
 template <int CTRL>
 __device__ __forceinline__ void best_with(float& bv, int& bi) {
   const float ov = dpp<CTRL>(bv);
