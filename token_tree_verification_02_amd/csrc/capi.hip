@@ -116,10 +116,12 @@ int plan_attention(const tv_attn_desc* d, AttnPlan* p, int cus) {
     p->rsplit = (qb + 7) / 8;
   }
   const int tkt = p->tk * p->ks;
-  // split long prefixes so the grid covers the chip about twice, in chunks of at
-  // least 1024 tokens so partial outputs stay a small fraction of the KV bytes
+  // split long prefixes so the grid covers the chip once (one workgroup per
+  // compute unit streams faster than two sharing it, and fewer partial outputs
+  // are written and merged), in chunks of at least 1024 tokens so partial outputs
+  // stay a small fraction of the KV bytes
   const long long base = (long long)d->B * d->Hkv * p->rsplit;
-  const long long target = 2LL * cus;
+  const long long target = cus;
   if (base > 0 && base < target && p->cap > 1024) {
     const long long want = (target + base - 1) / base;
     long long cl = (p->cap + want - 1) / want;
