@@ -261,7 +261,7 @@ int tree_verify_greedy(int B, int n, int V, int logits_dtype, const void* logits
  *     walk spread over up to 16 workgroups, each owning a slice of the
  *     vocabulary, which exchange row statistics through the workspace at each
  *     step (slices chosen so that all B * slices workgroups fit on the device
- *     at once, 512 on MI355X; it needs `status`, else mode 1 runs).  Mode 2
+ *     at once, 768 on MI355X; it needs `status`, else mode 1 runs).  Mode 2
  *     spreads its walk over slices the same way (they exchange only at the
  *     residual passes and the draw), with the same condition.  0 takes 2
  *     while all rows together are at most 1 GiB, else 3.  The results are the same in every mode.  In mode 3

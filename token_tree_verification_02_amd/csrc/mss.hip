@@ -38,7 +38,7 @@ namespace tv {
 namespace {
 
 constexpr int kThreads = 512;             // one workgroup per sequence
-constexpr int kThreadsSliced = 256;        // several per sequence: two fit on a CU
+constexpr int kThreadsSliced = 256;        // several per sequence: three fit on a CU
 constexpr int kEPT = 8;                      // elements per thread per chunk
 constexpr int kChunk = kThreads * kEPT;      // 4096 (the workspace's row padding)
 constexpr int kSeg = 64 * kEPT;              // 512 elements: one wave's share of a chunk
@@ -47,10 +47,14 @@ constexpr int kMaxNS = 16;                   // vocabulary slices per sequence (
 constexpr int kXRec = 8;                     // doubles per exchange record
 constexpr int kSpinMax = 1 << 18;            // default: polls before a slice gives up on its peers
 // A pass over a row visits chunks in groups of kU whose loads are all issued
-// before any of them is used, so a workgroup keeps kU * 8 KB of each
-// row in flight instead of waiting out one memory latency per chunk.
+// before any of them is used, so a workgroup keeps kU chunks of each row in
+// flight instead of waiting out one memory latency per chunk.  The sliced walk
+// takes groups of 6 (bf16): a slice of workload-sized rows is then one group,
+// within the register budget of three workgroups per compute unit.
 template <bool BF16>
 constexpr int kGroup = BF16 ? 8 : 4;
+template <bool BF16>
+constexpr int kGroupSliced = BF16 ? 6 : 3;
 
 template <bool BF16>
 __device__ __forceinline__ void load8(const void* row, int e0, int V, bool vec, float (&v)[kEPT]) {
@@ -549,11 +553,13 @@ __global__ __launch_bounds__(256) void mss_clear_kernel(int B, uint64_t* __restr
 // row statistics, residual sums, caught values and the draw's slice totals
 // are exchanged at each reduction (see exchange), and the slice holding the
 // drawn token writes the outputs.
-// Sliced walk (256 threads): two waves per SIMD at least (the register budget
-// that lets two of its workgroups share a CU), so its grid of up to 512
+// Sliced walk (256 threads): three waves per SIMD at least (the register budget
+// that lets three of its workgroups share a CU), so its grid of up to 768
 // workgroups is resident at once and no slice waits on a peer that cannot start.
+// (Three per unit measured faster than two, with 11 instead of 8 slices per
+// sequence on 64 sequences, and than four, whose budget spills.)
 template <bool BF16, int NTH>
-__global__ __launch_bounds__(NTH, NTH == kThreadsSliced ? 2 : 1) void mss_kernel(int n, int V, int vec, const void* __restrict__ logits,
+__global__ __launch_bounds__(NTH, NTH == kThreadsSliced ? 3 : 1) void mss_kernel(int n, int V, int vec, const void* __restrict__ logits,
                                                   const void* __restrict__ ssm, const int32_t* __restrict__ tokens,
                                                   const int32_t* __restrict__ parent,
                                                   const float* __restrict__ u_acc, const float* __restrict__ u_smp,
@@ -586,7 +592,7 @@ __global__ __launch_bounds__(NTH, NTH == kThreadsSliced ? 2 : 1) void mss_kernel
   const int cf = min(c1, nfull);
   uint64_t* const rec = NS > 1 ? xrec + (size_t)b * 2 * NS * kXW : nullptr;
   int xr = 0;  // exchanges so far
-  constexpr int kU = kGroup<BF16>;
+  constexpr int kU = NTH == kThreadsSliced ? kGroupSliced<BF16> : kGroup<BF16>;
   int32_t* pr = path_out + (size_t)b * n;
 
   // ---- load and check the tree: parents before children, tokens inside the vocabulary
@@ -730,9 +736,9 @@ __global__ __launch_bounds__(NTH, NTH == kThreadsSliced ? 2 : 1) void mss_kernel
         using PRaw = Raw<FL ? BF16 : false>;
         const void* prow = FL ? (const void*)lrow : (const void*)rin;
         int ch = c0;
-        // three rows in flight here, so a smaller group; a slice of the sliced walk
-        // holds few chunks, so there the whole slice goes in one group
-        constexpr int kR = NTH == kThreadsSliced ? (BF16 ? 8 : 4) : (BF16 ? 4 : 2);
+        // three rows in flight here, so a smaller group for one workgroup per
+        // sequence; the sliced walk keeps its group (a slice's chunks at once)
+        constexpr int kR = NTH == kThreadsSliced ? kGroupSliced<BF16> : (BF16 ? 4 : 2);
         for (; ch < cf; ch += kR) {  // partial last group as in the entry pass
           PRaw pq[kR];  // the current distribution: raw logits or residual
           Raw<BF16> qq[kR], nq[kR];
