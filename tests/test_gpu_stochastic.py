@@ -107,6 +107,10 @@ CASES = {
     "odd_v7_bf16": (W.config(2, B=12, L_lo=16, L_hi=16, vocab=7, tree="chain"), 1.0),
     "star_low_accept": (W.config(2, B=6, L_lo=16, L_hi=16, vocab=3000, tree="expand:39", n=40), 4.0),
     "v200k_chain": (W.config(2, B=2, L_lo=16, L_hi=16, vocab=200_003, tree="chain", n=6), 1.0),
+    # the largest tree (256 nodes, one per thread of a slice) and the smallest (the root
+    # alone: no child to test, the bonus is drawn from the root's LLM distribution)
+    "n256_random": (W.config(2, B=3, L_lo=16, L_hi=16, vocab=3000, tree="random", n=256, max_depth=40), 1.0),
+    "root_only": (W.config(2, B=5, L_lo=16, L_hi=16, vocab=5000, tree="chain", n=1), 1.0),
 }
 
 
