@@ -9,3 +9,12 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: full-size workloads (minutes of host-side input generation)")
+
+
+def pytest_sessionstart(session):
+    """A checkout without the built library (it is not tracked) builds it once
+    before the tests that load it; an existing build is used as it is."""
+    from token_tree_verification_02_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from token_tree_verification_02_amd import build as _build
+        _build.build()
