@@ -154,6 +154,31 @@ def test_stochastic_modes_agree(name):
             np.testing.assert_array_equal(a, b_, err_msg=f"mode {mode} {what}")
 
 
+@pytest.mark.parametrize("mode", [1, 2, 3])
+def test_stochastic_masked_vocabulary(mode):
+    """Masked (-inf) vocabulary ranges: LLM rows without mass over the first 60% of the
+    vocabulary (whole slices of the sliced walk hold none), SSM rows without mass over
+    the second half (where both apply, p and q have disjoint supports, so every draft
+    token is either accepted outright or leaves the residual p), one-hot LLM rows (the
+    bonus token is fixed) and one-hot SSM rows (every draft token but one has q = 0)."""
+    cfg = W.config(2, B=10, L_lo=16, L_hi=16, vocab=40000)
+    log(f"case stochastic masked vocabulary mode {mode}")
+    w = W.make_stochastic(cfg, seed=41)
+    V = cfg.vocab
+    lg = W.bf16_bits_to_f32(w["logits"]).copy()
+    sg = W.bf16_bits_to_f32(w["ssm_logits"]).copy()
+    lg[0:4, :, : V * 6 // 10] = -np.inf
+    sg[2:6, :, V // 2:] = -np.inf
+    lg[6] = -np.inf
+    lg[6, :, 12345] = 3.0
+    sg[7] = -np.inf
+    sg[7, :, 777] = 0.0
+    w["logits"], w["ssm_logits"] = W.f32_to_bf16_bits(lg), W.f32_to_bf16_bits(sg)
+    plen = check(w, max_close_frac=0.0, mode=mode)
+    path, plen2, bonus, _ = run_gpu(w, mode)
+    assert bonus[6] == 12345
+
+
 def test_sliced_walk_give_up_path():
     """The sliced walk's bounded wait, forced from the host: with a poll limit of 0
     every slice gives up at its first exchange, the call still completes and every
