@@ -102,6 +102,28 @@ def test_expand_constant_rows(V, dtype, k):
     log(f"  appended {list(r[4] - n_cur)}")
 
 
+@pytest.mark.parametrize("V,dtype,k", [(32000, "bf16", 4), (1000, "f32", 6)])
+def test_expand_masked_rows(V, dtype, k):
+    """Rows masked with -inf: a whole row (the top k are the lowest indices), fewer
+    finite entries than k (the finite ones first, then the lowest masked indices),
+    finite entries only in the last 16-byte vector, and the first half masked."""
+    log(f"case expand masked rows V={V} {dtype} k={k}")
+    B, F, n_max = 3, 4, 128
+    n_cur = np.full(B, 8, np.int32)
+    parent, depth, tokens = start_trees(B, n_cur, n_max, seed=9)
+    frontier = np.tile(np.arange(1, F + 1, dtype=np.int32), (B, 1))
+    rng = np.random.default_rng(V)
+    x = rng.normal(0, 2, size=(B, F, V)).astype(np.float32)
+    x[:, 0] = -np.inf
+    x[:, 1] = -np.inf
+    x[:, 1, [V // 3, 2 * V // 3]] = [1.0, -2.0]
+    x[:, 2, : V - 8] = -np.inf
+    x[:, 3, : V // 2] = -np.inf
+    st = W.f32_to_bf16_bits(x) if dtype == "bf16" else x
+    r = check_expand(st, dtype, frontier, n_cur, parent, depth, tokens, k, n_max)
+    log(f"  appended {list(r[4] - n_cur)}")
+
+
 def test_expand_rejections_leave_trees_unchanged():
     log("case expand rejections")
     B, F, V, k, n_max = 4, 4, 500, 3, 40
