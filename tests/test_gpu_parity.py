@@ -135,13 +135,18 @@ SMALL = {
 
 
 @pytest.mark.parametrize("name", list(SMALL))
-@pytest.mark.parametrize("variant", ["plain", "balanced", "needle"])
+@pytest.mark.parametrize("variant", ["plain", "balanced", "needle", "ramp", "ramp_down"])
 def test_small_parity(name, variant):
+    """"ramp" / "ramp_down": prefix scores rising (falling) by about 0.2 per key, so
+    every tile moves the running maximum far past the rescale threshold (or every
+    later tile's terms underflow against it)."""
     if name in FP8_MANY_ROWS:
         pytest.skip(FP8_MANY_ROWS_REASON)
     cfg = SMALL[name]
     if cfg.dtype == "f32" and variant != "plain":
         pytest.skip("variants target the bf16 tolerance")
+    if cfg.kv == "fp8" and variant.startswith("ramp"):
+        pytest.skip("the ramp variants take a 16- or 32-bit cache")
     log(f"case {name} {variant}")
     w = W.make(cfg, seed=100 + cfg.index, variant=variant)
     d = run(w)

@@ -319,6 +319,11 @@ def make(cfg: Config, seed: int | None = None, *, variant: str = "plain", plant:
                  bit or a dropped prefix moves the output by far more than the bf16
                  tolerance.  a_b solves a^2 = sqrt(D)*(ln(L_b/|S|) + (a^2 + D/16)/(2D)).
       "needle"   one dominant prefix key at j = L_b - 1 (pins the prefix end).
+      "ramp"     prefix scores rising by about 0.2 per key (Q and the prefix keys share
+                 a first component that grows with the position): every 64-key tile
+                 raises the row maximum far past any rescale threshold of an online
+                 softmax.  "ramp_down": falling instead, so after the first tile every
+                 tile's terms sit far below the running maximum.  16- or 32-bit caches.
     plant: planted accept paths, duplicate sibling tokens and logit ties (needs vocab).
     room: cache capacity kept free after each prefix, in tokens (NaN-filled), for
           committing accepted tokens; paged sequences get blocks for L_b + room tokens.
@@ -433,6 +438,22 @@ def make(cfg: Config, seed: int | None = None, *, variant: str = "plain", plant:
                 k_cache[blk, :, j % PAGE, :] = val
             else:
                 k_cache[b, :, j, :] = val
+    elif variant in ("ramp", "ramp_down"):
+        if fp8:
+            raise ValueError("the ramp variants take a 16- or 32-bit cache")
+        step = 0.2 * math.sqrt(D) / 4.0  # with q[..., 0] = 4: a score step of 0.2
+        for b in range(B):
+            L = int(prefix_len[b])
+            q[b, ..., 0] = 4.0
+            if L == 0:
+                continue
+            pos = np.arange(L) if variant == "ramp" else (L - 1 - np.arange(L))
+            col = np.repeat((pos * step).astype(np.float32)[:, None], Hkv, axis=1)  # [L][Hkv]
+            if cfg.paged:
+                j = np.arange(L)
+                k_cache[out["block_table"][b, j // PAGE], :, j % PAGE, 0] = _store(col, dt)
+            else:
+                k_cache[b, :, :L, 0] = _store(col.T, dt)
     elif variant != "plain":
         raise ValueError(variant)
 
