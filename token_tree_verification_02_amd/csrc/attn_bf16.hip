@@ -128,43 +128,7 @@ __global__ __launch_bounds__(64 * RB * KS) void attn_bf16_kernel(AttnArgs a, int
   const int g = t % Hkv;
   const int b = t / Hkv;
 
-  const int Lraw = a.plen[b];
-  const int L = Lraw < 0 ? 0 : (Lraw > cap ? cap : Lraw);
-  const AS4 int32_t* btc = (const AS4 int32_t*)a.bt;
-
-  if (a.status != nullptr && c == 0 && rs == 0 && g == 0) {
-    int bad = (Lraw < 0 || Lraw > cap);
-    if (a.paged) {
-      const int nb = (L + TV_PAGE - 1) / TV_PAGE;
-      for (int i = tid; i < nb; i += C::NT) {
-        const int id = a.bt[(size_t)b * a.max_blocks + i];
-        bad |= (id < 0 || id >= a.num_blocks);
-      }
-    }
-    // workgroup OR through the first LDS word (the ring is not in use yet), so
-    // the kernel needs no LDS beyond its ring
-    int AS3* flag = (int AS3*)smem;
-    if (tid == 0) *flag = 0;
-    __syncthreads();
-    if (bad) *flag = 1;
-    __syncthreads();
-    bad = *flag;
-    __syncthreads();  // read by every thread before the ring is written
-    if (tid == 0) a.status[b] = bad ? TV_EINVAL : TV_OK;
-  }
-
-  const int k0 = c * chunk_len;
-  const int k1 = min(L, k0 + chunk_len);
-  const int npre = k1 > k0 ? k1 - k0 : 0;
-  const bool has_tree = (c == 0);
-  if (npre == 0 && !has_tree) return;  // empty chunk (uniform per workgroup)
-  const int nc_b = L > 0 ? (L + chunk_len - 1) / chunk_len : 1;
-  const bool direct = (nc_b == 1);
-
-  const int T_pre = (npre + TK - 1) / TK;
-  const int T = T_pre + (has_tree ? (n + TK - 1) / TK : 0);
-  const int iters = (T + KS - 1) / KS;
-
+  const int Lraw = a.plen[b];  // its latency overlaps the speculative issue below
   const char* kc = (const char*)a.kc;
   const char* vc = (const char*)a.vc;
   const char* ktr = (const char*)a.kt;
@@ -199,6 +163,68 @@ __global__ __launch_bounds__(64 * RB * KS) void attn_bf16_kernel(AttnArgs a, int
     gran_[q] = gran;
     voff[q] = (uint32_t)(((a.paged ? (key & 15) : key) * D + gran * 8) * 2);
   }
+
+  // Contiguous cache: the first ring tiles of this wave's group are issued as full
+  // prefix tiles before the prefix length arrives (their addresses do not depend
+  // on it, and each lies inside the cache row of Lmax tokens); the prologue below
+  // issues again any that turn out partial, tree tiles or past the end, which
+  // overwrites the same LDS lines (a wave's DMA lines land in issue order).  Not in
+  // the workgroups that check the sequence's status (they use the ring's first
+  // word as a flag first), nor with an fp8 cache.
+  const bool spec = !FP8 && !a.paged && !(a.status != nullptr && c == 0 && rs == 0 && g == 0);
+  auto spec_tile = [&](int i) { return spec && c * chunk_len + (i * KS + ks) * TK + TK <= cap; };
+#pragma unroll
+  for (int i = 0; i < S - 1; ++i) {
+    if (spec_tile(i)) {
+      const int tstart = c * chunk_len + (i * KS + ks) * TK;
+      const char* kb = kc + (rowbase + tstart) * D * 2;
+      const char* vb = vc + (rowbase + tstart) * D * 2;
+      const uint32_t gbase = ring + i * C::STAGE + ks * C::GSTAGE;
+#pragma unroll
+      for (int q = 0; q < C::LPW; ++q)
+        dma_full(q * RB >= C::HL ? vb : kb, voff[q], gbase + (q * RB + rb) * 1024);
+    }
+  }
+
+  const int L = Lraw < 0 ? 0 : (Lraw > cap ? cap : Lraw);
+  const AS4 int32_t* btc = (const AS4 int32_t*)a.bt;
+
+  if (a.status != nullptr && c == 0 && rs == 0 && g == 0) {
+    int bad = (Lraw < 0 || Lraw > cap);
+    if (a.paged) {
+      const int nb = (L + TV_PAGE - 1) / TV_PAGE;
+      for (int i = tid; i < nb; i += C::NT) {
+        const int id = a.bt[(size_t)b * a.max_blocks + i];
+        bad |= (id < 0 || id >= a.num_blocks);
+      }
+    }
+    // workgroup OR through the first LDS word (the ring is not in use yet), so
+    // the kernel needs no LDS beyond its ring
+    int AS3* flag = (int AS3*)smem;
+    if (tid == 0) *flag = 0;
+    __syncthreads();
+    if (bad) *flag = 1;
+    __syncthreads();
+    bad = *flag;
+    __syncthreads();  // read by every thread before the ring is written
+    if (tid == 0) a.status[b] = bad ? TV_EINVAL : TV_OK;
+  }
+
+  const int k0 = c * chunk_len;
+  const int k1 = min(L, k0 + chunk_len);
+  const int npre = k1 > k0 ? k1 - k0 : 0;
+  const bool has_tree = (c == 0);
+  if (npre == 0 && !has_tree) {  // empty chunk (uniform per workgroup)
+    wait_vmcnt<0>();              // speculative lines land before the workgroup's LDS is released
+    return;
+  }
+  const int nc_b = L > 0 ? (L + chunk_len - 1) / chunk_len : 1;
+  const bool direct = (nc_b == 1);
+
+  const int T_pre = (npre + TK - 1) / TK;
+  const int T = T_pre + (has_tree ? (n + TK - 1) / TK : 0);
+  const int iters = (T + KS - 1) / KS;
+
 
   // ---- issue the DMA lines this wave owns for tile tt of its group into stage st
   auto issue = [=](int tt, int st) {
@@ -388,10 +414,13 @@ __global__ __launch_bounds__(64 * RB * KS) void attn_bf16_kernel(AttnArgs a, int
   // then leaves no load of its own pending inside the loop
 #pragma unroll
   for (int i = 0; i < S - 1; ++i) {
-    if constexpr (FP8)
-      issue8(i * KS + ks, i);
-    else
-      issue(i * KS + ks, i);
+    const int tt = i * KS + ks;
+    if constexpr (FP8) {
+      issue8(tt, i);
+    } else {
+      // a speculated tile stands if it is a full prefix tile of this chunk
+      if (!(spec_tile(i) && tt < T_pre && k0 + tt * TK + TK <= k1)) issue(tt, i);
+    }
   }
   wait_vmcnt<0>();
 
