@@ -78,7 +78,10 @@ struct Cfg {
   static constexpr int KB = TK / 32;           // 32-key MFMA blocks per tile
   static constexpr int DB = D / 32;            // 32-row d blocks of O^T
   static constexpr int SD = D / 16;            // k-steps of the QK^T product
-  static constexpr int MERGE = (KS > 1) ? (KS - 1) * RB * 64 * 66 * 4 : 0;
+  // key-split combine: one LDS slot per lane of every wave (O^T values, max, sum),
+  // padded to a multiple of 16 bytes so the slots take 128-bit accesses
+  static constexpr int SLOT = DB * 16 + 4;
+  static constexpr int MERGE = (KS > 1) ? KS * RB * 64 * SLOT * 4 : 0;
   // fp8 cache: the ring stages fp8 tiles (1 byte per element) and one bf16 tile
   // buffer per group (CUR) holds the converted tile the MFMAs read
   static constexpr int GSTAGE8 = 2 * TK * D;
@@ -546,35 +549,67 @@ __global__ __launch_bounds__(64 * RB * KS) void attn_bf16_kernel(AttnArgs a, int
   }
   wait_vmcnt<0>();  // drain the trailing zero-page loads before LDS is reused or released
 
-  // ---- combine the key-split groups of each query block
+  // ---- combine the key-split groups of each query block. Every group leaves its
+  // partial output (unnormalised O^T columns, running max, partial sum) in LDS; then
+  // the whole workgroup shares the rescale-and-sum and the stores: one work item is
+  // 8 consecutive d of one query row, so 16 threads write a row as 16-byte pieces.
   if constexpr (KS > 1) {
     lds_barrier();
     float* mb = (float*)smem;
-    if (ks > 0) {
-      float* dst = mb + (((ks - 1) * RB + rb) * 64 + lane) * 66;
+    {
+      float* dst = mb + ((ks * RB + rb) * 64 + lane) * C::SLOT;
 #pragma unroll
       for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) dst[db * 16 + r] = O[db][r];
-      dst[64] = m_run;
-      dst[65] = lsum;
+        for (int rq = 0; rq < 4; ++rq)
+          *(float4*)(dst + db * 16 + 4 * rq) = make_float4(O[db][4 * rq], O[db][4 * rq + 1], O[db][4 * rq + 2], O[db][4 * rq + 3]);
+      *(float2*)(dst + C::DB * 16) = make_float2(m_run, lsum);  // the max is the same on both half-lanes
     }
     lds_barrier();
-    if (ks > 0) return;
+    constexpr int CPR = D / 8;  // 8-value pieces per row
+    for (int it = tid; it < 32 * RB * CPR; it += C::NT) {
+      const int rr = it / CPR, ch = it % CPR;
+      const int qr = rs * 32 * RB + rr;
+      if (qr >= rows) break;  // rows grow with it: every later item is past the end too
+      const float* s0 = mb + ((rr >> 5) * 64 + (rr & 31)) * C::SLOT;  // half-lane 0 of group 0
+      constexpr int KSTEP = RB * 64 * C::SLOT, HSTEP = 32 * C::SLOT;
+      float M = -INFINITY;
 #pragma unroll
-    for (int k = 1; k < KS; ++k) {
-      const float* src = mb + (((k - 1) * RB + rb) * 64 + lane) * 66;
-      const float mk = src[64], lk = src[65];
-      const float M = fmaxf(m_run, mk);
-      const float wa = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - M);
-      const float wb = (mk == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mk - M);
+      for (int k = 0; k < KS; ++k) M = fmaxf(M, s0[k * KSTEP + C::DB * 16]);
+      float lt = 0.f, acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      const int off = (ch >> 2) * 16 + 4 * (ch & 3);  // O[db][4 rq ..]: db = ch / 4, rq = ch % 4
 #pragma unroll
-      for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) O[db][r] = O[db][r] * wa + src[db * 16 + r] * wb;
-      lsum = lsum * wa + lk * wb;
-      m_run = M;
+      for (int k = 0; k < KS; ++k) {
+        const float* sk = s0 + k * KSTEP;
+        const float mk = sk[C::DB * 16];
+        const float wk = (mk == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mk - M);
+        lt += wk * (sk[C::DB * 16 + 1] + sk[HSTEP + C::DB * 16 + 1]);
+        const float4 lo = *(const float4*)(sk + off), hi = *(const float4*)(sk + HSTEP + off);
+        acc[0] += wk * lo.x; acc[1] += wk * lo.y; acc[2] += wk * lo.z; acc[3] += wk * lo.w;
+        acc[4] += wk * hi.x; acc[5] += wk * hi.y; acc[6] += wk * hi.z; acc[7] += wk * hi.w;
+      }
+      const int u = qr / G, gi = qr % G, h = g * G + gi;
+      if (direct) {
+        const float inv = 1.f / lt;
+        uint4 w;
+        w.x = E::bits(acc[0] * inv) | (E::bits(acc[1] * inv) << 16);
+        w.y = E::bits(acc[2] * inv) | (E::bits(acc[3] * inv) << 16);
+        w.z = E::bits(acc[4] * inv) | (E::bits(acc[5] * inv) << 16);
+        w.w = E::bits(acc[6] * inv) | (E::bits(acc[7] * inv) << 16);
+        *(uint4*)((uint16_t*)a.out + ((size_t)(b * n + u) * a.Hq + h) * D + 8 * ch) = w;
+        if (a.lse != nullptr && ch == 0) a.lse[(size_t)(b * n + u) * a.Hq + h] = (M + __log2f(lt)) * kLn2;
+      } else {
+        const size_t pidx = ((size_t)(b * Hkv + g) * nchunks + c) * rows + qr;
+        float* wo = a.ws_o + pidx * D + 8 * ch;
+        *(float4*)wo = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        *(float4*)(wo + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
+        if (ch == 0) {
+          a.ws_ml[2 * pidx] = M;
+          a.ws_ml[2 * pidx + 1] = lt;
+        }
+      }
     }
+    return;
   }
 
   const float ltot = sum_xor32(lsum);
