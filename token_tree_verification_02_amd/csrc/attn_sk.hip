@@ -44,6 +44,7 @@ namespace {
 using namespace attn;
 
 constexpr int kTK = 64;  // keys per tile
+constexpr int kShadowValu = 4;  // vector instructions scheduled after each product of a shadowed block
 constexpr float kSumCap = 256.f;  // 2^kTau: a lane's block sum above this triggers a rescale
 constexpr int kSkQB = 1;  // 32-row query blocks per wave (256 rows per workgroup)
 
@@ -317,10 +318,16 @@ __device__ __forceinline__ void sk_qk(const char AS3* Kr, int kb, const typename
 // One 64-key tile for one wave holding one 32-row query block.  MASKED: key
 // validity from `lim` (keys of the tile that exist) and, for tree tiles, the
 // ancestor bits of each query's node.  Both key blocks' QK products are issued
-// first: block 1's run in the matrix core while block 0's softmax executes on
-// the VALU (in-flight MFMAs overlap later independent instructions, across the
-// rescale branch too); then per block QK -> max -> (rare) rescale -> softmax
-// -> PV, and the other wave on the SIMD fills the gaps.
+// first, then per block max -> (rare) rescale -> softmax -> PV.
+// Full tiles place each block's softmax in the shadow of the other block's
+// products: issued in bursts, a wave's products stall its issue while the matrix
+// core drains them, and its softmax then runs with the matrix core idle unless
+// the other wave on the SIMD happens to be in the opposite phase.  So block 0's
+// probabilities are emitted with block 1's QK products and block 1's with block
+// 0's PV products, and the scheduler alternates one product with up to
+// kShadowValu vector instructions (VALU or transcendental; 4 measured best
+// among 2 to 6).  The arithmetic and its order are those of one block after
+// the other.
 // slt: the score scale (log2 domain).
 template <class E, int D, int QB, bool MASKED>
 __device__ __forceinline__ void sk_tile(const char AS3* Kr, const char AS3* Vr,
@@ -329,30 +336,76 @@ __device__ __forceinline__ void sk_tile(const char AS3* Kr, const char AS3* Vr,
                                         const uint32_t (&kofs)[D / 16], const uint32_t (&vofs)[D / 32], float slt,
                                         int lim, bool tree, const uint64_t (&bits)[QB], int hh) {
   static_assert(QB == 1, "one query block per wave");
-  f32x16 Sa[2][1];
-  sk_qk<E, D, 1>(Kr, 0, qop, kofs, Sa[0]);
-  sk_qk<E, D, 1>(Kr, 1, qop, kofs, Sa[1]);
   if constexpr (!MASKED) {
     // Full prefix tile with the reference max already set (the first tile of a
     // segment takes the masked path): the probabilities are taken against the
     // reference directly, and the block's maximum is only computed, with a
     // rescale, when a lane's sum of 16 probabilities exceeds 2^kTau, i.e.
     // whenever some probability might (the same bound the masked path keeps).
+    constexpr int SD = D / 16, DB = D / 32, ROWB = 2 * D;
+    f32x16 S0[1], S1;
+    sk_qk<E, D, 1>(Kr, 0, qop, kofs, S0);
+    typename E::V8 P0[1][2], P1[1][2];
+    float lb0 = 0.f, lb1 = 0.f;
+    {  // block 1's QK products, block 0's probabilities in their shadow
+      typename E::V8 kop[SD];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      typename E::V8 P[1][2];
-      float lb = 0.f;
-      sk_probs<E>(Sa[kb][0], P[0], lb, slt, m_run[0]);
-      if (__builtin_expect(__any(lb > kSumCap), 0)) {
-        sk_rescale<D>(O[0], m_run[0], lsum[0], sk_colmax(Sa[kb][0]) * slt);
-        lb = 0.f;
-        sk_probs<E>(Sa[kb][0], P[0], lb, slt, m_run[0]);
+      for (int sd = 0; sd < SD; ++sd) kop[sd] = *(const typename E::V8 AS3*)(Kr + 32 * ROWB + kofs[sd]);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) S1[r] = 0.f;
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int sd = 0; sd < SD; ++sd) S1 = E::mfma(kop[sd], qop[0][sd], S1);
+      sk_probs<E>(S0[0], P0[0], lb0, slt, m_run[0]);
+#pragma unroll
+      for (int i = 0; i < SD; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);            // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x402, kShadowValu, 0);  // then VALU / transcendental
       }
-      lsum[0] += lb;
-      sk_pv<E, D, 1>(Vr, kb, P, O, vofs);
+      __builtin_amdgcn_sched_barrier(0);
     }
+    if (__builtin_expect(__any(lb0 > kSumCap), 0)) {
+      sk_rescale<D>(O[0], m_run[0], lsum[0], sk_colmax(S0[0]) * slt);
+      lb0 = 0.f;
+      sk_probs<E>(S0[0], P0[0], lb0, slt, m_run[0]);
+    }
+    lsum[0] += lb0;
+    {  // block 0's PV products, block 1's probabilities in their shadow
+      typename E::V8 vop[2][DB];
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const char AS3* vp = Vr + (16 * half) * ROWB + vofs[db];
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 AS3*)vp);
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 AS3*)(vp + 4 * ROWB));
+          vop[half][db] = __builtin_bit_cast(typename E::V8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) O[0][db] = E::mfma(vop[half][db], P0[0][half], O[0][db]);
+      sk_probs<E>(S1, P1[0], lb1, slt, m_run[0]);
+#pragma unroll
+      for (int i = 0; i < 2 * DB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x402, kShadowValu, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (__builtin_expect(__any(lb1 > kSumCap), 0)) {
+      sk_rescale<D>(O[0], m_run[0], lsum[0], sk_colmax(S1) * slt);
+      lb1 = 0.f;
+      sk_probs<E>(S1, P1[0], lb1, slt, m_run[0]);
+    }
+    lsum[0] += lb1;
+    sk_pv<E, D, 1>(Vr, 1, P1, O, vofs);
     return;
   }
+  f32x16 Sa[2][1];
+  sk_qk<E, D, 1>(Kr, 0, qop, kofs, Sa[0]);
+  sk_qk<E, D, 1>(Kr, 1, qop, kofs, Sa[1]);
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
     if constexpr (MASKED) sk_mask(Sa[kb][0], kb, lim, tree, bits[0], hh);
