@@ -210,12 +210,18 @@ __device__ __forceinline__ uint64_t pick_word(const uint64_t (&m)[4], int w) {
 // that are not ancestors of the lane's node, become -inf.  The lane holds key
 // 16*(r>>3) + 8*hh + (r&7) of the block.
 __device__ __forceinline__ void sk_mask(f32x16& s, int kb, int lim, bool tree, uint64_t bits, int hh) {
-  const uint32_t w32 = (uint32_t)(bits >> (32 * kb)) >> (8 * hh);
+  const int nv = lim - 32 * kb;  // valid keys of the block (lim is uniform)
+  if (!tree && nv >= 32) return;  // e.g. a segment's first tile: nothing to mask
+  // one keep bit per key of the block, then per score a sign-extended bit field
+  // selects the score or -inf (two VALU per score)
+  uint32_t keep = nv >= 32 ? ~0u : (nv <= 0 ? 0u : (1u << nv) - 1u);
+  if (tree) keep &= (uint32_t)(bits >> (32 * kb));
+  keep >>= 8 * hh;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    const int ko = kb * 32 + 16 * (r >> 3) + 8 * hh + (r & 7);
-    const bool ok = ko < lim && (!tree || ((w32 >> (16 * (r >> 3) + (r & 7))) & 1u));
-    s[r] = ok ? s[r] : -INFINITY;
+    const int pos = 16 * (r >> 3) + (r & 7);
+    const uint32_t m = (uint32_t)((int)(keep << (31 - pos)) >> 31);  // all ones iff the key is kept
+    s[r] = __uint_as_float((__float_as_uint(s[r]) & m) | (0xff800000u & ~m));
   }
 }
 
