@@ -334,13 +334,17 @@ __device__ __forceinline__ void sk_qk(const char AS3* Kr, int kb, const typename
 // kShadowValu vector instructions (VALU or transcendental; 4 measured best
 // among 2 to 6).  The arithmetic and its order are those of one block after
 // the other.
+// refill: the ring's DMA for a later tile, issued once block 0's QK products are
+// in the matrix core (its scalar address work then overlaps them; issued right
+// after the barrier it delayed the first products, issued after block 1's
+// products it delayed the PV products).
 // slt: the score scale (log2 domain).
-template <class E, int D, int QB, bool MASKED>
+template <class E, int D, int QB, bool MASKED, class RF>
 __device__ __forceinline__ void sk_tile(const char AS3* Kr, const char AS3* Vr,
                                         const typename E::V8 (&qop)[QB][D / 16],
                                         f32x16 (&O)[QB][D / 32], float (&m_run)[QB], float (&lsum)[QB],
                                         const uint32_t (&kofs)[D / 16], const uint32_t (&vofs)[D / 32], float slt,
-                                        int lim, bool tree, const uint64_t (&bits)[QB], int hh) {
+                                        int lim, bool tree, const uint64_t (&bits)[QB], int hh, RF&& refill) {
   static_assert(QB == 1, "one query block per wave");
   if constexpr (!MASKED) {
     // Full prefix tile with the reference max already set (the first tile of a
@@ -351,6 +355,7 @@ __device__ __forceinline__ void sk_tile(const char AS3* Kr, const char AS3* Vr,
     constexpr int SD = D / 16, DB = D / 32, ROWB = 2 * D;
     f32x16 S0[1], S1;
     sk_qk<E, D, 1>(Kr, 0, qop, kofs, S0);
+    refill();
     typename E::V8 P0[1][2], P1[1][2];
     float lb0 = 0.f, lb1 = 0.f;
     {  // block 1's QK products, block 0's probabilities in their shadow
@@ -411,6 +416,7 @@ __device__ __forceinline__ void sk_tile(const char AS3* Kr, const char AS3* Vr,
   }
   f32x16 Sa[2][1];
   sk_qk<E, D, 1>(Kr, 0, qop, kofs, Sa[0]);
+  refill();
   sk_qk<E, D, 1>(Kr, 1, qop, kofs, Sa[1]);
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
@@ -656,21 +662,22 @@ __global__ __launch_bounds__(64 * RB) void attn_sk_kernel(AttnArgs a, SkArgs k) 
         for (int r = 0; r < 16; ++r) O[qb][db][r] = 0.f;
 
     // One tile iteration: wait for the tile, free the stage of the previous one,
-    // refill the ring, compute.  The full prefix tiles of the segment run first
-    // in a loop without any masking code, then the masked ones (the ragged last
-    // prefix tile and the tree tiles) in a second loop.
+    // compute, refilling the ring from inside the tile (after its first products).
+    // The full prefix tiles of the segment run first in a loop without any masking
+    // code, then the masked ones (the ragged last prefix tile and the tree tiles)
+    // in a second loop.
     auto step = [&](auto masked_c, int j) {
       constexpr bool MASKED = decltype(masked_c)::value;
       wait_vmcnt<WAITN>();  // this wave's lines of tile `it` have landed
       lds_barrier();        // ... everyone's, and everyone left tile it-1
-      {
+      auto refill = [&]() {
         const bool live = it + S - 1 < ntiles;
         issue(ic, live, ring + ((it + S - 1) % S) * STAGE, ids);
         if (live) {
           cursor_next(ic, plen, B, Hkv, k.cap, ttree);
           load_ids(ic, ids);  // consumed by the next tile's issue
         }
-      }
+      };
       const int off = cc.off + j;
       const int st = it % S;
       const char AS3* Kr = (const char AS3*)smem + st * STAGE;
@@ -688,7 +695,7 @@ __global__ __launch_bounds__(64 * RB) void attn_sk_kernel(AttnArgs a, SkArgs k) 
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) bits[qb] = 0ull;
       }
-      sk_tile<E, D, QB, MASKED>(Kr, Vr, qop, O, m_run, lsum, kofs, vofs, sl2, lim, tree, bits, hh);
+      sk_tile<E, D, QB, MASKED>(Kr, Vr, qop, O, m_run, lsum, kofs, vofs, sl2, lim, tree, bits, hh, refill);
       ++it;
     };
     // full prefix tiles come first; the segment's first tile always takes the
