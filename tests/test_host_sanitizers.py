@@ -29,7 +29,7 @@ def test_capi_host_layer_under_sanitizers(tmp_path):
     if cc is None:
         pytest.skip("hipcc not available")
     inc = ["-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG, "csrc")]
-    # sanitizers on the host side only (this build has no device code)
+    # sanitizers on the host side only (the sanitizer binary holds no device code)
     san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
            "-Xarch_host", "-fno-sanitize-recover=all"]
     common = ["-x", "hip", "--offload-host-only", "-O1", "-g", "-std=c++17", *inc, *san]
