@@ -8,9 +8,10 @@
 // sharing their first token's node).
 //
 // topk_kernel reads one SSM logits row per workgroup in two passes of 16-byte
-// vectors.  The first takes each thread's maximum, then the maxima of 16 groups
-// of 16 threads: they are 16 entries of the row, so the k-th largest of them
-// (k <= 16) bounds the row's k-th largest value from below.  The second pass
+// vectors.  The first takes each thread's maximum, then the maxima of the
+// workgroup's groups of 16 threads (32 of them): they are entries of the row, so
+// the k-th largest of them (k <= 16) bounds the row's k-th largest value from
+// below.  The second pass
 // (mostly cache hits) skips every vector whose maximum is below that bound and
 // keeps, per thread, its best 16 (value desc, index asc) among the entries at
 // or above it, which are few, so the insertion code rarely runs.  k rounds of a
@@ -31,6 +32,10 @@ namespace tv {
 namespace {
 
 constexpr int kKeep = TV_TOPK_MAX;  // per-thread list length (>= k)
+// threads per SSM row: 512 keep twice 256's loads in flight (128000-entry rows
+// 9% faster, 32000-entry rows 2%); 1024 lose more to the k rounds' barriers
+// across 16 waves than they gain
+constexpr int kTopkThreads = 512;
 
 // Workgroup barrier that orders LDS accesses only (no wait for global stores).
 __device__ __forceinline__ void lds_sync() {
@@ -65,16 +70,17 @@ __device__ __forceinline__ void keep_insert(float (&lv)[kKeep], int (&li)[kKeep]
 // checks its sequence's frontier (ids in [0, n_cur), room for the children)
 // before writing; slot 0 reports status and the new node count.
 template <bool BF16>
-__global__ __launch_bounds__(256) void topk_kernel(int F, int V, int k, int n_max, const void* __restrict__ logits,
+__global__ __launch_bounds__(kTopkThreads) void topk_kernel(int F, int V, int k, int n_max, const void* __restrict__ logits,
                                                    const int32_t* __restrict__ frontier,
                                                    const int32_t* __restrict__ n_cur, int32_t* __restrict__ parent,
                                                    int32_t* __restrict__ depth, int32_t* __restrict__ tokens,
                                                    float* __restrict__ scores, int32_t* __restrict__ n_out,
                                                    int32_t* __restrict__ status) {
-  __shared__ float sv[2][4];  // per round (double-buffered): each wave's best head
-  __shared__ int si[2][4];
-  __shared__ unsigned long long sb[4];
-  __shared__ float s_gmax[16];
+  constexpr int NW = kTopkThreads / 64, NG = kTopkThreads / 16;
+  __shared__ float sv[2][NW];  // per round (double-buffered): each wave's best head
+  __shared__ int si[2][NW];
+  __shared__ unsigned long long sb[NW];
+  __shared__ float s_gmax[NG];
   __shared__ float s_thr;
   __shared__ float s_v[kKeep];  // the k winners, written out after the rounds
   __shared__ int s_i[kKeep];
@@ -89,7 +95,7 @@ __global__ __launch_bounds__(256) void topk_kernel(int F, int V, int k, int n_ma
   if (lane == 0) sb[wv] = bl;
   bad = __syncthreads_or(bad);
   int nvalid = 0, valid_before = 0;
-  for (int w = 0; w < 4; ++w) {
+  for (int w = 0; w < NW; ++w) {
     nvalid += __popcll(sb[w]);
     if (w < (f >> 6)) valid_before += __popcll(sb[w]);
   }
@@ -116,13 +122,13 @@ __global__ __launch_bounds__(256) void topk_kernel(int F, int V, int k, int n_ma
   // Visit every element of this thread's share in increasing index order:
   // 16-byte vectors first, then the unaligned tail one by one.
   auto sweep = [&](auto&& fn) {
-    for (int base = 0; base < nv; base += R1 * 256) {
+    for (int base = 0; base < nv; base += R1 * kTopkThreads) {
       uint4 w[R1];
 #pragma unroll
-      for (int r = 0; r < R1; ++r) w[r] = vp[min(base + r * 256 + tid, nv - 1)];
+      for (int r = 0; r < R1; ++r) w[r] = vp[min(base + r * kTopkThreads + tid, nv - 1)];
 #pragma unroll
       for (int r = 0; r < R1; ++r) {
-        const int vi = base + r * 256 + tid;
+        const int vi = base + r * kTopkThreads + tid;
         if (vi >= nv) continue;
         const uint32_t q[4] = {w[r].x, w[r].y, w[r].z, w[r].w};
 #pragma unroll
@@ -130,12 +136,12 @@ __global__ __launch_bounds__(256) void topk_kernel(int F, int V, int k, int n_ma
           fn(BF16 ? ((e & 1) ? bf16hi(q[e >> 1]) : bf16lo(q[e >> 1])) : __uint_as_float(q[e]), vi * EPV + e);
       }
     }
-    for (int i = nv * EPV + tid; i < V; i += 256)
+    for (int i = nv * EPV + tid; i < V; i += kTopkThreads)
       fn(BF16 ? bf16_to_f32(((const uint16_t*)row)[i]) : ((const float*)row)[i], i);
   };
 
-  // ---- pass 1: each thread's maximum, then the maxima of 16 groups of 16
-  // threads; the k-th largest of those 16 entries bounds the row's k-th largest
+  // ---- pass 1: each thread's maximum, then the maxima of NG groups of 16
+  // threads; the k-th largest of those NG entries bounds the row's k-th largest
   // value from below
   float tmax = -INFINITY;
   sweep([&](float x, int) { tmax = fmaxf(tmax, x); });
@@ -143,11 +149,11 @@ __global__ __launch_bounds__(256) void topk_kernel(int F, int V, int k, int n_ma
   for (int o = 8; o > 0; o >>= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, o));
   if ((tid & 15) == 0) s_gmax[tid >> 4] = tmax;
   lds_sync();
-  if (tid < 16) {
+  if (tid < NG) {
     const float mine = s_gmax[tid];
     int above = 0;  // group maxima ranked before mine: larger, or equal from a lower group
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
+    for (int t = 0; t < NG; ++t) {
       const float o = s_gmax[t];
       above += o > mine || (o == mine && t < tid);
     }
@@ -161,13 +167,13 @@ __global__ __launch_bounds__(256) void topk_kernel(int F, int V, int k, int n_ma
   int li[kKeep];
 #pragma unroll
   for (int s = 0; s < kKeep; ++s) lv[s] = -INFINITY, li[s] = INT_MAX;
-  for (int base = 0; base < nv; base += R2 * 256) {
+  for (int base = 0; base < nv; base += R2 * kTopkThreads) {
     uint4 w[R2];
 #pragma unroll
-    for (int r = 0; r < R2; ++r) w[r] = vp[min(base + r * 256 + tid, nv - 1)];
+    for (int r = 0; r < R2; ++r) w[r] = vp[min(base + r * kTopkThreads + tid, nv - 1)];
 #pragma unroll
     for (int r = 0; r < R2; ++r) {
-      const int vi = base + r * 256 + tid;
+      const int vi = base + r * kTopkThreads + tid;
       const uint32_t q[4] = {w[r].x, w[r].y, w[r].z, w[r].w};
       float m;  // the vector's maximum: most vectors stop here
       if (BF16)
@@ -187,7 +193,7 @@ __global__ __launch_bounds__(256) void topk_kernel(int F, int V, int k, int n_ma
       }
     }
   }
-  for (int i = nv * EPV + tid; i < V; i += 256) {  // unaligned rows and the tail
+  for (int i = nv * EPV + tid; i < V; i += kTopkThreads) {  // unaligned rows and the tail
     const float x = BF16 ? bf16_to_f32(((const uint16_t*)row)[i]) : ((const float*)row)[i];
     if (x >= thr) keep_insert(lv, li, x, i);
   }
@@ -209,7 +215,7 @@ __global__ __launch_bounds__(256) void topk_kernel(int F, int V, int k, int n_ma
     float v = sv[j & 1][0];  // every thread takes the workgroup's winner itself
     int i = si[j & 1][0];
 #pragma unroll
-    for (int w = 1; w < 4; ++w)
+    for (int w = 1; w < NW; ++w)
       if (before(sv[j & 1][w], si[j & 1][w], v, i)) v = sv[j & 1][w], i = si[j & 1][w];
     if (tid == 0) s_v[j] = v, s_i[j] = i;
     if (li[0] == i) {  // indices are unique, so exactly one thread owns the winner
@@ -320,10 +326,10 @@ hipError_t launch_expand(int B, int F, int V, int k, int n_max, int bf16, const 
                          int32_t* n_out, int32_t* status, hipStream_t s) {
   if (B == 0) return hipSuccess;
   if (bf16)
-    hipLaunchKernelGGL(topk_kernel<true>, dim3(B * F), dim3(256), 0, s, F, V, k, n_max, logits, frontier, n_cur,
+    hipLaunchKernelGGL(topk_kernel<true>, dim3(B * F), dim3(kTopkThreads), 0, s, F, V, k, n_max, logits, frontier, n_cur,
                        parent, depth, tokens, scores, n_out, status);
   else
-    hipLaunchKernelGGL(topk_kernel<false>, dim3(B * F), dim3(256), 0, s, F, V, k, n_max, logits, frontier, n_cur,
+    hipLaunchKernelGGL(topk_kernel<false>, dim3(B * F), dim3(kTopkThreads), 0, s, F, V, k, n_max, logits, frontier, n_cur,
                        parent, depth, tokens, scores, n_out, status);
   return hipGetLastError();
 }
