@@ -169,6 +169,14 @@ EDGE = {
     "fp32_paged_gqa": W.config(4, B=2, dtype="f32", L_lo=30, L_hi=700, n=12, vocab=0),
     "fp32_d128": W.config(2, B=1, dtype="f32", L_lo=200, L_hi=200, Hq=4, Hkv=2, vocab=0),
     "b1_long_split": W.config(4, B=1, L_lo=20000, L_hi=20000, vocab=0),
+    # many-row kernel, the bounds of a 64-key tile's two 32-key mask blocks: a last prefix
+    # tile with 31, 32 or 33 valid keys, prefixes shorter than one tile, and trees of 96
+    # nodes (a second tree tile whose second block holds no node)
+    "sk_prefix_64k_plus_31": W.config(3, B=2, L_lo=2079, L_hi=2079, vocab=0),
+    "sk_prefix_64k_plus_32": W.config(3, B=2, L_lo=2080, L_hi=2080, vocab=0),
+    "sk_prefix_64k_plus_33": W.config(4, B=2, L_lo=2081, L_hi=2081, vocab=0),
+    "sk_prefix_under_64": W.config(4, B=6, L_lo=1, L_hi=63, vocab=0),
+    "sk_tree_n96": W.config(3, B=2, n=96, tree="random", max_depth=8, L_lo=100, L_hi=300, vocab=0),
 }
 
 
