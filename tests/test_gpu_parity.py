@@ -177,6 +177,10 @@ EDGE = {
     "sk_prefix_64k_plus_33": W.config(4, B=2, L_lo=2081, L_hi=2081, vocab=0),
     "sk_prefix_under_64": W.config(4, B=6, L_lo=1, L_hi=63, vocab=0),
     "sk_tree_n96": W.config(3, B=2, n=96, tree="random", max_depth=8, L_lo=100, L_hi=300, vocab=0),
+    # few-row plans one row past a 32-row query block (2 and 4 row waves): the key-split
+    # groups' combined epilogue stops at the last row, contiguous and chunked
+    "rows33": W.config(2, B=2, n=33, tree="random", max_depth=6, L_lo=500, L_hi=900, vocab=0),
+    "rows65_chunks": W.config(2, B=1, n=65, tree="random", max_depth=8, L_lo=7000, L_hi=7000, vocab=0),
 }
 
 
